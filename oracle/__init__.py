@@ -1,0 +1,125 @@
+"""CPU oracle for MoE expert-parallel dispatch + combine (ctypes over plain C).
+
+TEST INFRASTRUCTURE ONLY: only ``tests/``, ``__graft_entry__.smoke()`` and
+``bench.py``'s ``cpu_baseline`` leg may import or call this package.  The
+product library (``combine_count_amd``) never touches it and shares no code
+with it.
+
+The arithmetic lives in ``epdc_oracle.c`` (sequential, single-threaded,
+``-O2 -ffp-contract=off``); this module only builds it with gcc when no
+library is built yet and marshals numpy arrays.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+SRC = os.path.join(_HERE, "epdc_oracle.c")
+LIB = os.path.join(_HERE, "liboracle.so")
+CFLAGS = ["-O2", "-ffp-contract=off", "-fno-fast-math", "-std=c11", "-fPIC", "-shared"]
+
+
+def build(src: str = SRC, out: str = LIB, extra: tuple = ()) -> str:
+    """Compile the oracle with gcc; returns the library path."""
+    tmp = out + f".tmp{os.getpid()}"
+    subprocess.run(["gcc", *CFLAGS, *extra, "-o", tmp, src, "-lm"], check=True)
+    os.replace(tmp, out)
+    return out
+
+
+_lib_cache: dict[str, ctypes.CDLL] = {}
+
+
+def load(path: str | None = None) -> ctypes.CDLL:
+    path = path or LIB
+    if path in _lib_cache:
+        return _lib_cache[path]
+    if path == LIB and (not os.path.exists(LIB) or os.path.getmtime(LIB) < os.path.getmtime(SRC)):
+        build()
+    lib = ctypes.CDLL(path)
+    i32, p = ctypes.c_int32, ctypes.c_void_p
+    lib.oracle_dispatch.restype = i32
+    lib.oracle_dispatch.argtypes = [i32] * 7 + [p] * 9
+    lib.oracle_combine.restype = i32
+    lib.oracle_combine.argtypes = [i32] * 7 + [p] * 5 + [i32, p, p]
+    _lib_cache[path] = lib
+    return lib
+
+
+def _ptr(a):
+    if a is None:
+        return None
+    assert a.flags["C_CONTIGUOUS"], "oracle arrays must be C-contiguous"
+    return a.ctypes.data
+
+
+class DispatchOut:
+    def __init__(self, recvX, recvTokIdx, recvExpertIds, recvWeights, recvCount, sendMap):
+        self.recvX = recvX
+        self.recvTokIdx = recvTokIdx
+        self.recvExpertIds = recvExpertIds
+        self.recvWeights = recvWeights
+        self.recvCount = recvCount
+        self.sendMap = sendMap
+
+
+def dispatch(W, H, M, Epr, K, useWeights, x, expertIds, weights, *, fill=None, lib=None):
+    """Run the oracle dispatch on numpy inputs.
+
+    ``x``: uint16 [T][H] bf16 bits; ``expertIds``: int32 [T][K]; ``weights``:
+    float32 [T][K] or None.  Windows are pre-filled with ``fill`` (a dict of
+    sentinel values) so that untouched rows stay recognisable.
+    """
+    lib = lib or load()
+    T = x.shape[0]
+    fill = fill or {}
+    recvX = np.full((W, M, H), fill.get("recvX", 0), dtype=np.uint16)
+    recvTokIdx = np.full((W, M), fill.get("recvTokIdx", 0), dtype=np.int32)
+    recvExpertIds = np.full((W, M, K), fill.get("recvExpertIds", 0), dtype=np.int32)
+    recvWeights = np.full((W, M, K), fill.get("recvWeights", 0), dtype=np.float32)
+    recvCount = np.full((W,), -7, dtype=np.int32)
+    sendMap = np.full((T, K), -99, dtype=np.int32)
+    x = np.ascontiguousarray(x, dtype=np.uint16)
+    expertIds = np.ascontiguousarray(expertIds, dtype=np.int32)
+    if weights is not None:
+        weights = np.ascontiguousarray(weights, dtype=np.float32)
+    rc = lib.oracle_dispatch(W, H, M, Epr, K, int(useWeights), T,
+                             _ptr(x), _ptr(expertIds), _ptr(weights),
+                             _ptr(recvX), _ptr(recvTokIdx), _ptr(recvExpertIds),
+                             _ptr(recvWeights), _ptr(recvCount), _ptr(sendMap))
+    if rc != 0:
+        raise ValueError(f"oracle_dispatch rejected its arguments ({rc})")
+    return DispatchOut(recvX, recvTokIdx, recvExpertIds, recvWeights, recvCount, sendMap)
+
+
+def combine(W, H, M, Epr, K, useWeights, y, expertIds, weights, sendMap, tokens=None, lib=None):
+    """Run the oracle combine.  ``y``: uint16 [W][M][H]; returns uint16 rows.
+
+    With ``tokens`` (an int sequence) only those tokens are combined, in that
+    order; otherwise every token of ``sendMap``.
+    """
+    lib = lib or load()
+    T = sendMap.shape[0]
+    y = np.ascontiguousarray(y, dtype=np.uint16)
+    assert y.shape == (W, M, H)
+    expertIds = np.ascontiguousarray(expertIds, dtype=np.int32)
+    sendMap = np.ascontiguousarray(sendMap, dtype=np.int32)
+    if weights is not None:
+        weights = np.ascontiguousarray(weights, dtype=np.float32)
+    tok = None
+    n = T
+    if tokens is not None:
+        tok = np.ascontiguousarray(np.asarray(tokens, dtype=np.int32))
+        n = tok.shape[0]
+    out = np.empty((n, H), dtype=np.uint16)
+    acc = np.empty((H,), dtype=np.float32)
+    rc = lib.oracle_combine(W, H, M, Epr, K, int(useWeights), T,
+                            _ptr(y), _ptr(expertIds), _ptr(weights), _ptr(sendMap),
+                            _ptr(tok), n, _ptr(acc), _ptr(out))
+    if rc != 0:
+        raise ValueError(f"oracle_combine rejected its arguments ({rc})")
+    return out

@@ -1,0 +1,176 @@
+/*
+ * CPU oracle for one source rank's share of MoE expert-parallel dispatch and
+ * combine.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Nothing in the product path may import, call,
+ * link or execute this file or the library built from it: only tests/,
+ * __graft_entry__.smoke() and bench.py's cpu_baseline leg do.  It shares no
+ * code, header, table or helper with the HIP library; the two meet only in
+ * the seeded input generator (tests/workloads.py).
+ *
+ * Plain, sequential, single-threaded C.  Build with -O2 -ffp-contract=off so
+ * that the only fused multiply-add is the explicit fmaf() below.
+ *
+ * Notation (names as in the pages' EpCfg, MORI JIT v2 design doc, §3.2):
+ *   W  = worldSize           Epr = numExpertPerRank    E = W*Epr
+ *   K  = numExpertPerToken   H   = hiddenDim (bf16 elements per row)
+ *   M  = maxTokPerRank       T   = numTokens (0 <= T <= M)
+ * bf16 values travel as their 16-bit patterns (uint16_t).
+ *
+ * Parity pins (see tests/test_oracle_pins.py): brute force on tiny inputs,
+ * the closed-form expected count of unique (token, PE) pairs, the two
+ * statistics the pages print (about 1374 dropped-slot null entries at
+ * ct=512/topk=6/EP4; a 311 MB combine staging copy at EP8/4096 tokens/h7168),
+ * structural invariants, identity-expert special cases and an fp64
+ * recomputation within the fp32 summation error bound.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <string.h>
+
+/* bf16 -> fp32 is exact: the bf16 pattern is the upper half of the fp32. */
+static float bf16_to_f32(uint16_t b) {
+    uint32_t u = (uint32_t)b << 16;
+    float f;
+    memcpy(&f, &u, sizeof f);
+    return f;
+}
+
+/* fp32 -> bf16, round to nearest, ties to even (the IEEE default rounding
+ * applied at bf16 precision).  NaN stays a quiet NaN of the same sign. */
+static uint16_t f32_to_bf16_rne(float f) {
+    uint32_t u;
+    memcpy(&u, &f, sizeof u);
+    if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x0040u);
+    uint32_t lsb = (u >> 16) & 1u;
+    u += 0x7fffu + lsb;
+    return (uint16_t)(u >> 16);
+}
+
+/* Destination PE of one expert id, or -1 for an id outside [0, E).
+ * Experts are laid out in contiguous blocks of numExpertPerRank per PE; the
+ * kernels on the MORI JIT v2 page (§8) divide by numExpertPerRank for this. */
+static int32_t dest_pe(int32_t e, int32_t W, int32_t Epr) {
+    if (e < 0 || (int64_t)e >= (int64_t)W * Epr) return -1;
+    return e / Epr;
+}
+
+/*
+ * DISPATCH: COUNT + SCAN + FINALIZE, done as one sequential pass.
+ *
+ * mori PR #599 "Perf/ep disp 1250 ship" (items "ballot dedup" and "cached
+ * destPe/keep + deferred null write") describes the dispatch in two phases:
+ * COUNT finds each slot's destination PE and drops the slots of a token that
+ * hit a PE already taken by that token, so a token goes to each PE once; the
+ * dropped slots each receive a 4-byte "null" entry, written in FINALIZE
+ * together with the payload rows and the per-token metadata (three fields,
+ * the "perTokM" tokCap note of the same PR).  Dispatch only moves bytes
+ * (MORI JIT v2 §3.7), so rows and metadata are bitwise copies.
+ *
+ * Readings of what the pages leave open:
+ *   - the lowest slot index of a token keeps a PE, later slots drop;
+ *   - rows of each destination window are in ascending token order;
+ *   - window stride maxTokPerRank rows, flat index p*M + r, null = -1;
+ *   - per received row: source token index, the token's K expert ids and
+ *     its K weights (weights only when useWeights);
+ *   - ids outside [0, E) are dropped slots (null entry, no row);
+ *   - recvCount is stored, not accumulated (mori PR #599 follow-up commits:
+ *     the dispatch stores the received count so callers need no reset).
+ *
+ * Rows r >= recvCount[p] of every window are left untouched.
+ * Returns 0, or -1 on a negative size.
+ */
+int oracle_dispatch(int32_t W, int32_t H, int32_t M, int32_t Epr, int32_t K,
+                    int32_t useWeights, int32_t T,
+                    const uint16_t *x, const int32_t *expertIds, const float *weights,
+                    uint16_t *recvX, int32_t *recvTokIdx, int32_t *recvExpertIds,
+                    float *recvWeights, int32_t *recvCount, int32_t *sendMap) {
+    if (W <= 0 || H <= 0 || M <= 0 || Epr <= 0 || K <= 0 || T < 0 || T > M) return -1;
+    for (int32_t p = 0; p < W; ++p) recvCount[p] = 0;
+
+    for (int32_t t = 0; t < T; ++t) {
+        for (int32_t k = 0; k < K; ++k) {
+            int32_t e = expertIds[(int64_t)t * K + k];
+            int32_t p = dest_pe(e, W, Epr);
+            int keep = (p >= 0);
+            /* dedup: a PE already reached by an earlier slot of t drops k */
+            for (int32_t j = 0; keep && j < k; ++j)
+                if (dest_pe(expertIds[(int64_t)t * K + j], W, Epr) == p) keep = 0;
+            if (!keep) {
+                sendMap[(int64_t)t * K + k] = -1; /* the null entry */
+                continue;
+            }
+            int32_t r = recvCount[p]++;
+            int64_t row = (int64_t)p * M + r;
+            memcpy(recvX + row * H, x + (int64_t)t * H, (size_t)H * sizeof(uint16_t));
+            recvTokIdx[row] = t;
+            memcpy(recvExpertIds + row * K, expertIds + (int64_t)t * K, (size_t)K * sizeof(int32_t));
+            if (useWeights)
+                memcpy(recvWeights + row * K, weights + (int64_t)t * K, (size_t)K * sizeof(float));
+            sendMap[(int64_t)t * K + k] = (int32_t)row;
+        }
+    }
+    return 0;
+}
+
+/*
+ * COMBINE for one token: gather the rows this token's PEs returned and
+ * reduce them (MORI JIT v2 §5 and §9: the HIP backend's combine is a gather,
+ * PULL/QUAD, that reduces in place of a scatter; §3.7: combine sums, so it
+ * needs an arithmetic type).
+ *
+ * Readings:
+ *   - the PEs are visited in first-appearance slot order (the kept slots of
+ *     sendMap in ascending k);
+ *   - the scale of PE p is the fp32 sum, in slot order starting from +0, of
+ *     the weights of every slot of t whose expert lives on p (valid ids
+ *     only); with useWeights == 0 it is 1;
+ *   - accumulation in fp32 from +0 with one fused multiply-add per PE;
+ *   - output rounded to bf16, nearest-even; a token with no kept slot gives
+ *     a +0 row.
+ */
+static void combine_token(int32_t W, int32_t H, int32_t M, int32_t Epr, int32_t K,
+                          int32_t useWeights, int32_t t,
+                          const uint16_t *y, const int32_t *expertIds, const float *weights,
+                          const int32_t *sendMap, float *acc, uint16_t *outRow) {
+    for (int32_t h = 0; h < H; ++h) acc[h] = 0.0f;
+    for (int32_t k0 = 0; k0 < K; ++k0) {
+        int32_t flat = sendMap[(int64_t)t * K + k0];
+        if (flat < 0) continue;
+        int32_t p = flat / M;
+        int32_t r = flat % M;
+        float s = 1.0f;
+        if (useWeights) {
+            s = 0.0f;
+            for (int32_t k = k0; k < K; ++k)
+                if (dest_pe(expertIds[(int64_t)t * K + k], W, Epr) == p)
+                    s = s + weights[(int64_t)t * K + k];
+        }
+        const uint16_t *src = y + ((int64_t)p * M + r) * H;
+        for (int32_t h = 0; h < H; ++h) acc[h] = fmaf(s, bf16_to_f32(src[h]), acc[h]);
+    }
+    for (int32_t h = 0; h < H; ++h) outRow[h] = f32_to_bf16_rne(acc[h]);
+}
+
+/*
+ * COMBINE over tokens.  With tokens == NULL every token t in [0, T) is
+ * combined into out[t][:].  Otherwise out[i][:] receives token tokens[i]
+ * for i in [0, nList): the per-token form used to check sampled outputs of
+ * large runs.  acc is caller scratch of H floats.
+ * Returns 0, or -1 on a bad size or token index.
+ */
+int oracle_combine(int32_t W, int32_t H, int32_t M, int32_t Epr, int32_t K,
+                   int32_t useWeights, int32_t T,
+                   const uint16_t *y, const int32_t *expertIds, const float *weights,
+                   const int32_t *sendMap, const int32_t *tokens, int32_t nList,
+                   float *acc, uint16_t *out) {
+    if (W <= 0 || H <= 0 || M <= 0 || Epr <= 0 || K <= 0 || T < 0 || T > M) return -1;
+    int32_t n = tokens ? nList : T;
+    for (int32_t i = 0; i < n; ++i) {
+        int32_t t = tokens ? tokens[i] : i;
+        if (t < 0 || t >= T) return -1;
+        combine_token(W, H, M, Epr, K, useWeights, t, y, expertIds, weights, sendMap,
+                      acc, out + (int64_t)i * H);
+    }
+    return 0;
+}

@@ -1,0 +1,103 @@
+"""Plant plausible mistakes into copies of the oracle, on the CPU, and check
+that the pins catch every one of them.
+
+Each mutant is a text substitution applied to oracle/epdc_oracle.c; the
+mutated source is compiled into a temporary library and run through the pin
+checks of oracle_pins.py (cheapest first) until one fails.  No mutant may
+index outside its buffers, so none of them touches the id-range guard.
+"""
+import os
+
+import pytest
+
+import oracle
+import oracle_pins as pins
+
+MUTANTS = [
+    # (name, text in the oracle, replacement)
+    ("dedup keeps the last slot",
+     "for (int32_t j = 0; keep && j < k; ++j)",
+     "for (int32_t j = k + 1; keep && j < K; ++j)"),
+    ("no dedup",
+     "== p) keep = 0;",
+     "== p) keep = 1;"),
+    ("PE by modulo instead of division",
+     "return e / Epr;",
+     "return e % W;"),
+    ("row index from the token instead of the counter",
+     "int32_t r = recvCount[p]++;",
+     "int32_t r = (recvCount[p]++, t % M);"),
+    ("flat index stride worldSize",
+     "sendMap[(int64_t)t * K + k] = (int32_t)row;",
+     "sendMap[(int64_t)t * K + k] = (int32_t)(r * W + p);"),
+    ("null entry 0 instead of -1",
+     "sendMap[(int64_t)t * K + k] = -1; /* the null entry */",
+     "sendMap[(int64_t)t * K + k] = 0;"),
+    ("metadata: slot stored as token index",
+     "recvTokIdx[row] = t;",
+     "recvTokIdx[row] = k;"),
+    ("weights copied from the mirrored token",
+     "memcpy(recvWeights + row * K, weights + (int64_t)t * K,",
+     "memcpy(recvWeights + row * K, weights + (int64_t)(T - 1 - t) * K,"),
+    ("combine: scale from the kept slot only",
+     "for (int32_t k = k0; k < K; ++k)",
+     "for (int32_t k = k0; k < k0 + 1; ++k)"),
+    ("combine: scale misses the kept slot",
+     "for (int32_t k = k0; k < K; ++k)",
+     "for (int32_t k = k0 + 1; k < K; ++k)"),
+    ("combine: weight subtracted",
+     "s = s + weights[(int64_t)t * K + k];",
+     "s = s - weights[(int64_t)t * K + k];"),
+    ("combine: weights read with the slot index reversed",
+     "s = s + weights[(int64_t)t * K + k];",
+     "s = s + weights[(int64_t)t * K + (K - 1 - k)];"),
+    ("combine: returned row read with swapped stride",
+     "const uint16_t *src = y + ((int64_t)p * M + r) * H;",
+     "const uint16_t *src = y + ((int64_t)r * W + p) * H;"),
+    ("combine: separate multiply and add",
+     "acc[h] = fmaf(s, bf16_to_f32(src[h]), acc[h]);",
+     "acc[h] = s * bf16_to_f32(src[h]) + acc[h];"),
+    ("combine: PEs in reverse slot order",
+     "for (int32_t k0 = 0; k0 < K; ++k0) {",
+     "for (int32_t k0 = K - 1; k0 >= 0; --k0) {"),
+    ("combine: accumulator not cleared per token",
+     "for (int32_t h = 0; h < H; ++h) acc[h] = 0.0f;",
+     ";"),
+    ("bf16 rounding by truncation",
+     "u += 0x7fffu + lsb;",
+     "u += 0u * lsb;"),
+    ("bf16 rounding ties away from zero",
+     "u += 0x7fffu + lsb;",
+     "u += 0x8000u + 0u * lsb;"),
+]
+
+# cheapest checks first
+ORDER = [
+    pins.check_worked_example,
+    pins.check_brute_force_random,
+    pins.check_reading_fma_and_order,
+    pins.check_combine_identity_cases,
+    pins.check_combine_fp64_bound,
+    pins.check_brute_force_exhaustive,
+    pins.check_invariants,
+    pins.check_closed_form_unique_pairs,
+    pins.check_page_null_entries,
+    pins.check_page_staging_bytes,
+]
+
+
+@pytest.mark.parametrize("name,old,new", MUTANTS, ids=[m[0] for m in MUTANTS])
+def test_pins_catch_mutant(tmp_path, name, old, new):
+    src = open(oracle.SRC).read()
+    assert src.count(old) == 1, f"mutation site for '{name}' not unique in the oracle"
+    mpath = tmp_path / "mutant.c"
+    mpath.write_text(src.replace(old, new))
+    lib = oracle.load(oracle.build(str(mpath), str(tmp_path / "libmutant.so")))
+    for check in ORDER:
+        try:
+            fails = check(lib)
+        except Exception as e:  # a mutant that breaks a check's own preconditions is caught too
+            fails = [f"{check.__name__} raised {e!r}"]
+        if fails:
+            return
+    pytest.fail(f"no pin catches the mutant '{name}'")
