@@ -1,0 +1,194 @@
+#!/usr/bin/env python3
+"""Benchmark of one GPU's share of MoE EP dispatch + combine on an MI355X.
+
+A step is one pass of the whole path -- COUNT, SCAN, FINALIZE (epdc_dispatch)
+then COMBINE (epdc_combine) -- over one batch of seeded synthetic input that
+is already resident in HBM.  The default workload is the 4096-token,
+hiddenDim-7168 configuration (worldSize 8, 32 experts per rank, topk 8,
+Zipf(1.1) expert popularity, softmax weights).
+
+Prints one JSON line: whole-job HBM throughput from the algorithmic bytes of
+a step, the time per step, a roofline entry for the dominant kernel (HIP
+events around each launch in the timed region) and the CPU oracle timed on
+a bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+sys.path.insert(0, os.path.join(ROOT, "tests"))
+
+METRIC = "dispatch+combine µs and achieved HBM GB/s (% of peak), 1×MI355X"
+HBM_PEAK_GBPS = 8000.0
+PROFILES = os.path.join(ROOT, "profiles")
+KERNEL_SOURCES = [os.path.join(ROOT, "combine_count_amd", "csrc", f)
+                  for f in ("dispatch.hip", "combine.hip", "epdc_internal.h")]
+
+
+def parse_args():
+    ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="gen_zipf_h7168")
+    ap.add_argument("--seed", type=int, default=1)
+    ap.add_argument("--cpu-seconds", type=float, default=12.0,
+                    help="wall-clock budget of the CPU-oracle sample (0 disables it)")
+    return ap.parse_args()
+
+
+def algorithmic_bytes(w, U):
+    """Bytes the method must move (each input read once, each output written
+    once); U = unique (token, PE) pairs of the seeded input."""
+    T, K, H, W, s = w.numTokens, w.numExpertPerToken, w.hiddenDim, w.worldSize, 2
+    wt = 1 if w.useWeights else 0
+    disp = (T * H * s + T * K * 4 + wt * T * K * 4            # x, expertIds, weights
+            + U * H * s + U * 4 + U * K * 4 + wt * U * K * 4  # rows, token idx, ids, weights
+            + T * K * 4 + W * 4)                               # sendMap, recvCount
+    comb = T * K * 4 + wt * (T * K * 4 + T * K * 4) + U * H * s + T * H * s
+    return disp, comb
+
+
+def kernel_source_hash():
+    h = hashlib.sha256()
+    for p in KERNEL_SOURCES:
+        with open(p, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def read_traffic(kernel, workload):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, or
+    None if there is none or the kernels changed since it was taken."""
+    path = os.path.join(PROFILES, f"{kernel}_{workload}_pmc.txt")
+    if not os.path.exists(path):
+        return None
+    kv = {}
+    with open(path) as f:
+        for line in f:
+            if ":" in line and not line.startswith("#"):
+                k, v = line.split(":", 1)
+                kv[k.strip()] = v.strip()
+    if kv.get("kernel_source_sha256_16") != kernel_source_hash():
+        return None
+    try:
+        return float(kv["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def cpu_baseline(w, inp, budget_s, disp_b, comb_b):
+    import oracle
+    step, _ = oracle.timed_step(w.worldSize, w.hiddenDim, w.maxTokPerRank, w.numExpertPerRank,
+                                w.numExpertPerToken, w.useWeights, inp.x, inp.expertIds, inp.weights, inp.y)
+    step()  # untimed: page in the buffers
+    n, t0 = 0, time.perf_counter()
+    while True:
+        step()
+        n += 1
+        el = time.perf_counter() - t0
+        if el >= budget_s or n >= 1000:
+            break
+    return {"value": round((disp_b + comb_b) * n / el / 1e9, 3), "unit": "GB/s", "cores": 1,
+            "kind": "oracle",
+            "sample": f"{n} full dispatch+combine steps of {w.name} (seed {inp.seed}), single-threaded C "
+                      f"oracle, {el:.1f} s wall",
+            "ms_per_step": round(el / n * 1e3, 2)}
+
+
+def main():
+    args = parse_args()
+    if args.gpus != 1:
+        print(f"bench.py: --gpus {args.gpus}: this build runs one GPU's share of dispatch/combine on a "
+              "single GPU; multi-GPU runs are not part of it.", file=sys.stderr)
+        return 2
+    import numpy as np
+    import torch
+
+    import combine_count_amd as epdc
+    import workloads
+    from gpu_harness import GpuRun
+
+    w = workloads.CONFIGS[args.workload]
+    print(f"[bench] generating {w.name} seed {args.seed}", file=sys.stderr, flush=True)
+    inp = workloads.make_inputs(w, args.seed)
+    g = GpuRun(w, inp)
+    g.dispatch()
+    g.combine()
+    torch.cuda.synchronize()
+    U = int(g.recvCount.sum().item())
+    disp_b, comb_b = algorithmic_bytes(w, U)
+    stream = torch.cuda.current_stream()
+
+    print(f"[bench] warmup {args.warmup}", file=sys.stderr, flush=True)
+    for _ in range(args.warmup):
+        g.dispatch()
+        g.combine()
+    torch.cuda.synchronize()
+
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_start.record(stream)
+    for i in range(args.steps):
+        ev[i][0].record(stream)
+        g.dispatch()
+        ev[i][1].record(stream)
+        g.combine()
+        ev[i][2].record(stream)
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    total_ms = t_start.elapsed_time(t_end)
+    ms_step = total_ms / args.steps
+    d_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in ev]))
+    c_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in ev]))
+    print(f"[bench] U={U} dispatch {d_ms * 1e3:.1f} us ({disp_b / d_ms / 1e6:.0f} GB/s), combine "
+          f"{c_ms * 1e3:.1f} us ({comb_b / c_ms / 1e6:.0f} GB/s), step {ms_step * 1e3:.1f} us",
+          file=sys.stderr, flush=True)
+
+    if d_ms >= c_ms:
+        dom, dom_b, dom_ms = "dispatch", disp_b, d_ms
+    else:
+        dom, dom_b, dom_ms = "combine", comb_b, c_ms
+    achieved = dom_b / dom_ms / 1e6
+    roofline = {"bound": "hbm", "kernel": dom, "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS,
+                "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
+                "traffic": read_traffic(dom, w.name),
+                "us_per_launch": round(dom_ms * 1e3, 2), "algorithmic_bytes_per_launch": dom_b}
+
+    cpu = None
+    if args.cpu_seconds > 0:
+        print("[bench] timing the CPU oracle", file=sys.stderr, flush=True)
+        cpu = cpu_baseline(w, inp, args.cpu_seconds, disp_b, comb_b)
+
+    value = (disp_b + comb_b) / (ms_step * 1e-3) / 1e9
+    line = {
+        "metric": METRIC, "value": round(value, 1), "unit": "GB/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": w.name, "worldSize": w.worldSize, "numExpertPerRank": w.numExpertPerRank,
+                   "numTokens": w.numTokens, "maxTokPerRank": w.maxTokPerRank,
+                   "numExpertPerToken": w.numExpertPerToken, "hiddenDim": w.hiddenDim,
+                   "routing": w.routing + ("(s=1.1)" if w.routing == "zipf" else ""),
+                   "useWeights": w.useWeights, "seed": args.seed, "unique_token_pe_pairs": U,
+                   "bytes_per_step": disp_b + comb_b,
+                   "dispatch_us": round(d_ms * 1e3, 2), "combine_us": round(c_ms * 1e3, 2),
+                   "frac_of_hbm_peak": round(value / HBM_PEAK_GBPS, 4)},
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

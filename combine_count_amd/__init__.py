@@ -1,0 +1,11 @@
+"""MI355X-native MoE expert-parallel dispatch + combine (one GPU's share).
+
+The compute path is libepdc.so (hand-written HIP for gfx950) behind the C
+ABI in include/epdc.h; this package is its Python binding.
+"""
+from .binding import (EPDC_BF16, EXPORTS, EpCfg, EpdcError, epdc_combine, epdc_dispatch,
+                      epdc_dispatch_scratch_bytes, epdc_last_error, load_library)
+from .buffers import DispatchBuffers
+
+__all__ = ["EPDC_BF16", "EXPORTS", "EpCfg", "EpdcError", "epdc_combine", "epdc_dispatch",
+           "epdc_dispatch_scratch_bytes", "epdc_last_error", "load_library", "DispatchBuffers"]

@@ -1,0 +1,125 @@
+"""ctypes binding of libepdc.so (include/epdc.h), same entry-point names.
+
+Argument marshalling only: tensors become their device pointers, the stream
+defaults to torch's current stream, and a negative return code becomes an
+``EpdcError``.  Every step of dispatch and combine runs in the HIP kernels of
+libepdc.so; there is no other code path.  If the library is not built this
+module raises on first use.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libepdc.so")
+
+EPDC_BF16, EPDC_FP32, EPDC_FP8, EPDC_FP4X2 = 0, 1, 2, 3
+ERRORS = {
+    -1: "EPDC_ERR_INVALID_ARG",
+    -2: "EPDC_ERR_UNSUPPORTED",
+    -3: "EPDC_ERR_CAPACITY",
+    -4: "EPDC_ERR_ALIGN",
+    -5: "EPDC_ERR_NULLPTR",
+    -6: "EPDC_ERR_SCRATCH",
+    -7: "EPDC_ERR_HIP",
+}
+EXPORTS = ("epdc_dispatch_scratch_bytes", "epdc_dispatch", "epdc_combine", "epdc_last_error")
+
+
+class EpdcError(RuntimeError):
+    def __init__(self, code: int, message: str):
+        super().__init__(f"{ERRORS.get(code, code)}: {message}")
+        self.code = code
+
+
+class EpCfg(ctypes.Structure):
+    """epdc_cfg: field names as in the pages' EpCfg."""
+    _fields_ = [
+        ("worldSize", ctypes.c_int32),
+        ("hiddenDim", ctypes.c_int32),
+        ("maxTokPerRank", ctypes.c_int32),
+        ("numExpertPerRank", ctypes.c_int32),
+        ("numExpertPerToken", ctypes.c_int32),
+        ("dtype", ctypes.c_int32),
+        ("useWeights", ctypes.c_int32),
+    ]
+
+    def __repr__(self):
+        return "EpCfg(" + ", ".join(f"{n}={getattr(self, n)}" for n, _ in self._fields_) + ")"
+
+
+_lib = None
+
+
+def load_library() -> ctypes.CDLL:
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is not built: run __graft_entry__.build() "
+                           "(hipcc --offload-arch=gfx950); there is no fallback path")
+    lib = ctypes.CDLL(LIB_PATH)
+    p, i32, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t
+    cfgp = ctypes.POINTER(EpCfg)
+    lib.epdc_dispatch_scratch_bytes.restype = sz
+    lib.epdc_dispatch_scratch_bytes.argtypes = [cfgp]
+    lib.epdc_dispatch.restype = ctypes.c_int
+    lib.epdc_dispatch.argtypes = [cfgp, i32] + [p] * 10 + [sz, p]
+    lib.epdc_combine.restype = ctypes.c_int
+    lib.epdc_combine.argtypes = [cfgp, i32] + [p] * 5 + [p]
+    lib.epdc_last_error.restype = ctypes.c_char_p
+    lib.epdc_last_error.argtypes = []
+    _lib = lib
+    return lib
+
+
+def _ptr(a):
+    if a is None:
+        return None
+    if isinstance(a, int):
+        return a
+    return a.data_ptr()
+
+
+def _stream(s):
+    if s is None:
+        import torch
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(s, int):
+        return s
+    return s.cuda_stream
+
+
+def _check(rc: int, check: bool) -> int:
+    if rc != 0 and check:
+        raise EpdcError(rc, epdc_last_error())
+    return rc
+
+
+def epdc_last_error() -> str:
+    return load_library().epdc_last_error().decode()
+
+
+def epdc_dispatch_scratch_bytes(cfg: EpCfg) -> int:
+    return load_library().epdc_dispatch_scratch_bytes(ctypes.byref(cfg))
+
+
+def epdc_dispatch(cfg: EpCfg, numTokens: int, x, expertIds, weights, recvX, recvTokIdx, recvExpertIds,
+                  recvWeights, recvCount, sendMap, scratch, scratchBytes: int | None = None,
+                  stream=None, check: bool = True) -> int:
+    if scratchBytes is None:
+        scratchBytes = 0 if scratch is None or isinstance(scratch, int) else scratch.numel() * scratch.element_size()
+    rc = load_library().epdc_dispatch(
+        ctypes.byref(cfg), int(numTokens), _ptr(x), _ptr(expertIds), _ptr(weights), _ptr(recvX),
+        _ptr(recvTokIdx), _ptr(recvExpertIds), _ptr(recvWeights), _ptr(recvCount), _ptr(sendMap),
+        _ptr(scratch), int(scratchBytes), _stream(stream))
+    return _check(rc, check)
+
+
+def epdc_combine(cfg: EpCfg, numTokens: int, y, expertIds, weights, sendMap, out, stream=None,
+                 check: bool = True) -> int:
+    rc = load_library().epdc_combine(
+        ctypes.byref(cfg), int(numTokens), _ptr(y), _ptr(expertIds), _ptr(weights), _ptr(sendMap),
+        _ptr(out), _stream(stream))
+    return _check(rc, check)

@@ -1,0 +1,181 @@
+// EP combine for gfx950: gather + weighted reduction, fp32 accumulate,
+// bf16 (round to nearest even) out.
+//
+// MORI JIT v2 design doc, §5 and §9: the HIP backend's combine is a gather
+// (each token pulls the rows its PEs returned); §3.7: combine sums, so it
+// needs an arithmetic dtype (bf16 here).  mori PR #599 "Perf/ep disp 1250
+// ship", item "meta prefetch": the gather's per-token metadata (token
+// indices, weights) is loaded once, up front.
+//
+// One wave64 per (token, column slab of CPW chunks of 512 elements):
+//   * lanes k < K load the token's K sendMap entries, expert ids and weights
+//     once; a ballot over "sendMap >= 0" gives the kept slots, i.e. the
+//     token's PEs in first-appearance order;
+//   * lane k0 of a kept slot sums, in slot order from +0, the weights of the
+//     slots on its PE (read from the other lanes by shuffles);
+//   * the PE loop walks the kept slots in ascending order, the next PE's
+//     rows loaded while the current one is reduced (two register buffers);
+//     every lane owns 8 contiguous elements per chunk, one 16-byte access.
+#include "epdc_internal.h"
+
+namespace epdc {
+namespace {
+
+__device__ __forceinline__ float bf16lo(uint32_t u) { return __uint_as_float(u << 16); }
+__device__ __forceinline__ float bf16hi(uint32_t u) { return __uint_as_float(u & 0xffff0000u); }
+
+// fp32 -> bf16 bits, round to nearest, ties to even; NaN stays a quiet NaN.
+__device__ __forceinline__ uint32_t f32_to_bf16(float f) {
+    uint32_t u = __float_as_uint(f);
+    if ((u & 0x7fffffffu) > 0x7f800000u) return (u >> 16) | 0x40u;
+    u += 0x7fffu + ((u >> 16) & 1u);
+    return u >> 16;
+}
+
+__device__ __forceinline__ void fma8(float (&a)[8], float s, u32x4 v) {
+    a[0] = __builtin_fmaf(s, bf16lo(v.x), a[0]);
+    a[1] = __builtin_fmaf(s, bf16hi(v.x), a[1]);
+    a[2] = __builtin_fmaf(s, bf16lo(v.y), a[2]);
+    a[3] = __builtin_fmaf(s, bf16hi(v.y), a[3]);
+    a[4] = __builtin_fmaf(s, bf16lo(v.z), a[4]);
+    a[5] = __builtin_fmaf(s, bf16hi(v.z), a[5]);
+    a[6] = __builtin_fmaf(s, bf16lo(v.w), a[6]);
+    a[7] = __builtin_fmaf(s, bf16hi(v.w), a[7]);
+}
+
+// Loads chunks [slab*CPW, slab*CPW + CPW) of a row; with FULL every chunk is
+// known to be inside the row (H a multiple of 512, chunks a multiple of CPW).
+template <int CPW, bool FULL>
+__device__ __forceinline__ void load_slab(u32x4 (&v)[CPW], const uint16_t *row, int slab, int nChunks,
+                                          int H, int lane) {
+#pragma unroll
+    for (int c = 0; c < CPW; ++c) {
+        const int gc = slab * CPW + c;
+        const int e = gc * kChunkElems + lane * 8;
+        if (FULL || (gc < nChunks && e < H)) v[c] = *reinterpret_cast<const u32x4 *>(row + e);
+    }
+}
+
+// acc += sc[j] * row j for j = 0..N-1, in that order; all N rows' chunks are
+// loaded first.
+template <int N, int CPW, bool FULL>
+__device__ __forceinline__ void gather_reduce(float (&acc)[CPW][8], const CombineParams &P,
+                                              const int32_t (&fl)[8], const float (&sc)[8], int slab,
+                                              int lane) {
+    u32x4 v[N][CPW];
+#pragma unroll
+    for (int j = 0; j < N; ++j) load_slab<CPW, FULL>(v[j], P.y + (int64_t)fl[j] * P.H, slab, P.nChunks, P.H, lane);
+#pragma unroll
+    for (int j = 0; j < N; ++j)
+#pragma unroll
+        for (int c = 0; c < CPW; ++c) fma8(acc[c], sc[j], v[j][c]);
+}
+
+template <int CPW, bool FULL>
+__global__ __launch_bounds__(256) void combine_kernel(CombineParams P, int nSlabs) {
+    const int lane = threadIdx.x & 63;
+    const int item = blockIdx.x * 4 + (threadIdx.x >> 6);
+    const int32_t t = item / nSlabs;
+    const int slab = item - t * nSlabs;
+    if (t >= P.T) return;  // whole wave
+
+    // Per-token metadata, one slot per lane.
+    const int32_t E = P.W * P.Epr;
+    int32_t flat = -1, pe = -1;
+    float w = 0.0f;
+    if (lane < P.K) {
+        const int64_t o = (int64_t)t * P.K + lane;
+        flat = P.sendMap[o];
+        const int32_t e = P.expertIds[o];
+        if (e >= 0 && e < E) pe = P.eprShift >= 0 ? (e >> P.eprShift) : (e / P.Epr);
+        if (P.useWeights) w = P.weights[o];
+    }
+    // Kept slots; an entry outside [0, W*M) (not written by a dispatch of
+    // this cfg) counts as dropped rather than being read out of bounds.
+    const uint64_t kept = __ballot(lane < P.K && flat >= 0 && flat < P.W * P.M);
+
+    // Scale of each kept slot's PE: sum of the token's weights on that PE,
+    // in slot order starting from +0.
+    float s = 1.0f;
+    if (P.useWeights) {
+        s = 0.0f;
+        for (int k = 0; k < P.K; ++k) {
+            const int32_t pk = __shfl(pe, k);
+            const float wk = __shfl(w, k);
+            if (k >= lane && pe >= 0 && pk == pe) s = s + wk;
+        }
+    }
+
+    float acc[CPW][8];
+#pragma unroll
+    for (int c = 0; c < CPW; ++c)
+#pragma unroll
+        for (int j = 0; j < 8; ++j) acc[c][j] = 0.0f;
+
+    // PE loop over the kept slots in ascending order, in groups of up to 8:
+    // every row of a group is requested before the first is reduced, and the
+    // group is straight-line code, so each wait is for exactly one row.
+    uint64_t rem = kept;
+    while (rem) {
+        int32_t fl[8];
+        float sc[8];
+        int n = 0;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const int k = rem ? __builtin_ctzll(rem) : 0;
+            fl[j] = __builtin_amdgcn_readlane(flat, k);
+            sc[j] = __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(s), k));
+            n += rem ? 1 : 0;
+            rem &= rem - 1;
+        }
+        switch (n) {
+            case 1: gather_reduce<1, CPW, FULL>(acc, P, fl, sc, slab, lane); break;
+            case 2: gather_reduce<2, CPW, FULL>(acc, P, fl, sc, slab, lane); break;
+            case 3: gather_reduce<3, CPW, FULL>(acc, P, fl, sc, slab, lane); break;
+            case 4: gather_reduce<4, CPW, FULL>(acc, P, fl, sc, slab, lane); break;
+            case 5: gather_reduce<5, CPW, FULL>(acc, P, fl, sc, slab, lane); break;
+            case 6: gather_reduce<6, CPW, FULL>(acc, P, fl, sc, slab, lane); break;
+            case 7: gather_reduce<7, CPW, FULL>(acc, P, fl, sc, slab, lane); break;
+            default: gather_reduce<8, CPW, FULL>(acc, P, fl, sc, slab, lane); break;
+        }
+    }
+
+    uint16_t *orow = P.out + (int64_t)t * P.H;
+#pragma unroll
+    for (int c = 0; c < CPW; ++c) {
+        const int gc = slab * CPW + c;
+        const int e = gc * kChunkElems + lane * 8;
+        if (FULL || (gc < P.nChunks && e < P.H)) {
+            u32x4 o;
+            o.x = f32_to_bf16(acc[c][0]) | (f32_to_bf16(acc[c][1]) << 16);
+            o.y = f32_to_bf16(acc[c][2]) | (f32_to_bf16(acc[c][3]) << 16);
+            o.z = f32_to_bf16(acc[c][4]) | (f32_to_bf16(acc[c][5]) << 16);
+            o.w = f32_to_bf16(acc[c][6]) | (f32_to_bf16(acc[c][7]) << 16);
+            *reinterpret_cast<u32x4 *>(orow + e) = o;
+        }
+    }
+}
+
+template <int CPW>
+hipError_t launch(const CombineParams &P, hipStream_t stream) {
+    const int nSlabs = ceil_div(P.nChunks, CPW);
+    const int64_t waves = (int64_t)P.T * nSlabs;
+    const bool full = (P.H % kChunkElems == 0) && (P.nChunks % CPW == 0);
+    if (full)
+        hipLaunchKernelGGL((combine_kernel<CPW, true>), dim3(ceil_div(waves, 4)), dim3(256), 0, stream, P,
+                           nSlabs);
+    else
+        hipLaunchKernelGGL((combine_kernel<CPW, false>), dim3(ceil_div(waves, 4)), dim3(256), 0, stream, P,
+                           nSlabs);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_combine(const CombineParams &P, hipStream_t stream) {
+    if (P.T == 0) return hipSuccess;
+    if (P.nChunks % 2 == 0 && (int64_t)P.T * (P.nChunks / 2) >= 8192) return launch<2>(P, stream);
+    return launch<1>(P, stream);
+}
+
+}  // namespace epdc

@@ -1,0 +1,189 @@
+// Host side of the C ABI declared in include/epdc.h: argument checks, error
+// reporting and the launch.  Every check runs before anything is enqueued;
+// no entry point lets an exception escape (MORI JIT v2 design doc, §6: all
+// C entry points are noexcept and report through a last-error string).
+#include "../../include/epdc.h"
+
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdio>
+#include <string>
+
+#include "epdc_internal.h"
+
+namespace {
+
+thread_local std::string g_lastError;
+
+int fail(int code, const char *fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    g_lastError = buf;
+    return code;
+}
+
+bool aligned(const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+int32_t pow2_ceil(int32_t v) {
+    int32_t r = 1;
+    while (r < v) r <<= 1;
+    return r;
+}
+
+int32_t log2_exact(int32_t v) {
+    if (v <= 0 || (v & (v - 1))) return -1;
+    int32_t s = 0;
+    while ((1 << s) < v) ++s;
+    return s;
+}
+
+// Checks shared by both entry points (EpCfg validity: MORI JIT v2 design doc,
+// §3.5 -- 16-byte token rows, topk and worldSize within one wavefront,
+// receive capacity covering the worst case).
+int check_cfg(const epdc_cfg *c, int32_t numTokens) {
+    if (!c) return fail(EPDC_ERR_NULLPTR, "cfg is NULL");
+    if (c->worldSize < 1 || c->worldSize > 64)
+        return fail(EPDC_ERR_INVALID_ARG, "worldSize %d outside [1, 64]", c->worldSize);
+    if (c->numExpertPerToken < 1 || c->numExpertPerToken > 64)
+        return fail(EPDC_ERR_INVALID_ARG, "numExpertPerToken %d outside [1, 64]", c->numExpertPerToken);
+    if (c->numExpertPerRank < 1)
+        return fail(EPDC_ERR_INVALID_ARG, "numExpertPerRank %d < 1", c->numExpertPerRank);
+    const int64_t E = (int64_t)c->worldSize * c->numExpertPerRank;
+    if (E > INT32_MAX) return fail(EPDC_ERR_INVALID_ARG, "worldSize*numExpertPerRank overflows int32");
+    if (c->numExpertPerToken > E)
+        return fail(EPDC_ERR_INVALID_ARG, "numExpertPerToken %d > number of experts %lld",
+                    c->numExpertPerToken, (long long)E);
+    if (c->hiddenDim < 1) return fail(EPDC_ERR_INVALID_ARG, "hiddenDim %d < 1", c->hiddenDim);
+    if (c->maxTokPerRank < 1) return fail(EPDC_ERR_INVALID_ARG, "maxTokPerRank %d < 1", c->maxTokPerRank);
+    if ((int64_t)c->worldSize * c->maxTokPerRank > INT32_MAX)
+        return fail(EPDC_ERR_INVALID_ARG, "worldSize*maxTokPerRank overflows the int32 flat index");
+    if (c->dtype != EPDC_BF16)
+        return fail(EPDC_ERR_UNSUPPORTED, "dtype %d not supported (only EPDC_BF16 = 0)", c->dtype);
+    if (c->useWeights != 0 && c->useWeights != 1)
+        return fail(EPDC_ERR_UNSUPPORTED, "useWeights must be 0 or 1, got %d", c->useWeights);
+    if (((int64_t)c->hiddenDim * 2) % 16 != 0)
+        return fail(EPDC_ERR_ALIGN, "hiddenDim*2 = %lld bytes is not a multiple of 16",
+                    (long long)c->hiddenDim * 2);
+    if (numTokens < 0) return fail(EPDC_ERR_INVALID_ARG, "numTokens %d < 0", numTokens);
+    if (numTokens > c->maxTokPerRank)
+        return fail(EPDC_ERR_CAPACITY, "numTokens %d > maxTokPerRank %d", numTokens, c->maxTokPerRank);
+    return EPDC_OK;
+}
+
+size_t scratch_bytes(const epdc_cfg *c) {
+    const int64_t nTiles = ((int64_t)c->maxTokPerRank + epdc::kTile - 1) / epdc::kTile;
+    return (size_t)(nTiles * pow2_ceil(c->worldSize) * sizeof(int32_t));
+}
+
+int hip_status(hipError_t e, const char *what) {
+    if (e == hipSuccess) return EPDC_OK;
+    return fail(EPDC_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t epdc_dispatch_scratch_bytes(const epdc_cfg *cfg) {
+    try {
+        if (check_cfg(cfg, 0) != EPDC_OK) return 0;
+        return scratch_bytes(cfg);
+    } catch (...) {
+        return 0;
+    }
+}
+
+int epdc_dispatch(const epdc_cfg *cfg, int32_t numTokens, const void *x, const int32_t *expertIds,
+                  const float *weights, void *recvX, int32_t *recvTokIdx, int32_t *recvExpertIds,
+                  float *recvWeights, int32_t *recvCount, int32_t *sendMap, void *scratch,
+                  size_t scratchBytes, void *stream) {
+    try {
+        g_lastError.clear();
+        int rc = check_cfg(cfg, numTokens);
+        if (rc != EPDC_OK) return rc;
+        if (!recvCount) return fail(EPDC_ERR_NULLPTR, "recvCount is NULL");
+        if (!aligned(recvCount, 4)) return fail(EPDC_ERR_ALIGN, "recvCount not 4-byte aligned");
+        if (numTokens > 0) {
+            if (!x || !expertIds || !recvX || !recvTokIdx || !recvExpertIds || !sendMap || !scratch)
+                return fail(EPDC_ERR_NULLPTR, "a required dispatch pointer is NULL");
+            if (cfg->useWeights && (!weights || !recvWeights))
+                return fail(EPDC_ERR_NULLPTR, "useWeights=1 needs weights and recvWeights");
+            if (!aligned(x, 16) || !aligned(recvX, 16))
+                return fail(EPDC_ERR_ALIGN, "x and recvX must be 16-byte aligned");
+            if (!aligned(expertIds, 4) || !aligned(recvTokIdx, 4) || !aligned(recvExpertIds, 4) ||
+                !aligned(sendMap, 4) || !aligned(scratch, 4) ||
+                (cfg->useWeights && (!aligned(weights, 4) || !aligned(recvWeights, 4))))
+                return fail(EPDC_ERR_ALIGN, "int32/fp32 arrays and scratch must be 4-byte aligned");
+            if (scratchBytes < scratch_bytes(cfg))
+                return fail(EPDC_ERR_SCRATCH, "scratchBytes %zu < %zu required", scratchBytes,
+                            scratch_bytes(cfg));
+        }
+        epdc::DispatchParams P{};
+        P.W = cfg->worldSize;
+        P.H = cfg->hiddenDim;
+        P.M = cfg->maxTokPerRank;
+        P.Epr = cfg->numExpertPerRank;
+        P.K = cfg->numExpertPerToken;
+        P.T = numTokens;
+        P.useWeights = cfg->useWeights;
+        P.Wp = pow2_ceil(cfg->worldSize);
+        P.eprShift = log2_exact(cfg->numExpertPerRank);
+        P.nChunks = epdc::ceil_div(cfg->hiddenDim, epdc::kChunkElems);
+        P.x = static_cast<const uint16_t *>(x);
+        P.expertIds = expertIds;
+        P.weights = cfg->useWeights ? weights : nullptr;
+        P.recvX = static_cast<uint16_t *>(recvX);
+        P.recvTokIdx = recvTokIdx;
+        P.recvExpertIds = recvExpertIds;
+        P.recvWeights = cfg->useWeights ? recvWeights : nullptr;
+        P.recvCount = recvCount;
+        P.sendMap = sendMap;
+        P.tileCount = static_cast<int32_t *>(scratch);
+        return hip_status(epdc::launch_dispatch(P, static_cast<hipStream_t>(stream)), "dispatch launch");
+    } catch (...) {
+        return fail(EPDC_ERR_HIP, "unexpected C++ exception in epdc_dispatch");
+    }
+}
+
+int epdc_combine(const epdc_cfg *cfg, int32_t numTokens, const void *y, const int32_t *expertIds,
+                 const float *weights, const int32_t *sendMap, void *out, void *stream) {
+    try {
+        g_lastError.clear();
+        int rc = check_cfg(cfg, numTokens);
+        if (rc != EPDC_OK) return rc;
+        if (numTokens == 0) return EPDC_OK;
+        if (!y || !expertIds || !sendMap || !out)
+            return fail(EPDC_ERR_NULLPTR, "a required combine pointer is NULL");
+        if (cfg->useWeights && !weights) return fail(EPDC_ERR_NULLPTR, "useWeights=1 needs weights");
+        if (!aligned(y, 16) || !aligned(out, 16))
+            return fail(EPDC_ERR_ALIGN, "y and out must be 16-byte aligned");
+        if (!aligned(expertIds, 4) || !aligned(sendMap, 4) || (cfg->useWeights && !aligned(weights, 4)))
+            return fail(EPDC_ERR_ALIGN, "int32/fp32 arrays must be 4-byte aligned");
+        epdc::CombineParams P{};
+        P.W = cfg->worldSize;
+        P.H = cfg->hiddenDim;
+        P.M = cfg->maxTokPerRank;
+        P.Epr = cfg->numExpertPerRank;
+        P.K = cfg->numExpertPerToken;
+        P.T = numTokens;
+        P.useWeights = cfg->useWeights;
+        P.eprShift = log2_exact(cfg->numExpertPerRank);
+        P.nChunks = epdc::ceil_div(cfg->hiddenDim, epdc::kChunkElems);
+        P.y = static_cast<const uint16_t *>(y);
+        P.expertIds = expertIds;
+        P.weights = cfg->useWeights ? weights : nullptr;
+        P.sendMap = sendMap;
+        P.out = static_cast<uint16_t *>(out);
+        return hip_status(epdc::launch_combine(P, static_cast<hipStream_t>(stream)), "combine launch");
+    } catch (...) {
+        return fail(EPDC_ERR_HIP, "unexpected C++ exception in epdc_combine");
+    }
+}
+
+const char *epdc_last_error(void) { return g_lastError.c_str(); }
+
+}  // extern "C"

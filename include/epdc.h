@@ -1,0 +1,148 @@
+/*
+ * epdc.h -- C ABI of libepdc.so: one source rank's share of MoE
+ * expert-parallel token dispatch and combine on one MI355X (gfx950).
+ *
+ * Operations (definitions from the pages):
+ *   dispatch  COUNT -> SCAN -> FINALIZE.  mori PR #599 "Perf/ep disp 1250
+ *             ship", items "ballot dedup" and "cached destPe/keep + deferred
+ *             null write": each (token, top-k slot) maps to a destination PE;
+ *             a token reaches each PE at most once; the rows and per-token
+ *             metadata are written into per-PE receive windows and every
+ *             dropped slot gets a 4-byte null entry.  Dispatch only moves bytes
+ *             (MORI JIT v2 design doc, §3.7).
+ *   combine   MORI JIT v2 design doc, §5 and §9: a gather combine -- each token
+ *             pulls the rows its PEs returned and reduces them.
+ *
+ * Argument names follow EpCfg (MORI JIT v2 design doc, §3.2).  The geometry
+ * fields of EpCfg (blockNum, warpPerBlock, waveSize) are not part of the ABI:
+ * the library picks launch geometry itself.
+ *
+ * Conventions for every entry point:
+ *   - Every pointer named "device" is device memory owned by the caller; the
+ *     library allocates nothing, copies nothing to the host and never
+ *     synchronises.  Calls are asynchronous on `stream` (a hipStream_t; NULL
+ *     is the default stream), so they can be captured into a HIP graph.
+ *   - All checks run on the host before any launch.  On failure a negative
+ *     EPDC_ERR_* code is returned, nothing is launched, and epdc_last_error()
+ *     describes the failure.  No entry point throws.
+ *   - Index layout: T = numTokens, K = numExpertPerToken, W = worldSize,
+ *     M = maxTokPerRank, H = hiddenDim, Epr = numExpertPerRank, E = W*Epr.
+ *     All arrays are dense row-major with exactly these extents.
+ */
+#ifndef EPDC_H
+#define EPDC_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Wire dtype numbering kept equal to the pages' EpDType (MORI JIT v2 design
+ * doc, §3.7 and §7: the enum values must match the binding's table). */
+typedef enum {
+    EPDC_BF16 = 0,
+    EPDC_FP32 = 1,
+    EPDC_FP8 = 2,
+    EPDC_FP4X2 = 3
+} epdc_dtype;
+
+enum {
+    EPDC_OK = 0,
+    EPDC_ERR_INVALID_ARG = -1, /* a cfg field out of range, numTokens < 0, K > E, W*M too large */
+    EPDC_ERR_UNSUPPORTED = -2, /* dtype other than EPDC_BF16, useWeights not 0/1              */
+    EPDC_ERR_CAPACITY = -3,    /* numTokens > maxTokPerRank                                    */
+    EPDC_ERR_ALIGN = -4,       /* hiddenDim*2 not a multiple of 16, or a misaligned pointer    */
+    EPDC_ERR_NULLPTR = -5,     /* a required pointer (or cfg) is NULL                          */
+    EPDC_ERR_SCRATCH = -6,     /* scratchBytes below epdc_dispatch_scratch_bytes(cfg)          */
+    EPDC_ERR_HIP = -7          /* the HIP runtime reported an error (no device, launch failed) */
+};
+
+/* Shape and options of one dispatch/combine pair (EpCfg field names).
+ *   worldSize          W, 1..64 (one bit per PE in a 64-lane wavefront)
+ *   hiddenDim          H elements per token row; H*2 bytes must be a multiple of 16
+ *   maxTokPerRank      M >= 1: capacity of x and of each receive window, in rows;
+ *                      W*M must not exceed 2^31-1 (flat indices are int32)
+ *   numExpertPerRank   Epr >= 1; expert e lives on PE e / Epr
+ *   numExpertPerToken  K, 1..64, K <= E
+ *   dtype              EPDC_BF16 only
+ *   useWeights         1: dispatch copies the weights, combine applies them; 0: ignored */
+typedef struct epdc_cfg {
+    int32_t worldSize;
+    int32_t hiddenDim;
+    int32_t maxTokPerRank;
+    int32_t numExpertPerRank;
+    int32_t numExpertPerToken;
+    int32_t dtype;
+    int32_t useWeights;
+} epdc_cfg;
+
+/* Bytes of device scratch epdc_dispatch needs for this cfg (a few KB: one
+ * int32 per (64-token tile, PE)).  Returns 0 if cfg is invalid.  The scratch
+ * holds no state between calls; it needs no initialisation. */
+size_t epdc_dispatch_scratch_bytes(const epdc_cfg *cfg);
+
+/*
+ * Dispatch numTokens tokens (0 <= numTokens <= maxTokPerRank).
+ *
+ * Inputs (device, read only):
+ *   x            [T][H] bf16 token rows, 16-byte aligned
+ *   expertIds    [T][K] int32 top-k expert ids; an id outside [0, E) marks a
+ *                dropped slot (ids are not range-checked on the host)
+ *   weights      [T][K] fp32; may be NULL iff useWeights == 0
+ * Outputs (device, written):
+ *   recvX          [W][M][H] bf16, 16-byte aligned: recvX[p][r] is a bitwise copy
+ *                  of the r-th token (ascending token order) that reaches PE p
+ *   recvTokIdx     [W][M] int32: that token's index
+ *   recvExpertIds  [W][M][K] int32: that token's K expert ids
+ *   recvWeights    [W][M][K] fp32: that token's K weights; NULL iff useWeights == 0
+ *   recvCount      [W] int32: rows written per PE -- stored, not accumulated
+ *                  (mori PR #599 follow-up commits: the dispatch stores the
+ *                  received count, so callers need no reset kernel)
+ *   sendMap        [T][K] int32: for the lowest slot k of token t on PE p,
+ *                  p*M + r; for every other slot (duplicate PE or invalid
+ *                  id) -1, the null entry
+ *   Rows r >= recvCount[p] of every window are left untouched.
+ * Scratch (device): at least epdc_dispatch_scratch_bytes(cfg) bytes, 4-byte
+ *   aligned; two calls in flight at once need two scratch buffers.
+ * With numTokens == 0 only recvCount is written (zeros); the token-sized
+ * pointers may then be NULL.
+ */
+int epdc_dispatch(const epdc_cfg *cfg, int32_t numTokens,
+                  const void *x, const int32_t *expertIds, const float *weights,
+                  void *recvX, int32_t *recvTokIdx, int32_t *recvExpertIds,
+                  float *recvWeights, int32_t *recvCount, int32_t *sendMap,
+                  void *scratch, size_t scratchBytes, void *stream);
+
+/*
+ * Combine numTokens tokens from the rows their PEs returned.
+ *
+ * Inputs (device, read only):
+ *   y          [W][M][H] bf16, 16-byte aligned: returned rows, indexed like recvX
+ *   expertIds  [T][K] int32, the ids given to the matching dispatch
+ *   weights    [T][K] fp32 or NULL iff useWeights == 0
+ *   sendMap    [T][K] int32 as written by the matching dispatch
+ * Output (device): out [T][H] bf16, 16-byte aligned.
+ *
+ * For token t, the PEs of its kept slots (sendMap >= 0) are visited in
+ * ascending slot order.  PE p's scale is the fp32 sum, in slot order from +0,
+ * of the weights of t's slots whose valid expert lives on p (1 when
+ * useWeights == 0).  out[t][h] = bf16_rne(acc), acc = fmaf(scale_p,
+ * y[p][r_p][h], acc) over those PEs from acc = +0.  A token with no kept slot
+ * yields +0.  A sendMap entry outside [0, W*M) counts as a dropped slot.
+ * Results are deterministic and bit-identical run to run.
+ */
+int epdc_combine(const epdc_cfg *cfg, int32_t numTokens,
+                 const void *y, const int32_t *expertIds, const float *weights,
+                 const int32_t *sendMap, void *out, void *stream);
+
+/* Message for the last failing call on this thread ("" if none).  The
+ * pointer stays valid until the next epdc_* call on the same thread. */
+const char *epdc_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* EPDC_H */

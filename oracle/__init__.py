@@ -123,3 +123,33 @@ def combine(W, H, M, Epr, K, useWeights, y, expertIds, weights, sendMap, tokens=
     if rc != 0:
         raise ValueError(f"oracle_combine rejected its arguments ({rc})")
     return out
+
+
+def timed_step(W, H, M, Epr, K, useWeights, x, expertIds, weights, y, lib=None):
+    """A callable running one oracle dispatch + combine into preallocated
+    buffers (allocation kept out of the timed call), for bench.py's CPU
+    baseline.  Returns (step, outputs)."""
+    lib = lib or load()
+    T = x.shape[0]
+    outs = dict(
+        recvX=np.empty((W, M, H), np.uint16), recvTokIdx=np.empty((W, M), np.int32),
+        recvExpertIds=np.empty((W, M, K), np.int32), recvWeights=np.empty((W, M, K), np.float32),
+        recvCount=np.empty((W,), np.int32), sendMap=np.empty((T, K), np.int32),
+        out=np.empty((T, H), np.uint16), acc=np.empty((H,), np.float32))
+    x = np.ascontiguousarray(x, dtype=np.uint16)
+    expertIds = np.ascontiguousarray(expertIds, dtype=np.int32)
+    weights = np.ascontiguousarray(weights, dtype=np.float32) if useWeights else None
+    y = np.ascontiguousarray(y, dtype=np.uint16)
+    o = outs
+
+    def step():
+        rc = lib.oracle_dispatch(W, H, M, Epr, K, int(useWeights), T, _ptr(x), _ptr(expertIds),
+                                 _ptr(weights), _ptr(o["recvX"]), _ptr(o["recvTokIdx"]),
+                                 _ptr(o["recvExpertIds"]), _ptr(o["recvWeights"]), _ptr(o["recvCount"]),
+                                 _ptr(o["sendMap"]))
+        rc |= lib.oracle_combine(W, H, M, Epr, K, int(useWeights), T, _ptr(y), _ptr(expertIds),
+                                 _ptr(weights), _ptr(o["sendMap"]), None, T, _ptr(o["acc"]), _ptr(o["out"]))
+        if rc:
+            raise RuntimeError("oracle step failed")
+
+    return step, outs

@@ -1,0 +1,116 @@
+"""Helpers that run the HIP library and the oracle on the same seeded inputs.
+
+Windows are pre-filled with the same sentinels on both sides, so whole-buffer
+equality also proves that rows past recvCount are left untouched and that no
+row is written twice or elsewhere.
+"""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+import combine_count_amd as epdc
+import oracle
+import workloads
+
+SENT_X = 0xDEAD           # bf16 bits
+SENT_I32 = -12345
+SENT_IDS = -777
+SENT_W = -3.5
+SENT_MAP = -99
+FILL = {"recvX": SENT_X, "recvTokIdx": SENT_I32, "recvExpertIds": SENT_IDS, "recvWeights": SENT_W}
+
+
+def cfg_of(w: workloads.Workload) -> epdc.EpCfg:
+    return epdc.EpCfg(w.worldSize, w.hiddenDim, w.maxTokPerRank, w.numExpertPerRank,
+                      w.numExpertPerToken, epdc.EPDC_BF16, w.useWeights)
+
+
+def bits_to_dev(bits: np.ndarray, dev="cuda") -> torch.Tensor:
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).to(dev).view(torch.bfloat16)
+
+
+def dev_to_bits(t: torch.Tensor) -> np.ndarray:
+    return t.view(torch.int16).cpu().numpy().view(np.uint16)
+
+
+class GpuRun:
+    """Device copies of one input set plus sentinel-filled dispatch outputs."""
+
+    def __init__(self, w: workloads.Workload, inp: workloads.Inputs, dev="cuda"):
+        self.w = w
+        self.cfg = cfg_of(w)
+        W, M, H, K, T = w.worldSize, w.maxTokPerRank, w.hiddenDim, w.numExpertPerToken, w.numTokens
+        self.x = bits_to_dev(inp.x, dev)
+        self.ids = torch.from_numpy(inp.expertIds).to(dev)
+        self.wts = torch.from_numpy(inp.weights).to(dev) if w.useWeights else None
+        self.y = bits_to_dev(inp.y, dev) if inp.y is not None else None
+        self.recvX = torch.full((W, M, H), np.int16(np.uint16(SENT_X).view(np.int16)), dtype=torch.int16,
+                                device=dev).view(torch.bfloat16)
+        self.recvTokIdx = torch.full((W, M), SENT_I32, dtype=torch.int32, device=dev)
+        self.recvExpertIds = torch.full((W, M, K), SENT_IDS, dtype=torch.int32, device=dev)
+        self.recvWeights = torch.full((W, M, K), SENT_W, dtype=torch.float32, device=dev)
+        self.recvCount = torch.full((W,), -7, dtype=torch.int32, device=dev)
+        self.sendMap = torch.full((T, K), SENT_MAP, dtype=torch.int32, device=dev)
+        nb = epdc.epdc_dispatch_scratch_bytes(self.cfg)
+        self.scratch = torch.zeros(max(nb, 4) // 4 + 1, dtype=torch.int32, device=dev)
+        self.out = torch.full((T, H), 0x7FC1, dtype=torch.int16, device=dev).view(torch.bfloat16)
+
+    def dispatch(self, stream=None):
+        w = self.w
+        return epdc.epdc_dispatch(self.cfg, w.numTokens, self.x, self.ids, self.wts, self.recvX,
+                                  self.recvTokIdx, self.recvExpertIds,
+                                  self.recvWeights if w.useWeights else None, self.recvCount,
+                                  self.sendMap, self.scratch, stream=stream)
+
+    def combine(self, y=None, weights="default", stream=None):
+        w = self.w
+        wts = self.wts if weights == "default" else weights
+        return epdc.epdc_combine(self.cfg, w.numTokens, self.y if y is None else y, self.ids,
+                                 wts if w.useWeights else None, self.sendMap, self.out, stream=stream)
+
+
+def oracle_dispatch(w: workloads.Workload, inp: workloads.Inputs):
+    return oracle.dispatch(w.worldSize, w.hiddenDim, w.maxTokPerRank, w.numExpertPerRank,
+                           w.numExpertPerToken, w.useWeights, inp.x, inp.expertIds,
+                           inp.weights if w.useWeights else None, fill=FILL)
+
+
+def oracle_combine(w: workloads.Workload, y_bits, inp: workloads.Inputs, sendMap, tokens=None, weights=None):
+    wts = inp.weights if weights is None else weights
+    return oracle.combine(w.worldSize, w.hiddenDim, w.maxTokPerRank, w.numExpertPerRank,
+                          w.numExpertPerToken, w.useWeights, y_bits, inp.expertIds,
+                          wts if w.useWeights else None, sendMap, tokens=tokens)
+
+
+def assert_dispatch_equal(g: GpuRun, o, tag=""):
+    """Every dispatch output, whole buffers, bit for bit."""
+    w = g.w
+    cnt = g.recvCount.cpu().numpy()
+    assert np.array_equal(cnt, o.recvCount), f"{tag} recvCount {cnt} != oracle {o.recvCount}"
+    smap = g.sendMap.cpu().numpy()
+    if not np.array_equal(smap, o.sendMap):
+        bad = np.argwhere(smap != o.sendMap)[0]
+        raise AssertionError(f"{tag} sendMap differs first at {bad.tolist()}: "
+                             f"{smap[tuple(bad)]} vs {o.sendMap[tuple(bad)]}")
+    tok = g.recvTokIdx.cpu().numpy()
+    assert np.array_equal(tok, o.recvTokIdx), f"{tag} recvTokIdx differs"
+    ids = g.recvExpertIds.cpu().numpy()
+    assert np.array_equal(ids, o.recvExpertIds), f"{tag} recvExpertIds differs"
+    wt = g.recvWeights.cpu().numpy()
+    if w.useWeights:
+        assert np.array_equal(wt.view(np.uint32), o.recvWeights.view(np.uint32)), f"{tag} recvWeights differs"
+    else:
+        assert (wt == np.float32(SENT_W)).all(), f"{tag} recvWeights written with useWeights=0"
+    rx = dev_to_bits(g.recvX)
+    if not np.array_equal(rx, o.recvX):
+        bad = np.argwhere(rx != o.recvX)[0]
+        raise AssertionError(f"{tag} recvX differs first at {bad.tolist()}")
+
+
+def assert_bits_equal(got: np.ndarray, exp: np.ndarray, tag=""):
+    if not np.array_equal(got, exp):
+        bad = np.argwhere(got != exp)
+        t, h = bad[0]
+        raise AssertionError(f"{tag} {len(bad)} elements differ; first out[{t}][{h}] = "
+                             f"{hex(int(got[t, h]))} vs oracle {hex(int(exp[t, h]))}")

@@ -1,0 +1,147 @@
+"""The C ABI on a host with or without a GPU: the library loads, exports
+every symbol include/epdc.h declares, and rejects every invalid argument on
+the host with its documented code before anything is launched."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+import combine_count_amd as epdc
+from combine_count_amd.binding import LIB_PATH
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "epdc.h")
+
+OK_CFG = dict(worldSize=8, hiddenDim=7168, maxTokPerRank=4096, numExpertPerRank=32,
+              numExpertPerToken=8, dtype=0, useWeights=1)
+P16 = 0x10000  # a fake, 16-byte aligned device address: never dereferenced on these paths
+
+
+def cfg(**kw):
+    d = dict(OK_CFG)
+    d.update(kw)
+    return epdc.EpCfg(**d)
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(epdc_[a-z_]+)\s*\(", src)))
+
+
+def test_header_declares_the_binding_exports():
+    assert declared_functions() == sorted(epdc.EXPORTS)
+
+
+def test_library_exports_every_declared_symbol():
+    lib = ctypes.CDLL(LIB_PATH)
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+    nm = subprocess.run(["nm", "-D", "--defined-only", LIB_PATH], capture_output=True, text=True, check=True)
+    exported = set(re.findall(r" T (epdc_\w+)", nm.stdout))
+    assert set(declared_functions()) <= exported
+
+
+def test_header_compiles_as_c():
+    r = subprocess.run(["gcc", "-std=c99", "-Wall", "-Werror", "-fsyntax-only", "-x", "c", HEADER],
+                       capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr
+
+
+def test_scratch_bytes():
+    assert epdc.epdc_dispatch_scratch_bytes(cfg()) == (4096 // 64) * 8 * 4
+    assert epdc.epdc_dispatch_scratch_bytes(cfg(worldSize=5, maxTokPerRank=65)) == 2 * 8 * 4
+    assert epdc.epdc_dispatch_scratch_bytes(cfg(hiddenDim=7170)) == 0
+
+
+def _dispatch(c, T, **ptrs):
+    args = dict(x=P16, expertIds=P16, weights=P16, recvX=P16, recvTokIdx=P16, recvExpertIds=P16,
+                recvWeights=P16, recvCount=P16, sendMap=P16, scratch=P16)
+    args.update(ptrs)
+    return epdc.epdc_dispatch(c, T, args["x"], args["expertIds"], args["weights"], args["recvX"],
+                              args["recvTokIdx"], args["recvExpertIds"], args["recvWeights"],
+                              args["recvCount"], args["sendMap"], args["scratch"],
+                              scratchBytes=ptrs.get("scratchBytes", 1 << 20), stream=0, check=False)
+
+
+def _combine(c, T, **ptrs):
+    args = dict(y=P16, expertIds=P16, weights=P16, sendMap=P16, out=P16)
+    args.update(ptrs)
+    return epdc.epdc_combine(c, T, args["y"], args["expertIds"], args["weights"], args["sendMap"],
+                             args["out"], stream=0, check=False)
+
+
+REJECT = [
+    # (what, cfg overrides, numTokens, pointer overrides, expected code)
+    ("worldSize 0", dict(worldSize=0), 8, {}, -1),
+    ("worldSize 65", dict(worldSize=65), 8, {}, -1),
+    ("topk 0", dict(numExpertPerToken=0), 8, {}, -1),
+    ("topk 65", dict(numExpertPerToken=65), 8, {}, -1),
+    ("topk > experts", dict(worldSize=2, numExpertPerRank=2, numExpertPerToken=5), 8, {}, -1),
+    ("numExpertPerRank 0", dict(numExpertPerRank=0), 8, {}, -1),
+    ("hiddenDim 0", dict(hiddenDim=0), 8, {}, -1),
+    ("maxTokPerRank 0", dict(maxTokPerRank=0), 0, {}, -1),
+    ("flat index overflow", dict(worldSize=64, maxTokPerRank=40_000_000), 8, {}, -1),
+    ("negative tokens", {}, -1, {}, -1),
+    ("dtype fp8", dict(dtype=2), 8, {}, -2),
+    ("dtype fp32", dict(dtype=1), 8, {}, -2),
+    ("useWeights 2", dict(useWeights=2), 8, {}, -2),
+    ("capacity", {}, 4097, {}, -3),
+    ("row bytes not 16-aligned", dict(hiddenDim=7164), 8, {}, -4),
+    ("x misaligned", {}, 8, dict(x=P16 + 8), -4),
+    ("recvX misaligned", {}, 8, dict(recvX=P16 + 4), -4),
+    ("ids misaligned", {}, 8, dict(expertIds=P16 + 2), -4),
+    ("x null", {}, 8, dict(x=None), -5),
+    ("sendMap null", {}, 8, dict(sendMap=None), -5),
+    ("recvCount null", {}, 0, dict(recvCount=None), -5),
+    ("weights null with useWeights", {}, 8, dict(weights=None), -5),
+    ("recvWeights null with useWeights", {}, 8, dict(recvWeights=None), -5),
+    ("scratch too small", {}, 8, dict(scratchBytes=16), -6),
+]
+
+
+@pytest.mark.parametrize("what,over,T,ptrs,code", REJECT, ids=[r[0] for r in REJECT])
+def test_dispatch_rejects(what, over, T, ptrs, code):
+    assert _dispatch(cfg(**over), T, **ptrs) == code
+    assert epdc.epdc_last_error() != ""
+
+
+COMBINE_REJECT = [
+    ("worldSize 65", dict(worldSize=65), 8, {}, -1),
+    ("dtype fp8", dict(dtype=2), 8, {}, -2),
+    ("capacity", {}, 4097, {}, -3),
+    ("out misaligned", {}, 8, dict(out=P16 + 8), -4),
+    ("y misaligned", {}, 8, dict(y=P16 + 2), -4),
+    ("y null", {}, 8, dict(y=None), -5),
+    ("weights null with useWeights", {}, 8, dict(weights=None), -5),
+]
+
+
+@pytest.mark.parametrize("what,over,T,ptrs,code", COMBINE_REJECT, ids=[r[0] for r in COMBINE_REJECT])
+def test_combine_rejects(what, over, T, ptrs, code):
+    assert _combine(cfg(**over), T, **ptrs) == code
+    assert epdc.epdc_last_error() != ""
+
+
+def test_unweighted_accepts_null_weights_without_gpu():
+    """Valid unweighted arguments pass every host check; with no GPU the
+    launch itself reports EPDC_ERR_HIP instead of crashing."""
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("host without a GPU only")
+    c = cfg(useWeights=0)
+    assert _dispatch(c, 8, weights=None, recvWeights=None) == -7
+    assert _combine(c, 8, weights=None) == -7
+    assert "dispatch" in epdc.epdc_last_error() or "combine" in epdc.epdc_last_error()
+
+
+def test_zero_tokens_needs_only_recvcount_without_gpu():
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("host without a GPU only")
+    n = dict(x=None, expertIds=None, weights=None, recvX=None, recvTokIdx=None, recvExpertIds=None,
+             recvWeights=None, sendMap=None, scratch=None, scratchBytes=0)
+    assert _dispatch(cfg(), 0, **n) == -7  # passes the checks, then no device
+    assert _combine(cfg(), 0, y=None, expertIds=None, weights=None, sendMap=None, out=None) == 0

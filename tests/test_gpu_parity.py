@@ -1,0 +1,144 @@
+"""HIP library vs the CPU oracle, through the C ABI, on an MI355X.
+
+Dispatch must match bit for bit on every output buffer (windows pre-filled
+with sentinels, so untouched rows are checked too); combine must match bit
+for bit (both sides accumulate in the same order with one fused multiply-add
+per PE).  Inputs are the seeded synthetic workloads of workloads.py at their
+full sizes, plus edge shapes: empty and ragged inputs, widths that are not a
+multiple of 512, non-power-of-two worldSize / numExpertPerRank, tokens with
+more than 8 destinations, the 64-PE / 64-slot maxima and invalid expert ids.
+"""
+import dataclasses
+
+import numpy as np
+import pytest
+import torch
+
+import combine_count_amd as epdc
+import workloads
+from gpu_harness import (GpuRun, assert_bits_equal, assert_dispatch_equal, dev_to_bits, oracle_combine,
+                         oracle_dispatch)
+
+pytestmark = pytest.mark.gpu
+
+CONFIG_SEEDS = [
+    ("tiny", 1), ("tiny", 2), ("tiny", 3),
+    ("pr_scale", 1), ("pr_scale", 2), ("pr_scale", 3),
+    ("epcfg_defaults", 1), ("epcfg_defaults", 2), ("epcfg_defaults", 3),
+    ("gen_zipf_h2048", 1), ("gen_zipf_h2048", 2),
+    ("gen_zipf_h7168", 1),
+    ("gen_edge_t1", 1), ("gen_edge_t1", 2), ("gen_edge_t1", 3),
+    ("gen_edge_t8", 1), ("gen_edge_t8", 2), ("gen_edge_t8", 3),
+    ("large_unweighted", 1),
+    ("large_weighted", 1),
+]
+
+
+def _check_case(w: workloads.Workload, inp: workloads.Inputs, tag: str):
+    print(f"[parity] {tag}: {w}", flush=True)
+    g = GpuRun(w, inp)
+    g.dispatch()
+    torch.cuda.synchronize()
+    o = oracle_dispatch(w, inp)
+    assert_dispatch_equal(g, o, tag)
+    if w.numTokens == 0:
+        return
+    # combine over independent returned rows y
+    g.combine()
+    torch.cuda.synchronize()
+    exp = oracle_combine(w, inp.y, inp, o.sendMap)
+    assert_bits_equal(dev_to_bits(g.out), exp, f"{tag} combine")
+    # identity expert: the returned rows are the dispatched rows
+    g.combine(y=g.recvX)
+    torch.cuda.synchronize()
+    exp = oracle_combine(w, o.recvX, inp, o.sendMap)
+    assert_bits_equal(dev_to_bits(g.out), exp, f"{tag} identity combine")
+
+
+@pytest.mark.parametrize("name,seed", CONFIG_SEEDS, ids=[f"{n}-s{s}" for n, s in CONFIG_SEEDS])
+def test_config_parity(name, seed):
+    w = workloads.CONFIGS[name]
+    _check_case(w, workloads.cached_inputs(name, seed), f"{name} seed {seed}")
+
+
+EDGE = [
+    # name, worldSize, numExpertPerRank, maxTokPerRank, numTokens, topk, hiddenDim, routing, useWeights
+    ("empty", 4, 4, 64, 0, 2, 128, "uniform", 1),
+    ("ragged_w3_epr5_h136", 3, 5, 128, 100, 4, 136, "uniform", 1),
+    ("ragged_w5_epr3_h1032", 5, 3, 1024, 1000, 7, 1032, "uniform", 1),
+    ("more_than_8_dest", 16, 2, 320, 300, 12, 512, "uniform", 1),
+    ("more_than_8_dest_unweighted", 16, 2, 320, 257, 12, 1024, "zipf", 0),
+    ("max_w64_k64", 64, 1, 80, 70, 64, 64, "uniform", 1),
+    ("single_pe", 1, 8, 96, 65, 3, 8, "uniform", 1),
+    ("topk1", 8, 4, 200, 129, 1, 2048, "uniform", 1),
+    ("m_gt_t", 8, 32, 4096, 777, 8, 7168, "zipf", 1),
+    ("one_token_full_row", 8, 32, 64, 1, 8, 7168, "uniform", 0),
+]
+
+
+@pytest.mark.parametrize("case", EDGE, ids=[e[0] for e in EDGE])
+def test_edge_parity(case):
+    name, W, Epr, M, T, K, H, routing, useW = case
+    w = workloads.Workload(name, W, Epr, M, T, K, H, routing, useW)
+    _check_case(w, workloads.make_inputs(w, 5), name)
+
+
+def test_invalid_expert_ids():
+    """Ids outside [0, E) are dropped slots: null entry, no row, no weight."""
+    w = workloads.Workload("invalid_ids", 8, 4, 256, 250, 6, 1024, "uniform", 1)
+    inp = workloads.make_inputs(w, 9)
+    rng = np.random.Generator(np.random.PCG64(99))
+    ids = inp.expertIds.copy()
+    E = w.numExperts
+    mask = rng.random(ids.shape) < 0.25
+    bad = rng.choice(np.array([-1, -2, E, E + 5, 2**31 - 1, -(2**31)], dtype=np.int64), size=ids.shape)
+    ids[mask] = bad[mask].astype(np.int32)
+    ids[3, :] = -1  # a token with no valid slot combines to +0
+    inp = dataclasses.replace(inp, expertIds=ids)
+    _check_case(w, inp, "invalid_ids")
+
+
+def test_deterministic_and_graph_replay():
+    """Two eager runs are bitwise equal; a captured dispatch+combine graph
+    replayed several times (eager work and syncs in between) equals eager."""
+    w = workloads.CONFIGS["pr_scale"]
+    inp = workloads.cached_inputs("pr_scale", 1)
+    g = GpuRun(w, inp)
+    g.dispatch()
+    g.combine()
+    torch.cuda.synchronize()
+    ref = {k: getattr(g, k).clone() for k in ("recvX", "recvTokIdx", "recvExpertIds", "recvWeights",
+                                              "recvCount", "sendMap", "out")}
+    g.dispatch()
+    g.combine()
+    torch.cuda.synchronize()
+    for k, v in ref.items():
+        assert torch.equal(getattr(g, k).view(torch.int16) if v.dtype == torch.bfloat16 else getattr(g, k),
+                           v.view(torch.int16) if v.dtype == torch.bfloat16 else v), f"rerun differs: {k}"
+    s = torch.cuda.Stream()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(s):
+        g.dispatch(stream=s)  # warm-up on the capture stream
+        g.combine(stream=s)
+    torch.cuda.synchronize()
+    with torch.cuda.graph(graph, stream=s):
+        g.dispatch(stream=s)
+        g.combine(stream=s)
+    for rep in range(4):
+        g.recvCount.fill_(-1)
+        g.sendMap.fill_(-5)
+        g.out.view(torch.int16).fill_(0x1234)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        for k, v in ref.items():
+            a = getattr(g, k)
+            if v.dtype == torch.bfloat16:
+                a, v = a.view(torch.int16), v.view(torch.int16)
+            assert torch.equal(a, v), f"graph replay {rep} differs from eager: {k}"
+
+
+def test_library_is_in_tree():
+    lib = epdc.load_library()
+    assert lib._name.endswith("combine_count_amd/libepdc.so")
+    assert torch.cuda.is_available()
