@@ -39,8 +39,14 @@ def parse_args():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="gen_zipf_h7168")
     ap.add_argument("--seed", type=int, default=1)
+    ap.add_argument("--rotate", type=int, default=3,
+                    help="independent buffer sets (inputs and outputs) cycled step by step, so that a "
+                         "step never finds its data in the 256 MB Infinity Cache (1 = hot)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="wall-clock budget of the CPU-oracle sample (0 disables it)")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="also run a plain torch device copy of MIB MiB 5 times first: the known-size "
+                         "kernel that scales rocprofv3 FETCH_SIZE / WRITE_SIZE readings")
     return ap.parse_args()
 
 
@@ -116,10 +122,27 @@ def main():
     import workloads
     from gpu_harness import GpuRun
 
+    if args.copy_calibration:
+        n = args.copy_calibration * (1 << 20)
+        src = torch.empty(n, dtype=torch.uint8, device="cuda").random_(0, 255)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(5):
+            dst.copy_(src)
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / 5
+        print(f"[bench] copy calibration: {n} bytes read + {n} written, {ms * 1e3:.1f} us per copy, "
+              f"{2 * n / ms / 1e6:.0f} GB/s", file=sys.stderr, flush=True)
+        del src, dst
+
     w = workloads.CONFIGS[args.workload]
     print(f"[bench] generating {w.name} seed {args.seed}", file=sys.stderr, flush=True)
     inp = workloads.make_inputs(w, args.seed)
-    g = GpuRun(w, inp)
+    sets = [GpuRun(w, inp) for _ in range(max(1, args.rotate))]
+    g = sets[0]
     g.dispatch()
     g.combine()
     torch.cuda.synchronize()
@@ -128,9 +151,9 @@ def main():
     stream = torch.cuda.current_stream()
 
     print(f"[bench] warmup {args.warmup}", file=sys.stderr, flush=True)
-    for _ in range(args.warmup):
-        g.dispatch()
-        g.combine()
+    for i in range(args.warmup):
+        sets[i % len(sets)].dispatch()
+        sets[i % len(sets)].combine()
     torch.cuda.synchronize()
 
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
@@ -139,10 +162,11 @@ def main():
     torch.cuda.synchronize()
     t_start.record(stream)
     for i in range(args.steps):
+        s = sets[i % len(sets)]
         ev[i][0].record(stream)
-        g.dispatch()
+        s.dispatch()
         ev[i][1].record(stream)
-        g.combine()
+        s.combine()
         ev[i][2].record(stream)
     t_end.record(stream)
     torch.cuda.synchronize()
@@ -150,6 +174,7 @@ def main():
     ms_step = total_ms / args.steps
     d_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in ev]))
     c_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in ev]))
+    scratch_ok = all(s.scratch_clean() for s in sets)
     print(f"[bench] U={U} dispatch {d_ms * 1e3:.1f} us ({disp_b / d_ms / 1e6:.0f} GB/s), combine "
           f"{c_ms * 1e3:.1f} us ({comb_b / c_ms / 1e6:.0f} GB/s), step {ms_step * 1e3:.1f} us",
           file=sys.stderr, flush=True)
@@ -182,6 +207,7 @@ def main():
                    "useWeights": w.useWeights, "seed": args.seed, "unique_token_pe_pairs": U,
                    "bytes_per_step": disp_b + comb_b,
                    "dispatch_us": round(d_ms * 1e3, 2), "combine_us": round(c_ms * 1e3, 2),
+                   "buffer_sets_rotated": len(sets), "scratch_clean": scratch_ok,
                    "frac_of_hbm_peak": round(value / HBM_PEAK_GBPS, 4)},
         "roofline": roofline,
         "cpu_baseline": cpu,

@@ -52,7 +52,7 @@ __device__ __forceinline__ void load_slab(u32x4 (&v)[CPW], const uint16_t *row, 
     for (int c = 0; c < CPW; ++c) {
         const int gc = slab * CPW + c;
         const int e = gc * kChunkElems + lane * 8;
-        if (FULL || (gc < nChunks && e < H)) v[c] = *reinterpret_cast<const u32x4 *>(row + e);
+        if (FULL || (gc < nChunks && e < H)) v[c] = load16<EPDC_COMBINE_NT_LOAD>(row + e);
     }
 }
 
@@ -151,7 +151,7 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineParams P, int nSlab
             o.y = f32_to_bf16(acc[c][2]) | (f32_to_bf16(acc[c][3]) << 16);
             o.z = f32_to_bf16(acc[c][4]) | (f32_to_bf16(acc[c][5]) << 16);
             o.w = f32_to_bf16(acc[c][6]) | (f32_to_bf16(acc[c][7]) << 16);
-            *reinterpret_cast<u32x4 *>(orow + e) = o;
+            store16<EPDC_COMBINE_NT_STORE>(orow + e, o);
         }
     }
 }
@@ -174,8 +174,12 @@ hipError_t launch(const CombineParams &P, hipStream_t stream) {
 
 hipError_t launch_combine(const CombineParams &P, hipStream_t stream) {
     if (P.T == 0) return hipSuccess;
+#if EPDC_COMBINE_CPW == 0
     if (P.nChunks % 2 == 0 && (int64_t)P.T * (P.nChunks / 2) >= 8192) return launch<2>(P, stream);
     return launch<1>(P, stream);
+#else
+    return launch<EPDC_COMBINE_CPW>(P, stream);
+#endif
 }
 
 }  // namespace epdc

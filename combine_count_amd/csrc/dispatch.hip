@@ -23,6 +23,9 @@
 namespace epdc {
 namespace {
 
+constexpr bool kNtLoad = EPDC_DISPATCH_NT_LOAD;
+constexpr bool kNtStore = EPDC_DISPATCH_NT_STORE;
+
 __device__ __forceinline__ int32_t dest_pe(int32_t e, int32_t E, int32_t Epr, int32_t eprShift) {
     if (e < 0 || e >= E) return -1;
     return eprShift >= 0 ? (e >> eprShift) : (e / Epr);
@@ -42,19 +45,30 @@ __device__ __forceinline__ uint64_t token_pe_mask(const DispatchParams &P, int32
 
 __device__ __forceinline__ uint64_t lanemask_lt(int lane) { return (1ull << lane) - 1ull; }
 
-// ---------------------------------------------------------------- COUNT
-// One wave per 64-token tile: tileCount[tile][p] = tokens of the tile on p.
-__global__ __launch_bounds__(64) void count_kernel(DispatchParams P) {
-    const int lane = threadIdx.x;
-    const int tile = blockIdx.x;
-    const int32_t t = tile * kTile + lane;
-    const uint64_t m = (t < P.T) ? token_pe_mask(P, t) : 0ull;
-    int cnt = 0;
-    for (int p = 0; p < P.W; ++p) {
-        const uint64_t b = __ballot((m >> p) & 1ull);
-        if (lane == p) cnt = __popcll(b);
+// Published count of tile j on PE p, waited for with a bound.  Forward
+// progress: workgroups are dispatched in increasing blockIdx order (per XCD),
+// so every block of an earlier tile was dispatched before any block that
+// waits on it, and a block publishes before it waits on anything.  The bound
+// only matters if that ever fails with every slot held by waiting blocks: the
+// wait then gives up and flags the scratch error word (outputs invalid)
+// instead of hanging the GPU.
+constexpr int kMaxSpins = 1 << 18;
+
+__device__ __forceinline__ uint32_t load_published(uint32_t *slot) {
+    return __hip_atomic_load(slot, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+__device__ __noinline__ uint32_t wait_published(uint32_t *slot, uint32_t *errWord) {
+    uint32_t v = load_published(slot);
+    for (int spins = 0; v == 0; ++spins) {
+        if (spins >= kMaxSpins) {
+            __hip_atomic_store(errWord, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            return 1u;
+        }
+        __builtin_amdgcn_s_sleep(2);
+        v = load_published(slot);
     }
-    if (lane < P.Wp) P.tileCount[(int64_t)tile * P.Wp + lane] = cnt;
+    return v;
 }
 
 __global__ __launch_bounds__(64) void zero_count_kernel(int32_t *recvCount, int32_t W) {
@@ -71,7 +85,7 @@ __device__ __forceinline__ void load_slab(u32x4 (&v)[CPW], const uint16_t *row, 
     for (int c = 0; c < CPW; ++c) {
         const int gc = slab * CPW + c;
         const int e = gc * kChunkElems + lane * 8;
-        if (FULL || (gc < nChunks && e < H)) v[c] = *reinterpret_cast<const u32x4 *>(row + e);
+        if (FULL || (gc < nChunks && e < H)) v[c] = load16<kNtLoad>(row + e);
     }
 }
 
@@ -82,20 +96,27 @@ __device__ __forceinline__ void store_slab(const u32x4 (&v)[CPW], uint16_t *row,
     for (int c = 0; c < CPW; ++c) {
         const int gc = slab * CPW + c;
         const int e = gc * kChunkElems + lane * 8;
-        if (FULL || (gc < nChunks && e < H)) *reinterpret_cast<u32x4 *>(row + e) = v[c];
+        if (FULL || (gc < nChunks && e < H)) store16<kNtStore>(row + e, v[c]);
     }
 }
 
 // Stores one token's slab to every destination PE in its mask (the "ballot
-// walk": only live destinations are visited).  Straight-line for up to 8
-// destinations, so the stores sit in no loop and the only wait is the one
-// for this token's own loads.
+// walk": only live destinations are visited), all uniform scalar control.
+// A row at or past maxTokPerRank can only come from a scratch that was not
+// zero at launch; it is flagged and skipped rather than written.
+__device__ __forceinline__ bool row_ok(const DispatchParams &P, int32_t r) {
+    if (r < P.M) return true;
+    __hip_atomic_store(P.scratch + kScratchError, 2u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    return false;
+}
+
 template <int CPW, bool FULL>
 __device__ __forceinline__ void store_dest(const DispatchParams &P, const u32x4 (&v)[CPW],
                                            const uint64_t *sBal, const int32_t *sPre, uint64_t lt,
                                            int p, int slab, int lane) {
     const int32_t r = uniform(sPre[p] + __popcll(sBal[p] & lt));
-    store_slab<CPW, FULL>(v, P.recvX + ((int64_t)p * P.M + r) * P.H, slab, P.nChunks, P.H, lane);
+    if (row_ok(P, r))
+        store_slab<CPW, FULL>(v, P.recvX + ((int64_t)p * P.M + r) * P.H, slab, P.nChunks, P.H, lane);
 }
 
 template <int CPW, bool FULL>
@@ -119,72 +140,136 @@ __device__ __forceinline__ void store_token(const DispatchParams &P, const u32x4
     }
 }
 
-// ------------------------------------------------------ SCAN + FINALIZE
-// Block = 4 waves on one (64-token tile, token subset, column slab).
-// blockIdx.x = (tile * nSubs + sub) * nSlabs + slab; the block copies tokens
-// [sub*tpb, (sub+1)*tpb) of the tile, tpb = 64 / nSubs, over chunks
+// ------------------------------------------- COUNT + SCAN + FINALIZE
+// One kernel.  Block b = blockIdx.x = (tile * nSubs + sub) * nSlabs + slab
+// has 4 waves and copies the 4*NTW tokens [sub*4*NTW, (sub+1)*4*NTW) of a
+// 64-token tile -- NTW consecutive tokens per wave -- over chunks
 // [slab*CPW, (slab+1)*CPW).
-//   SCAN: the tile's base row on each PE is the sum of the counts of all
-//   earlier tiles (every thread sums a strided share; LDS adds combine them).
-//   The tile's routing is recomputed by wave 0 (ids are tiny and L2-hot).
-//   FINALIZE: each wave copies the slab of every 4th token of the subset to
-//   each of its destinations; the (sub 0, slab 0) block of a tile also writes
-//   the metadata, the sendMap entries (row or null) and, for the last tile,
-//   recvCount.
-template <int CPW, bool FULL>
-__global__ __launch_bounds__(256) void finalize_kernel(DispatchParams P, int nSlabs, int nSubs) {
+//   1. Each wave requests all of its NTW x slabs.
+//   2. COUNT (wave 0): the tile's PE masks and per-PE ballots; the tile's
+//      leader (its first block: sub 0, slab 0) publishes the per-PE counts
+//      as count+1.
+//   3. SCAN: the leader sums the published counts of all earlier tiles into
+//      the tile's base row on each PE and publishes it as base+1; the
+//      tile's other blocks wait for that single line (so polling traffic
+//      does not grow with the number of blocks per tile).
+//   4. FINALIZE: one wait for the wave's loads, then every store of its NTW
+//      tokens to every destination, with no further wait (vmcnt is one
+//      in-order counter for loads and stores on this ISA, so waiting on a
+//      load issued after a store would also wait for the store).  The
+//      (sub 0, slab 0) block of a tile also writes the metadata, the sendMap
+//      entries (row or null) and, for the last tile, recvCount.
+//   5. The last block to finish clears the published counts; the done
+//      counters wrap to zero by themselves, so the scratch is zero again for
+//      the next call (and for every replay of a captured graph).
+template <int CPW, int NTW, bool FULL>
+__global__ __launch_bounds__(256) void dispatch_kernel(DispatchParams P, int nSlabs, int nSubs, int nBlocks) {
     __shared__ uint64_t sMask[kTile];  // destination-PE set of each token of the tile
     __shared__ uint64_t sBal[64];      // per PE: which tokens of the tile go there
     __shared__ int32_t sPre[64];       // per PE: rows taken by earlier tiles
+    __shared__ uint32_t sLast;  // 1 in the block that finishes last
 
+    uint32_t *const hdr = P.scratch;
+    const int nTilesAll = ceil_div(P.T, kTile);
+    uint32_t *const published = P.scratch + kScratchHeaderWords;   // [tile][Wp]: count + 1
+    uint32_t *const prefixes = published + (int64_t)nTilesAll * P.Wp;  // [tile][Wp]: base + 1
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = uniform(tid >> 6);
-    const int slab = blockIdx.x % nSlabs;
-    const int ts = blockIdx.x / nSlabs;
+
+    if (tid < 64) sPre[tid] = 0;
+    __syncthreads();
+    const int b = blockIdx.x;
+    const int slab = b % nSlabs;
+    const int ts = b / nSlabs;
     const int sub = ts % nSubs;
     const int tile = ts / nSubs;
     const int32_t tok0 = tile * kTile;
     const int nTok = min(kTile, P.T - tok0);
-    const int tpb = kTile / nSubs;
-    const int iEnd = min(nTok, (sub + 1) * tpb);
-    const int iBeg = sub * tpb + wave;
-
-    // Start this wave's first row load before the scan.
-    u32x4 bufA[CPW], bufB[CPW];
+    const int iBeg = (sub * 4 + wave) * NTW;  // this wave's tokens: [iBeg, iBeg + NTW) of the tile
     const uint16_t *xTile = P.x + (int64_t)tok0 * P.H;
-    if (iBeg < iEnd) load_slab<CPW, FULL>(bufA, xTile + (int64_t)iBeg * P.H, slab, P.nChunks, P.H, lane);
 
-    if (tid < 64) sPre[tid] = 0;
-    __syncthreads();
-
-    // SCAN: exclusive base of this tile on each PE.  The row stride Wp is a
-    // power of two dividing 256, so thread tid only ever sums PE tid % Wp.
-    {
-        const int n = tile * P.Wp;
-        int acc = 0;
-        int idx = tid;
-        for (; idx + 3 * 256 < n; idx += 4 * 256) {
-            const int a = P.tileCount[idx], b = P.tileCount[idx + 256];
-            const int c = P.tileCount[idx + 512], d = P.tileCount[idx + 768];
-            acc += a + b + c + d;
+    // 1. Request every x slab of this wave (a token past the end of the tile
+    // re-reads the last one; it is not stored).
+    u32x4 buf[NTW][CPW];
+    auto load_x = [&]() {
+#pragma unroll
+        for (int j = 0; j < NTW; ++j) {
+            const int i = min(iBeg + j, nTok - 1);
+            load_slab<CPW, FULL>(buf[j], xTile + (int64_t)i * P.H, slab, P.nChunks, P.H, lane);
         }
-        for (; idx < n; idx += 256) acc += P.tileCount[idx];
-        if (acc) atomicAdd(&sPre[tid & (P.Wp - 1)], acc);
-    }
+    };
+#if EPDC_DISPATCH_XLOAD_PHASE == 0
+    load_x();
+#endif
 
-    // COUNT again for this tile (wave 0): PE masks and per-PE ballots.
+    // 2. COUNT for this tile (wave 0); the tile's leader block (sub 0,
+    // slab 0: the first block of the tile) publishes the per-PE counts.
+    const bool leader = (sub == 0 && slab == 0);
     if (wave == 0) {
         const int32_t t = tok0 + lane;
         const uint64_t m = (lane < nTok) ? token_pe_mask(P, t) : 0ull;
         sMask[lane] = m;
+        int cnt = 0;
         for (int p = 0; p < P.W; ++p) {
-            const uint64_t b = __ballot((m >> p) & 1ull);
-            if (lane == 0) sBal[p] = b;
+            const uint64_t bal = __ballot((m >> p) & 1ull);
+            if (lane == 0) sBal[p] = bal;
+            if (lane == p) cnt = __popcll(bal);
         }
+        if (leader && lane < P.Wp)
+            __hip_atomic_store(published + (int64_t)tile * P.Wp + lane, (uint32_t)cnt + 1u, __ATOMIC_RELAXED,
+                               __HIP_MEMORY_SCOPE_AGENT);
+    }
+
+#if EPDC_DISPATCH_XLOAD_PHASE == 1
+    load_x();
+#endif
+
+    // 3. SCAN: exclusive base of this tile on each PE.  The leader sums the
+    // published counts of all earlier tiles (the row stride Wp is a power of
+    // two dividing 256, so thread tid only ever sums PE tid % Wp) and
+    // publishes the result; the tile's other blocks wait for that one line.
+    if (leader) {
+        const int n = tile * P.Wp;
+        uint32_t acc = 0;
+        int idx = tid;
+        for (; idx + 3 * 256 < n; idx += 4 * 256) {
+            uint32_t v0 = load_published(published + idx), v1 = load_published(published + idx + 256);
+            uint32_t v2 = load_published(published + idx + 512), v3 = load_published(published + idx + 768);
+            if (v0 == 0) v0 = wait_published(published + idx, hdr + kScratchError);
+            if (v1 == 0) v1 = wait_published(published + idx + 256, hdr + kScratchError);
+            if (v2 == 0) v2 = wait_published(published + idx + 512, hdr + kScratchError);
+            if (v3 == 0) v3 = wait_published(published + idx + 768, hdr + kScratchError);
+            acc += v0 + v1 + v2 + v3 - 4u;
+        }
+        for (; idx < n; idx += 256) {
+            uint32_t v = load_published(published + idx);
+            if (v == 0) v = wait_published(published + idx, hdr + kScratchError);
+            acc += v - 1u;
+        }
+        if (acc) atomicAdd(&sPre[tid & (P.Wp - 1)], (int32_t)acc);
+        __syncthreads();
+        if (tid < P.Wp)
+            __hip_atomic_store(prefixes + (int64_t)tile * P.Wp + tid, (uint32_t)sPre[tid] + 1u, __ATOMIC_RELAXED,
+                               __HIP_MEMORY_SCOPE_AGENT);
+    } else if (tid < P.Wp) {
+        uint32_t v = load_published(prefixes + (int64_t)tile * P.Wp + tid);
+        if (v == 0) v = wait_published(prefixes + (int64_t)tile * P.Wp + tid, hdr + kScratchError);
+        sPre[tid] = (int32_t)(v - 1u);
     }
     __syncthreads();
 
+#if EPDC_DISPATCH_XLOAD_PHASE == 2
+    load_x();
+#endif
+
+    // 4. FINALIZE payload.
+    wait_vmcnt<0>();
+#pragma unroll
+    for (int j = 0; j < NTW; ++j)
+        if (iBeg + j < nTok) store_token<CPW, FULL>(P, buf[j], sMask, sBal, sPre, iBeg + j, slab, lane);
+
+    // 4. FINALIZE metadata.
     if (slab == 0 && sub == 0 && wave == 0) {
         if (lane < nTok) {
             const int32_t t = tok0 + lane;
@@ -198,6 +283,7 @@ __global__ __launch_bounds__(256) void finalize_kernel(DispatchParams P, int nSl
                 if (p >= 0 && !((seen >> p) & 1ull)) {
                     seen |= 1ull << p;
                     const int32_t r = sPre[p] + __popcll(sBal[p] & lanemask_lt(lane));
+                    if (!row_ok(P, r)) continue;
                     flat = p * P.M + r;
                     P.recvTokIdx[flat] = t;
                     int32_t *dIds = P.recvExpertIds + (int64_t)flat * P.K;
@@ -214,39 +300,40 @@ __global__ __launch_bounds__(256) void finalize_kernel(DispatchParams P, int nSl
             P.recvCount[lane] = sPre[lane] + __popcll(sBal[lane]);
     }
 
-    // FINALIZE payload, software-pipelined over this wave's tokens: the next
-    // token's slab is requested before the current one is stored, so a wait
-    // for a load never has to wait for earlier stores (one in-order vmcnt).
-    // The prefetch is unconditional -- the last token re-reads its own row --
-    // to keep every wait count exact.
-    // One explicit wait per token -- "all but the CPW loads just issued" --
-    // marks the current buffer complete before the destination branches,
-    // which would otherwise each get a conservative wait that also drains
-    // the previous destination's stores.
-    int i = iBeg;
-    while (i < iEnd) {
-        load_slab<CPW, FULL>(bufB, xTile + (int64_t)(i + 4 < iEnd ? i + 4 : i) * P.H, slab, P.nChunks,
-                             P.H, lane);
-        if (FULL) wait_vmcnt<CPW>(); else wait_vmcnt<0>();
-        store_token<CPW, FULL>(P, bufA, sMask, sBal, sPre, i, slab, lane);
-        i += 4;
-        if (i >= iEnd) break;
-        load_slab<CPW, FULL>(bufA, xTile + (int64_t)(i + 4 < iEnd ? i + 4 : i) * P.H, slab, P.nChunks,
-                             P.H, lane);
-        if (FULL) wait_vmcnt<CPW>(); else wait_vmcnt<0>();
-        store_token<CPW, FULL>(P, bufB, sMask, sBal, sPre, i, slab, lane);
-        i += 4;
+    // 5. Completion.  Every block has read all the counts it needs (their
+    // values were consumed before the barrier above) before it counts itself
+    // done, so the last one may clear them.
+    // Two-level count so that no counter takes more than ~nBlocks/32 atomics:
+    // the last block of each group (b % 32) counts its group done.
+    __syncthreads();
+    if (tid == 0) {
+        const int g = b % kDoneGroups;
+        const int nGroups = min(nBlocks, kDoneGroups);
+        const uint32_t inGroup = (uint32_t)((nBlocks - 1 - g) / kDoneGroups + 1);
+        uint32_t last = 0;
+        if (atomicInc(hdr + kScratchGroupBase + g * kDoneStride, inGroup - 1) == inGroup - 1)
+            last = atomicInc(hdr + kScratchDone, (uint32_t)(nGroups - 1)) == (uint32_t)(nGroups - 1);
+        sLast = last;
+    }
+    __syncthreads();
+    if (sLast) {
+        for (int i = tid; i < 2 * nTilesAll * P.Wp; i += 256)
+            __hip_atomic_store(published + i, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
 }
 
-template <int CPW>
-hipError_t launch_finalize(const DispatchParams &P, int nTiles, int nSubs, hipStream_t stream) {
+template <int CPW, int NTW>
+hipError_t launch_fused(const DispatchParams &P, int nTiles, hipStream_t stream) {
+    static_assert(kTile % (4 * NTW) == 0, "a block's tokens must tile the 64-token tile");
+    const int nSubs = kTile / (4 * NTW);
     const int nSlabs = ceil_div(P.nChunks, CPW);
-    const dim3 grid(nTiles * nSubs * nSlabs);
+    const int nBlocks = nTiles * nSubs * nSlabs;
     if (P.H % kChunkElems == 0 && P.nChunks % CPW == 0)
-        hipLaunchKernelGGL((finalize_kernel<CPW, true>), grid, dim3(256), 0, stream, P, nSlabs, nSubs);
+        hipLaunchKernelGGL((dispatch_kernel<CPW, NTW, true>), dim3(nBlocks), dim3(256), 0, stream, P, nSlabs,
+                           nSubs, nBlocks);
     else
-        hipLaunchKernelGGL((finalize_kernel<CPW, false>), grid, dim3(256), 0, stream, P, nSlabs, nSubs);
+        hipLaunchKernelGGL((dispatch_kernel<CPW, NTW, false>), dim3(nBlocks), dim3(256), 0, stream, P, nSlabs,
+                           nSubs, nBlocks);
     return hipGetLastError();
 }
 
@@ -258,18 +345,16 @@ hipError_t launch_dispatch(const DispatchParams &P, hipStream_t stream) {
         return hipGetLastError();
     }
     const int nTiles = ceil_div(P.T, kTile);
-    hipLaunchKernelGGL(count_kernel, dim3(nTiles), dim3(64), 0, stream, P);
-    hipError_t err = hipGetLastError();
-    if (err != hipSuccess) return err;
-    // Geometry: the largest work per block that still gives about 1536
-    // blocks (6 per CU), preferring 2-chunk slabs, then 1-chunk slabs with
-    // the tile's tokens split over 1..16 blocks.
-    constexpr int kTargetBlocks = 1536;
-    if (P.nChunks >= 2 && (int64_t)nTiles * ceil_div(P.nChunks, 2) >= kTargetBlocks)
-        return launch_finalize<2>(P, nTiles, 1, stream);
-    int nSubs = 1;
-    while (nSubs < 16 && (int64_t)nTiles * nSubs * P.nChunks < kTargetBlocks) nSubs *= 2;
-    return launch_finalize<1>(P, nTiles, nSubs, stream);
+#if EPDC_DISPATCH_CPW != 0 && EPDC_DISPATCH_NTW != 0
+    return launch_fused<EPDC_DISPATCH_CPW, EPDC_DISPATCH_NTW>(P, nTiles, stream);
+#else
+    // Geometry: 2-chunk slabs and 4 tokens per wave for wide rows and many
+    // tiles; smaller work units when there are few tokens or short rows.
+    const bool fullRows = P.H % kChunkElems == 0;
+    if (fullRows && P.nChunks % 2 == 0 && nTiles >= 32) return launch_fused<2, 4>(P, nTiles, stream);
+    if (nTiles >= 8) return launch_fused<1, 4>(P, nTiles, stream);
+    return launch_fused<1, 1>(P, nTiles, stream);
+#endif
 }
 
 }  // namespace epdc

@@ -76,7 +76,7 @@ int check_cfg(const epdc_cfg *c, int32_t numTokens) {
 
 size_t scratch_bytes(const epdc_cfg *c) {
     const int64_t nTiles = ((int64_t)c->maxTokPerRank + epdc::kTile - 1) / epdc::kTile;
-    return (size_t)(nTiles * pow2_ceil(c->worldSize) * sizeof(int32_t));
+    return (size_t)((epdc::kScratchHeaderWords + 2 * nTiles * pow2_ceil(c->worldSize)) * sizeof(uint32_t));
 }
 
 int hip_status(hipError_t e, const char *what) {
@@ -115,9 +115,9 @@ int epdc_dispatch(const epdc_cfg *cfg, int32_t numTokens, const void *x, const i
             if (!aligned(x, 16) || !aligned(recvX, 16))
                 return fail(EPDC_ERR_ALIGN, "x and recvX must be 16-byte aligned");
             if (!aligned(expertIds, 4) || !aligned(recvTokIdx, 4) || !aligned(recvExpertIds, 4) ||
-                !aligned(sendMap, 4) || !aligned(scratch, 4) ||
+                !aligned(sendMap, 4) || !aligned(scratch, 16) ||
                 (cfg->useWeights && (!aligned(weights, 4) || !aligned(recvWeights, 4))))
-                return fail(EPDC_ERR_ALIGN, "int32/fp32 arrays and scratch must be 4-byte aligned");
+                return fail(EPDC_ERR_ALIGN, "int32/fp32 arrays must be 4-byte aligned, scratch 16-byte");
             if (scratchBytes < scratch_bytes(cfg))
                 return fail(EPDC_ERR_SCRATCH, "scratchBytes %zu < %zu required", scratchBytes,
                             scratch_bytes(cfg));
@@ -142,7 +142,7 @@ int epdc_dispatch(const epdc_cfg *cfg, int32_t numTokens, const void *x, const i
         P.recvWeights = cfg->useWeights ? recvWeights : nullptr;
         P.recvCount = recvCount;
         P.sendMap = sendMap;
-        P.tileCount = static_cast<int32_t *>(scratch);
+        P.scratch = static_cast<uint32_t *>(scratch);
         return hip_status(epdc::launch_dispatch(P, static_cast<hipStream_t>(stream)), "dispatch launch");
     } catch (...) {
         return fail(EPDC_ERR_HIP, "unexpected C++ exception in epdc_dispatch");

@@ -31,6 +31,47 @@ __device__ __forceinline__ void wait_vmcnt() {
     __builtin_amdgcn_s_waitcnt((N & 0xF) | (0x7 << 4) | (0xF << 8) | ((N >> 4) << 14));
 }
 
+// Tuning knobs (compile-time; the defaults are the measured choices).
+#ifndef EPDC_DISPATCH_NT_LOAD
+#define EPDC_DISPATCH_NT_LOAD 0  // non-temporal loads of x
+#endif
+#ifndef EPDC_DISPATCH_NT_STORE
+#define EPDC_DISPATCH_NT_STORE 1  // non-temporal stores of recvX rows
+#endif
+#ifndef EPDC_COMBINE_NT_LOAD
+#define EPDC_COMBINE_NT_LOAD 1  // non-temporal loads of returned rows
+#endif
+#ifndef EPDC_COMBINE_NT_STORE
+#define EPDC_COMBINE_NT_STORE 1  // non-temporal stores of out rows
+#endif
+#ifndef EPDC_DISPATCH_CPW
+#define EPDC_DISPATCH_CPW 0  // 0: chosen from the shape
+#endif
+#ifndef EPDC_DISPATCH_NTW
+#define EPDC_DISPATCH_NTW 0  // tokens per wave; 0: chosen from the shape
+#endif
+#ifndef EPDC_DISPATCH_XLOAD_PHASE
+#define EPDC_DISPATCH_XLOAD_PHASE 2  // 0: x loads before COUNT, 1: after publishing, 2: after SCAN
+#endif
+#ifndef EPDC_COMBINE_CPW
+#define EPDC_COMBINE_CPW 0  // 0: chosen from the shape
+#endif
+
+// 16-byte access, optionally with the non-temporal (streaming) hint.
+template <bool NT>
+__device__ __forceinline__ u32x4 load16(const uint16_t *p) {
+    if (NT) return __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(p));
+    return *reinterpret_cast<const u32x4 *>(p);
+}
+
+template <bool NT>
+__device__ __forceinline__ void store16(uint16_t *p, u32x4 v) {
+    if (NT)
+        __builtin_nontemporal_store(v, reinterpret_cast<u32x4 *>(p));
+    else
+        *reinterpret_cast<u32x4 *>(p) = v;
+}
+
 // Routing tile: 64 tokens, one per lane of a wave64.
 constexpr int kTile = 64;
 // One 16-byte access per lane of a wave64 moves 512 bf16 elements (1 KiB).
@@ -50,8 +91,18 @@ struct DispatchParams {
     float *recvWeights;
     int32_t *recvCount;
     int32_t *sendMap;
-    int32_t *tileCount;  // scratch: [nTiles][Wp]
+    uint32_t *scratch;  // scratch: header words, then tile counts [nTilesMax][Wp]
 };
+
+// Dispatch scratch layout (32-bit words).  Zero-filled by the caller before
+// first use; every dispatch leaves it zeroed again (the error word aside).
+constexpr int kScratchDone = 0;    // groups finished (wraps to 0 after the last)
+constexpr int kScratchError = 2;   // set nonzero if a bounded wait ever timed out
+constexpr int kDoneGroups = 32;    // blocks finished, per group b % 32, one 128-byte line each
+constexpr int kDoneStride = 32;    // words between group counters
+constexpr int kScratchGroupBase = 32;
+constexpr int kScratchHeaderWords = kScratchGroupBase + kDoneGroups * kDoneStride;  // 4224 bytes
+// Published tile count: count + 1 (0 = not yet published by this call).
 
 struct CombineParams {
     int32_t W, H, M, Epr, K, T, useWeights;
@@ -64,7 +115,7 @@ struct CombineParams {
     uint16_t *out;
 };
 
-inline int32_t ceil_div(int64_t a, int64_t b) { return (int32_t)((a + b - 1) / b); }
+__host__ __device__ inline int32_t ceil_div(int64_t a, int64_t b) { return (int32_t)((a + b - 1) / b); }
 
 // Launchers: enqueue on `stream`, return the hipGetLastError() after launch.
 hipError_t launch_dispatch(const DispatchParams &p, hipStream_t stream);

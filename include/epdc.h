@@ -78,9 +78,17 @@ typedef struct epdc_cfg {
     int32_t useWeights;
 } epdc_cfg;
 
-/* Bytes of device scratch epdc_dispatch needs for this cfg (a few KB: one
- * int32 per (64-token tile, PE)).  Returns 0 if cfg is invalid.  The scratch
- * holds no state between calls; it needs no initialisation. */
+/* Bytes of device scratch epdc_dispatch needs for this cfg: a 4224-byte header
+ * (completion counters) plus two 32-bit words per (64-token tile, PE) -- a
+ * few KB.  Returns 0 if cfg is invalid.
+ *
+ * The scratch must be zero-filled once before its first use (e.g. one
+ * hipMemset at allocation).  Every dispatch leaves it zeroed again, so it
+ * needs no reset between calls or graph replays.  Word 2 (byte offset 8) is
+ * an error flag that a dispatch sets nonzero -- and never clears -- if one of
+ * its bounded in-kernel waits timed out, which means that call's outputs are
+ * invalid; it stays zero in correct operation.  One scratch buffer serves one
+ * dispatch at a time: calls that may run concurrently need separate buffers. */
 size_t epdc_dispatch_scratch_bytes(const epdc_cfg *cfg);
 
 /*
@@ -104,8 +112,8 @@ size_t epdc_dispatch_scratch_bytes(const epdc_cfg *cfg);
  *                  p*M + r; for every other slot (duplicate PE or invalid
  *                  id) -1, the null entry
  *   Rows r >= recvCount[p] of every window are left untouched.
- * Scratch (device): at least epdc_dispatch_scratch_bytes(cfg) bytes, 4-byte
- *   aligned; two calls in flight at once need two scratch buffers.
+ * Scratch (device): at least epdc_dispatch_scratch_bytes(cfg) bytes, 16-byte
+ *   aligned, zero-filled before its first use (see above).
  * With numTokens == 0 only recvCount is written (zeros); the token-sized
  * pointers may then be NULL.
  */

@@ -56,6 +56,10 @@ class GpuRun:
         self.scratch = torch.zeros(max(nb, 4) // 4 + 1, dtype=torch.int32, device=dev)
         self.out = torch.full((T, H), 0x7FC1, dtype=torch.int16, device=dev).view(torch.bfloat16)
 
+    def scratch_clean(self) -> bool:
+        """After a dispatch the scratch is all zero again (error flag included)."""
+        return bool((self.scratch == 0).all().item())
+
     def dispatch(self, stream=None):
         w = self.w
         return epdc.epdc_dispatch(self.cfg, w.numTokens, self.x, self.ids, self.wts, self.recvX,

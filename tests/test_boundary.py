@@ -51,8 +51,8 @@ def test_header_compiles_as_c():
 
 
 def test_scratch_bytes():
-    assert epdc.epdc_dispatch_scratch_bytes(cfg()) == (4096 // 64) * 8 * 4
-    assert epdc.epdc_dispatch_scratch_bytes(cfg(worldSize=5, maxTokPerRank=65)) == 2 * 8 * 4
+    assert epdc.epdc_dispatch_scratch_bytes(cfg()) == 4224 + 2 * (4096 // 64) * 8 * 4
+    assert epdc.epdc_dispatch_scratch_bytes(cfg(worldSize=5, maxTokPerRank=65)) == 4224 + 2 * 2 * 8 * 4
     assert epdc.epdc_dispatch_scratch_bytes(cfg(hiddenDim=7170)) == 0
 
 
@@ -93,6 +93,7 @@ REJECT = [
     ("x misaligned", {}, 8, dict(x=P16 + 8), -4),
     ("recvX misaligned", {}, 8, dict(recvX=P16 + 4), -4),
     ("ids misaligned", {}, 8, dict(expertIds=P16 + 2), -4),
+    ("scratch misaligned", {}, 8, dict(scratch=P16 + 4), -4),
     ("x null", {}, 8, dict(x=None), -5),
     ("sendMap null", {}, 8, dict(sendMap=None), -5),
     ("recvCount null", {}, 0, dict(recvCount=None), -5),

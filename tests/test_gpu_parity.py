@@ -41,6 +41,7 @@ def _check_case(w: workloads.Workload, inp: workloads.Inputs, tag: str):
     torch.cuda.synchronize()
     o = oracle_dispatch(w, inp)
     assert_dispatch_equal(g, o, tag)
+    assert g.scratch_clean(), f"{tag}: dispatch left its scratch non-zero (or a wait timed out)"
     if w.numTokens == 0:
         return
     # combine over independent returned rows y
@@ -131,6 +132,7 @@ def test_deterministic_and_graph_replay():
         torch.cuda.synchronize()
         graph.replay()
         torch.cuda.synchronize()
+        assert g.scratch_clean(), f"graph replay {rep} left the dispatch scratch non-zero"
         for k, v in ref.items():
             a = getattr(g, k)
             if v.dtype == torch.bfloat16:
