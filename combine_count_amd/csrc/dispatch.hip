@@ -156,9 +156,9 @@ __device__ __forceinline__ void store_token(const DispatchParams &P, const u32x4
 //   4. FINALIZE: one wait for the wave's loads, then every store of its NTW
 //      tokens to every destination, with no further wait (vmcnt is one
 //      in-order counter for loads and stores on this ISA, so waiting on a
-//      load issued after a store would also wait for the store).  The
-//      (sub 0, slab 0) block of a tile also writes the metadata, the sendMap
-//      entries (row or null) and, for the last tile, recvCount.
+//      load issued after a store would also wait for the store).  Then the
+//      waves of slab-0 blocks write their tokens' metadata and sendMap
+//      entries (row or null), and the last tile's leader recvCount.
 //   5. The last block to finish clears the published counts; the done
 //      counters wrap to zero by themselves, so the scratch is zero again for
 //      the next call (and for every replay of a captured graph).
@@ -259,44 +259,65 @@ __global__ __launch_bounds__(256) void dispatch_kernel(DispatchParams P, int nSl
     }
     __syncthreads();
 
+    // Metadata rows of this wave's tokens (slab-0 blocks only; lanes are
+    // slots), requested before x so that no wait below follows a store.
+    const int32_t E = P.W * P.Epr;
+    int32_t mid[NTW];
+    float mwt[NTW];
+#pragma unroll
+    for (int j = 0; j < NTW; ++j) {
+        mid[j] = -1;
+        mwt[j] = 0.0f;
+        const int i = iBeg + j;
+        if (slab == 0 && i < nTok && lane < P.K) {
+            const int64_t o = (int64_t)(tok0 + i) * P.K + lane;
+            mid[j] = P.expertIds[o];
+            if (P.useWeights) mwt[j] = P.weights[o];
+        }
+    }
+
 #if EPDC_DISPATCH_XLOAD_PHASE == 2
     load_x();
 #endif
 
-    // 4. FINALIZE payload.
+    // 4. FINALIZE payload: one wait for every load above, then only stores.
     wait_vmcnt<0>();
 #pragma unroll
     for (int j = 0; j < NTW; ++j)
         if (iBeg + j < nTok) store_token<CPW, FULL>(P, buf[j], sMask, sBal, sPre, iBeg + j, slab, lane);
 
-    // 4. FINALIZE metadata.
-    if (slab == 0 && sub == 0 && wave == 0) {
-        if (lane < nTok) {
-            const int32_t t = tok0 + lane;
-            const int32_t E = P.W * P.Epr;
-            const int32_t *ids = P.expertIds + (int64_t)t * P.K;
-            const float *wts = P.weights + (int64_t)t * P.K;
-            uint64_t seen = 0;
-            for (int k = 0; k < P.K; ++k) {
-                const int32_t p = dest_pe(ids[k], E, P.Epr, P.eprShift);
-                int32_t flat = -1;  // the null entry of a dropped slot
-                if (p >= 0 && !((seen >> p) & 1ull)) {
-                    seen |= 1ull << p;
-                    const int32_t r = sPre[p] + __popcll(sBal[p] & lanemask_lt(lane));
+    // 4. FINALIZE metadata (slab-0 blocks, each wave for its own tokens).
+    // Each destination's id / weight copies and the token's sendMap row are
+    // one coalesced store each.  The kept slot of PE p is the lowest lane
+    // whose expert lives on p; every other slot gets the null entry -1.
+    if (slab == 0) {
+#pragma unroll
+        for (int j = 0; j < NTW; ++j) {
+            const int i = iBeg + j;
+            if (i < nTok) {
+                const int32_t t = tok0 + i;
+                const int32_t pe = dest_pe(mid[j], E, P.Epr, P.eprShift);
+                int32_t flat = -1;
+                uint64_t m = uniform64(sMask[i]);
+                const uint64_t lt = lanemask_lt(i);
+                while (m) {
+                    const int p = __builtin_ctzll(m);
+                    m &= m - 1;
+                    const int32_t r = uniform(sPre[p] + __popcll(sBal[p] & lt));
                     if (!row_ok(P, r)) continue;
-                    flat = p * P.M + r;
-                    P.recvTokIdx[flat] = t;
-                    int32_t *dIds = P.recvExpertIds + (int64_t)flat * P.K;
-                    for (int j = 0; j < P.K; ++j) dIds[j] = ids[j];
-                    if (P.useWeights) {
-                        float *dW = P.recvWeights + (int64_t)flat * P.K;
-                        for (int j = 0; j < P.K; ++j) dW[j] = wts[j];
+                    const int32_t f = p * P.M + r;
+                    const uint64_t onP = __ballot(lane < P.K && pe == p);
+                    if (lane == __builtin_ctzll(onP)) flat = f;
+                    if (lane < P.K) {
+                        P.recvExpertIds[(int64_t)f * P.K + lane] = mid[j];
+                        if (P.useWeights) P.recvWeights[(int64_t)f * P.K + lane] = mwt[j];
                     }
+                    if (lane == 0) P.recvTokIdx[f] = t;
                 }
-                P.sendMap[(int64_t)t * P.K + k] = flat;
+                if (lane < P.K) P.sendMap[(int64_t)t * P.K + lane] = flat;
             }
         }
-        if (tok0 + kTile >= P.T && lane < P.W)
+        if (sub == 0 && wave == 0 && tok0 + kTile >= P.T && lane < P.W)
             P.recvCount[lane] = sPre[lane] + __popcll(sBal[lane]);
     }
 
@@ -337,6 +358,17 @@ hipError_t launch_fused(const DispatchParams &P, int nTiles, hipStream_t stream)
     return hipGetLastError();
 }
 
+// Tokens per wave: the most (fewer redundant COUNT/SCAN prologues) that
+// still gives about kTargetBlocks blocks (enough to fill the chip twice).
+template <int CPW>
+hipError_t launch_cpw(const DispatchParams &P, int nTiles, hipStream_t stream) {
+    constexpr int64_t kTargetBlocks = 2048;
+    const int64_t perTokenWave = (int64_t)nTiles * (kTile / 4) * ceil_div(P.nChunks, CPW);
+    if (perTokenWave >= 4 * kTargetBlocks) return launch_fused<CPW, 4>(P, nTiles, stream);
+    if (perTokenWave >= 2 * kTargetBlocks) return launch_fused<CPW, 2>(P, nTiles, stream);
+    return launch_fused<CPW, 1>(P, nTiles, stream);
+}
+
 }  // namespace
 
 hipError_t launch_dispatch(const DispatchParams &P, hipStream_t stream) {
@@ -348,12 +380,16 @@ hipError_t launch_dispatch(const DispatchParams &P, hipStream_t stream) {
 #if EPDC_DISPATCH_CPW != 0 && EPDC_DISPATCH_NTW != 0
     return launch_fused<EPDC_DISPATCH_CPW, EPDC_DISPATCH_NTW>(P, nTiles, stream);
 #else
-    // Geometry: 2-chunk slabs and 4 tokens per wave for wide rows and many
-    // tiles; smaller work units when there are few tokens or short rows.
-    const bool fullRows = P.H % kChunkElems == 0;
-    if (fullRows && P.nChunks % 2 == 0 && nTiles >= 32) return launch_fused<2, 4>(P, nTiles, stream);
-    if (nTiles >= 8) return launch_fused<1, 4>(P, nTiles, stream);
-    return launch_fused<1, 1>(P, nTiles, stream);
+    // Slab width: the widest of 8/7/4/2 chunks that divides the row (a wave
+    // then moves up to 8 KiB of a token with no bound checks); rows that are
+    // not a whole number of chunks use 1-chunk slabs with per-lane checks.
+    if (P.H % kChunkElems == 0) {
+        if (P.nChunks % 8 == 0) return launch_cpw<8>(P, nTiles, stream);
+        if (P.nChunks % 7 == 0) return launch_cpw<7>(P, nTiles, stream);
+        if (P.nChunks % 4 == 0) return launch_cpw<4>(P, nTiles, stream);
+        if (P.nChunks % 2 == 0) return launch_cpw<2>(P, nTiles, stream);
+    }
+    return launch_cpw<1>(P, nTiles, stream);
 #endif
 }
 

@@ -74,6 +74,11 @@ EDGE = [
     ("topk1", 8, 4, 200, 129, 1, 2048, "uniform", 1),
     ("m_gt_t", 8, 32, 4096, 777, 8, 7168, "zipf", 1),
     ("one_token_full_row", 8, 32, 64, 1, 8, 7168, "uniform", 0),
+    # geometry paths: 8-chunk slabs (1 and 2 per row), 2 tokens per wave
+    ("slab8_h4096", 8, 32, 1000, 1000, 8, 4096, "zipf", 1),
+    ("slab8_h8192_two_slabs", 4, 16, 300, 300, 6, 8192, "uniform", 1),
+    ("two_tokens_per_wave_t9000", 8, 32, 9000, 9000, 8, 7168, "uniform", 1),
+    ("slab2_h1024", 8, 32, 700, 700, 8, 1024, "zipf", 0),
 ]
 
 
