@@ -112,16 +112,19 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineParams P, int nSlab
 #pragma unroll
         for (int j = 0; j < 8; ++j) acc[c][j] = 0.0f;
 
-    // PE loop over the kept slots in ascending order, in groups of up to 8:
-    // every row of a group is requested before the first is reduced, and the
-    // group is straight-line code, so each wait is for exactly one row.
+    // PE loop over the kept slots in ascending order, in groups of up to
+    // kGroup: every row of a group is requested before the first is reduced,
+    // and the group is straight-line code, so each wait is for exactly one
+    // row.  kGroup bounds the registers held by in-flight rows (and so sets
+    // the occupancy).
+    constexpr int kGroup = EPDC_COMBINE_GROUP;
     uint64_t rem = kept;
     while (rem) {
         int32_t fl[8];
         float sc[8];
         int n = 0;
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
+        for (int j = 0; j < kGroup; ++j) {
             const int k = rem ? __builtin_ctzll(rem) : 0;
             fl[j] = __builtin_amdgcn_readlane(flat, k);
             sc[j] = __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(s), k));
@@ -130,13 +133,13 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineParams P, int nSlab
         }
         switch (n) {
             case 1: gather_reduce<1, CPW, FULL>(acc, P, fl, sc, slab, lane); break;
-            case 2: gather_reduce<2, CPW, FULL>(acc, P, fl, sc, slab, lane); break;
-            case 3: gather_reduce<3, CPW, FULL>(acc, P, fl, sc, slab, lane); break;
-            case 4: gather_reduce<4, CPW, FULL>(acc, P, fl, sc, slab, lane); break;
-            case 5: gather_reduce<5, CPW, FULL>(acc, P, fl, sc, slab, lane); break;
-            case 6: gather_reduce<6, CPW, FULL>(acc, P, fl, sc, slab, lane); break;
-            case 7: gather_reduce<7, CPW, FULL>(acc, P, fl, sc, slab, lane); break;
-            default: gather_reduce<8, CPW, FULL>(acc, P, fl, sc, slab, lane); break;
+            case 2: if constexpr (kGroup >= 2) gather_reduce<2, CPW, FULL>(acc, P, fl, sc, slab, lane); break;
+            case 3: if constexpr (kGroup >= 3) gather_reduce<3, CPW, FULL>(acc, P, fl, sc, slab, lane); break;
+            case 4: if constexpr (kGroup >= 4) gather_reduce<4, CPW, FULL>(acc, P, fl, sc, slab, lane); break;
+            case 5: if constexpr (kGroup >= 5) gather_reduce<5, CPW, FULL>(acc, P, fl, sc, slab, lane); break;
+            case 6: if constexpr (kGroup >= 6) gather_reduce<6, CPW, FULL>(acc, P, fl, sc, slab, lane); break;
+            case 7: if constexpr (kGroup >= 7) gather_reduce<7, CPW, FULL>(acc, P, fl, sc, slab, lane); break;
+            default: if constexpr (kGroup >= 8) gather_reduce<8, CPW, FULL>(acc, P, fl, sc, slab, lane); break;
         }
     }
 

@@ -188,6 +188,12 @@ __global__ __launch_bounds__(256) void dispatch_kernel(DispatchParams P, int nSl
     const int nTok = min(kTile, P.T - tok0);
     const int iBeg = (sub * 4 + wave) * NTW;  // this wave's tokens: [iBeg, iBeg + NTW) of the tile
     const uint16_t *xTile = P.x + (int64_t)tok0 * P.H;
+    // A launch of one tile needs no scratch at all (its base rows are 0); a
+    // block whose token group lies past the last token only counts itself
+    // done.
+    const bool multiTile = nTilesAll > 1;
+    const bool active = sub * 4 * NTW < nTok;
+    if (active) {
 
     // 1. Request every x slab of this wave (a token past the end of the tile
     // re-reads the last one; it is not stored).
@@ -216,7 +222,7 @@ __global__ __launch_bounds__(256) void dispatch_kernel(DispatchParams P, int nSl
             if (lane == 0) sBal[p] = bal;
             if (lane == p) cnt = __popcll(bal);
         }
-        if (leader && lane < P.Wp)
+        if (multiTile && leader && lane < P.Wp)
             __hip_atomic_store(published + (int64_t)tile * P.Wp + lane, (uint32_t)cnt + 1u, __ATOMIC_RELAXED,
                                __HIP_MEMORY_SCOPE_AGENT);
     }
@@ -229,7 +235,8 @@ __global__ __launch_bounds__(256) void dispatch_kernel(DispatchParams P, int nSl
     // published counts of all earlier tiles (the row stride Wp is a power of
     // two dividing 256, so thread tid only ever sums PE tid % Wp) and
     // publishes the result; the tile's other blocks wait for that one line.
-    if (leader) {
+    // Tile 0's base rows are 0: nothing to sum, publish or wait for.
+    if (tile > 0 && leader) {
         const int n = tile * P.Wp;
         uint32_t acc = 0;
         int idx = tid;
@@ -252,7 +259,7 @@ __global__ __launch_bounds__(256) void dispatch_kernel(DispatchParams P, int nSl
         if (tid < P.Wp)
             __hip_atomic_store(prefixes + (int64_t)tile * P.Wp + tid, (uint32_t)sPre[tid] + 1u, __ATOMIC_RELAXED,
                                __HIP_MEMORY_SCOPE_AGENT);
-    } else if (tid < P.Wp) {
+    } else if (tile > 0 && tid < P.Wp) {
         uint32_t v = load_published(prefixes + (int64_t)tile * P.Wp + tid);
         if (v == 0) v = wait_published(prefixes + (int64_t)tile * P.Wp + tid, hdr + kScratchError);
         sPre[tid] = (int32_t)(v - 1u);
@@ -321,11 +328,14 @@ __global__ __launch_bounds__(256) void dispatch_kernel(DispatchParams P, int nSl
             P.recvCount[lane] = sPre[lane] + __popcll(sBal[lane]);
     }
 
+    }  // active
+
     // 5. Completion.  Every block has read all the counts it needs (their
     // values were consumed before the barrier above) before it counts itself
     // done, so the last one may clear them.
     // Two-level count so that no counter takes more than ~nBlocks/32 atomics:
     // the last block of each group (b % 32) counts its group done.
+    if (!multiTile) return;
     __syncthreads();
     if (tid == 0) {
         const int g = b % kDoneGroups;
@@ -358,15 +368,15 @@ hipError_t launch_fused(const DispatchParams &P, int nTiles, hipStream_t stream)
     return hipGetLastError();
 }
 
-// Tokens per wave: the most (fewer redundant COUNT/SCAN prologues) that
-// still gives about kTargetBlocks blocks (enough to fill the chip twice).
+// Tokens per wave: one (most blocks, measured fastest at 4096 and 16384
+// tokens) unless that would exceed kMaxBlocks blocks.
 template <int CPW>
 hipError_t launch_cpw(const DispatchParams &P, int nTiles, hipStream_t stream) {
-    constexpr int64_t kTargetBlocks = 2048;
+    constexpr int64_t kMaxBlocks = 16384;
     const int64_t perTokenWave = (int64_t)nTiles * (kTile / 4) * ceil_div(P.nChunks, CPW);
-    if (perTokenWave >= 4 * kTargetBlocks) return launch_fused<CPW, 4>(P, nTiles, stream);
-    if (perTokenWave >= 2 * kTargetBlocks) return launch_fused<CPW, 2>(P, nTiles, stream);
-    return launch_fused<CPW, 1>(P, nTiles, stream);
+    if (perTokenWave <= kMaxBlocks) return launch_fused<CPW, 1>(P, nTiles, stream);
+    if (perTokenWave <= 2 * kMaxBlocks) return launch_fused<CPW, 2>(P, nTiles, stream);
+    return launch_fused<CPW, 4>(P, nTiles, stream);
 }
 
 }  // namespace

@@ -77,7 +77,8 @@ EDGE = [
     # geometry paths: 8-chunk slabs (1 and 2 per row), 2 tokens per wave
     ("slab8_h4096", 8, 32, 1000, 1000, 8, 4096, "zipf", 1),
     ("slab8_h8192_two_slabs", 4, 16, 300, 300, 6, 8192, "uniform", 1),
-    ("two_tokens_per_wave_t9000", 8, 32, 9000, 9000, 8, 7168, "uniform", 1),
+    ("t9000_ragged", 8, 32, 9000, 9000, 8, 7168, "uniform", 1),
+    ("two_tokens_per_wave_t40000", 8, 32, 40000, 40000, 8, 512, "uniform", 0),
     ("slab2_h1024", 8, 32, 700, 700, 8, 1024, "zipf", 0),
 ]
 
