@@ -43,9 +43,9 @@ def load(path: str | None = None) -> ctypes.CDLL:
     lib = ctypes.CDLL(path)
     i32, p = ctypes.c_int32, ctypes.c_void_p
     lib.oracle_dispatch.restype = i32
-    lib.oracle_dispatch.argtypes = [i32] * 7 + [p] * 9
+    lib.oracle_dispatch.argtypes = [i32] * 8 + [p] * 9
     lib.oracle_combine.restype = i32
-    lib.oracle_combine.argtypes = [i32] * 7 + [p] * 5 + [i32, p, p]
+    lib.oracle_combine.argtypes = [i32] * 8 + [p] * 5 + [i32, p, p]
     _lib_cache[path] = lib
     return lib
 
@@ -70,24 +70,28 @@ class DispatchOut:
 def dispatch(W, H, M, Epr, K, useWeights, x, expertIds, weights, *, fill=None, lib=None):
     """Run the oracle dispatch on numpy inputs.
 
-    ``x``: uint16 [T][H] bf16 bits; ``expertIds``: int32 [T][K]; ``weights``:
-    float32 [T][K] or None.  Windows are pre-filled with ``fill`` (a dict of
-    sentinel values) so that untouched rows stay recognisable.
+    ``x``: [T][H] rows of any 1-, 2- or 4-byte element type (bf16 as uint16
+    bits, fp32, fp8 / fp4x2 as uint8); ``expertIds``: int32 [T][K];
+    ``weights``: float32 [T][K] or None.  recvX has x's dtype.  Windows are
+    pre-filled with ``fill`` (a dict of sentinel values; recvX's is a byte,
+    repeated) so that untouched rows stay recognisable.
     """
     lib = lib or load()
     T = x.shape[0]
     fill = fill or {}
-    recvX = np.full((W, M, H), fill.get("recvX", 0), dtype=np.uint16)
+    eb = x.dtype.itemsize
+    recvX = np.empty((W, M, H), dtype=x.dtype)
+    recvX.view(np.uint8)[...] = fill.get("recvX_byte", 0xAD)
     recvTokIdx = np.full((W, M), fill.get("recvTokIdx", 0), dtype=np.int32)
     recvExpertIds = np.full((W, M, K), fill.get("recvExpertIds", 0), dtype=np.int32)
     recvWeights = np.full((W, M, K), fill.get("recvWeights", 0), dtype=np.float32)
     recvCount = np.full((W,), -7, dtype=np.int32)
     sendMap = np.full((T, K), -99, dtype=np.int32)
-    x = np.ascontiguousarray(x, dtype=np.uint16)
+    x = np.ascontiguousarray(x)
     expertIds = np.ascontiguousarray(expertIds, dtype=np.int32)
     if weights is not None:
         weights = np.ascontiguousarray(weights, dtype=np.float32)
-    rc = lib.oracle_dispatch(W, H, M, Epr, K, int(useWeights), T,
+    rc = lib.oracle_dispatch(W, H, M, Epr, K, int(useWeights), T, eb,
                              _ptr(x), _ptr(expertIds), _ptr(weights),
                              _ptr(recvX), _ptr(recvTokIdx), _ptr(recvExpertIds),
                              _ptr(recvWeights), _ptr(recvCount), _ptr(sendMap))
@@ -97,14 +101,16 @@ def dispatch(W, H, M, Epr, K, useWeights, x, expertIds, weights, *, fill=None, l
 
 
 def combine(W, H, M, Epr, K, useWeights, y, expertIds, weights, sendMap, tokens=None, lib=None):
-    """Run the oracle combine.  ``y``: uint16 [W][M][H]; returns uint16 rows.
+    """Run the oracle combine.  ``y``: [W][M][H] bf16 bits (uint16) or
+    float32; returns rows of the same dtype.
 
     With ``tokens`` (an int sequence) only those tokens are combined, in that
     order; otherwise every token of ``sendMap``.
     """
     lib = lib or load()
     T = sendMap.shape[0]
-    y = np.ascontiguousarray(y, dtype=np.uint16)
+    fp32 = y.dtype == np.float32
+    y = np.ascontiguousarray(y, dtype=np.float32 if fp32 else np.uint16)
     assert y.shape == (W, M, H)
     expertIds = np.ascontiguousarray(expertIds, dtype=np.int32)
     sendMap = np.ascontiguousarray(sendMap, dtype=np.int32)
@@ -115,9 +121,9 @@ def combine(W, H, M, Epr, K, useWeights, y, expertIds, weights, sendMap, tokens=
     if tokens is not None:
         tok = np.ascontiguousarray(np.asarray(tokens, dtype=np.int32))
         n = tok.shape[0]
-    out = np.empty((n, H), dtype=np.uint16)
+    out = np.empty((n, H), dtype=np.float32 if fp32 else np.uint16)
     acc = np.empty((H,), dtype=np.float32)
-    rc = lib.oracle_combine(W, H, M, Epr, K, int(useWeights), T,
+    rc = lib.oracle_combine(W, H, M, Epr, K, int(useWeights), T, int(fp32),
                             _ptr(y), _ptr(expertIds), _ptr(weights), _ptr(sendMap),
                             _ptr(tok), n, _ptr(acc), _ptr(out))
     if rc != 0:
@@ -143,11 +149,11 @@ def timed_step(W, H, M, Epr, K, useWeights, x, expertIds, weights, y, lib=None):
     o = outs
 
     def step():
-        rc = lib.oracle_dispatch(W, H, M, Epr, K, int(useWeights), T, _ptr(x), _ptr(expertIds),
+        rc = lib.oracle_dispatch(W, H, M, Epr, K, int(useWeights), T, 2, _ptr(x), _ptr(expertIds),
                                  _ptr(weights), _ptr(o["recvX"]), _ptr(o["recvTokIdx"]),
                                  _ptr(o["recvExpertIds"]), _ptr(o["recvWeights"]), _ptr(o["recvCount"]),
                                  _ptr(o["sendMap"]))
-        rc |= lib.oracle_combine(W, H, M, Epr, K, int(useWeights), T, _ptr(y), _ptr(expertIds),
+        rc |= lib.oracle_combine(W, H, M, Epr, K, int(useWeights), T, 0, _ptr(y), _ptr(expertIds),
                                  _ptr(weights), _ptr(o["sendMap"]), None, T, _ptr(o["acc"]), _ptr(o["out"]))
         if rc:
             raise RuntimeError("oracle step failed")

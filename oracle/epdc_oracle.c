@@ -13,8 +13,11 @@
  *
  * Notation (names as in the pages' EpCfg, MORI JIT v2 design doc, §3.2):
  *   W  = worldSize           Epr = numExpertPerRank    E = W*Epr
- *   K  = numExpertPerToken   H   = hiddenDim (bf16 elements per row)
+ *   K  = numExpertPerToken   H   = hiddenDim (elements per row)
  *   M  = maxTokPerRank       T   = numTokens (0 <= T <= M)
+ * Row element types (the pages' EpDType, MORI JIT v2 design doc, §3.7):
+ * dispatch moves rows of H elements of 2 (bf16), 4 (fp32) or 1 byte (fp8,
+ * and fp4x2 where H counts bytes); combine reduces bf16 or fp32 rows.
  * bf16 values travel as their 16-bit patterns (uint16_t).
  *
  * Parity pins (see tests/test_oracle_pins.py): brute force on tiny inputs,
@@ -77,15 +80,20 @@ static int32_t dest_pe(int32_t e, int32_t W, int32_t Epr) {
  *   - recvCount is stored, not accumulated (mori PR #599 follow-up commits:
  *     the dispatch stores the received count so callers need no reset).
  *
- * Rows r >= recvCount[p] of every window are left untouched.
- * Returns 0, or -1 on a negative size.
+ * Rows r >= recvCount[p] of every window are left untouched.  Rows are
+ * elemBytes * H bytes (the element type does not matter to a copy).
+ * Returns 0, or -1 on a bad size.
  */
 int oracle_dispatch(int32_t W, int32_t H, int32_t M, int32_t Epr, int32_t K,
-                    int32_t useWeights, int32_t T,
-                    const uint16_t *x, const int32_t *expertIds, const float *weights,
-                    uint16_t *recvX, int32_t *recvTokIdx, int32_t *recvExpertIds,
+                    int32_t useWeights, int32_t T, int32_t elemBytes,
+                    const void *x, const int32_t *expertIds, const float *weights,
+                    void *recvX, int32_t *recvTokIdx, int32_t *recvExpertIds,
                     float *recvWeights, int32_t *recvCount, int32_t *sendMap) {
     if (W <= 0 || H <= 0 || M <= 0 || Epr <= 0 || K <= 0 || T < 0 || T > M) return -1;
+    if (elemBytes != 1 && elemBytes != 2 && elemBytes != 4) return -1;
+    const int64_t rowBytes = (int64_t)H * elemBytes;
+    const unsigned char *xb = (const unsigned char *)x;
+    unsigned char *rb = (unsigned char *)recvX;
     for (int32_t p = 0; p < W; ++p) recvCount[p] = 0;
 
     for (int32_t t = 0; t < T; ++t) {
@@ -102,7 +110,7 @@ int oracle_dispatch(int32_t W, int32_t H, int32_t M, int32_t Epr, int32_t K,
             }
             int32_t r = recvCount[p]++;
             int64_t row = (int64_t)p * M + r;
-            memcpy(recvX + row * H, x + (int64_t)t * H, (size_t)H * sizeof(uint16_t));
+            memcpy(rb + row * rowBytes, xb + (int64_t)t * rowBytes, (size_t)rowBytes);
             recvTokIdx[row] = t;
             memcpy(recvExpertIds + row * K, expertIds + (int64_t)t * K, (size_t)K * sizeof(int32_t));
             if (useWeights)
@@ -126,13 +134,15 @@ int oracle_dispatch(int32_t W, int32_t H, int32_t M, int32_t Epr, int32_t K,
  *     the weights of every slot of t whose expert lives on p (valid ids
  *     only); with useWeights == 0 it is 1;
  *   - accumulation in fp32 from +0 with one fused multiply-add per PE;
- *   - output rounded to bf16, nearest-even; a token with no kept slot gives
- *     a +0 row.
+ *   - bf16 rows: output rounded to bf16, nearest-even; fp32 rows: the fp32
+ *     accumulator is the output (MORI JIT v2 §5: the combine reduces bf16 or
+ *     fp32 rows; byte types cannot be summed, §3.7);
+ *   - a token with no kept slot gives a +0 row.
  */
 static void combine_token(int32_t W, int32_t H, int32_t M, int32_t Epr, int32_t K,
-                          int32_t useWeights, int32_t t,
-                          const uint16_t *y, const int32_t *expertIds, const float *weights,
-                          const int32_t *sendMap, float *acc, uint16_t *outRow) {
+                          int32_t useWeights, int32_t fp32, int32_t t,
+                          const void *y, const int32_t *expertIds, const float *weights,
+                          const int32_t *sendMap, float *acc, void *outRow) {
     for (int32_t h = 0; h < H; ++h) acc[h] = 0.0f;
     for (int32_t k0 = 0; k0 < K; ++k0) {
         int32_t flat = sendMap[(int64_t)t * K + k0];
@@ -146,31 +156,44 @@ static void combine_token(int32_t W, int32_t H, int32_t M, int32_t Epr, int32_t 
                 if (dest_pe(expertIds[(int64_t)t * K + k], W, Epr) == p)
                     s = s + weights[(int64_t)t * K + k];
         }
-        const uint16_t *src = y + ((int64_t)p * M + r) * H;
-        for (int32_t h = 0; h < H; ++h) acc[h] = fmaf(s, bf16_to_f32(src[h]), acc[h]);
+        const int64_t row = (int64_t)p * M + r;
+        if (fp32) {
+            const float *src = (const float *)y + row * H;
+            for (int32_t h = 0; h < H; ++h) acc[h] = fmaf(s, src[h], acc[h]);
+        } else {
+            const uint16_t *src = (const uint16_t *)y + row * H;
+            for (int32_t h = 0; h < H; ++h) acc[h] = fmaf(s, bf16_to_f32(src[h]), acc[h]);
+        }
     }
-    for (int32_t h = 0; h < H; ++h) outRow[h] = f32_to_bf16_rne(acc[h]);
+    if (fp32) {
+        memcpy(outRow, acc, (size_t)H * sizeof(float));
+    } else {
+        uint16_t *o = (uint16_t *)outRow;
+        for (int32_t h = 0; h < H; ++h) o[h] = f32_to_bf16_rne(acc[h]);
+    }
 }
 
 /*
- * COMBINE over tokens.  With tokens == NULL every token t in [0, T) is
- * combined into out[t][:].  Otherwise out[i][:] receives token tokens[i]
+ * COMBINE over tokens, of bf16 rows (fp32 == 0) or fp32 rows (fp32 == 1).
+ * With tokens == NULL every token t in [0, T) is combined into out[t][:].  Otherwise out[i][:] receives token tokens[i]
  * for i in [0, nList): the per-token form used to check sampled outputs of
  * large runs.  acc is caller scratch of H floats.
  * Returns 0, or -1 on a bad size or token index.
  */
 int oracle_combine(int32_t W, int32_t H, int32_t M, int32_t Epr, int32_t K,
-                   int32_t useWeights, int32_t T,
-                   const uint16_t *y, const int32_t *expertIds, const float *weights,
+                   int32_t useWeights, int32_t T, int32_t fp32,
+                   const void *y, const int32_t *expertIds, const float *weights,
                    const int32_t *sendMap, const int32_t *tokens, int32_t nList,
-                   float *acc, uint16_t *out) {
+                   float *acc, void *out) {
     if (W <= 0 || H <= 0 || M <= 0 || Epr <= 0 || K <= 0 || T < 0 || T > M) return -1;
+    if (fp32 != 0 && fp32 != 1) return -1;
+    const int64_t outRowBytes = (int64_t)H * (fp32 ? 4 : 2);
     int32_t n = tokens ? nList : T;
     for (int32_t i = 0; i < n; ++i) {
         int32_t t = tokens ? tokens[i] : i;
         if (t < 0 || t >= T) return -1;
-        combine_token(W, H, M, Epr, K, useWeights, t, y, expertIds, weights, sendMap,
-                      acc, out + (int64_t)i * H);
+        combine_token(W, H, M, Epr, K, useWeights, fp32, t, y, expertIds, weights, sendMap,
+                      acc, (unsigned char *)out + (int64_t)i * outRowBytes);
     }
     return 0;
 }

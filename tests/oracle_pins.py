@@ -37,7 +37,7 @@ import workloads
 
 GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
 
-SENTINEL = {"recvX": 0xDEAD, "recvTokIdx": -12345, "recvExpertIds": -777, "recvWeights": -3.5}
+SENTINEL = {"recvX_byte": 0xAD, "recvTokIdx": -12345, "recvExpertIds": -777, "recvWeights": -3.5}
 
 
 # --------------------------------------------------------------------------
@@ -91,7 +91,7 @@ def compare_dispatch_with_brute(W, Epr, K, M, H, useWeights, x, ids, wts, lib, t
         if useWeights and not np.array_equal(out.recvWeights[p, r].view(np.uint32), wts[t].view(np.uint32)):
             fails.append(f"{tag}: recvWeights[{p}][{r}] != weights[{t}]")
     for p in range(W):
-        if not (out.recvX[p, count[p]:] == SENTINEL["recvX"]).all():
+        if not (out.recvX[p, count[p]:].view(np.uint8) == SENTINEL["recvX_byte"]).all():
             fails.append(f"{tag}: rows past recvCount[{p}] of recvX were written")
         if not (out.recvTokIdx[p, count[p]:] == SENTINEL["recvTokIdx"]).all():
             fails.append(f"{tag}: rows past recvCount[{p}] of recvTokIdx were written")
@@ -128,8 +128,20 @@ def check_brute_force_exhaustive(lib, max_cases=6000):
     return fails
 
 
+def _random_rows(rng, T, H, i):
+    """Row payloads of the four wire types in turn: bf16 bits, fp32, and the
+    one-byte fp8 / fp4x2 encodings (dispatch copies them without looking)."""
+    kind = i % 4
+    if kind == 0:
+        return rng.integers(0, 1 << 16, size=(T, H), dtype=np.uint16)
+    if kind == 1:
+        return rng.standard_normal((T, H)).astype(np.float32)
+    return rng.integers(0, 256, size=(T, H), dtype=np.uint8)
+
+
 def check_brute_force_random(lib):
-    """Random small shapes, including W and K that are not powers of two."""
+    """Random small shapes, including W and K that are not powers of two, over
+    all four row element sizes."""
     fails = []
     rng = np.random.Generator(np.random.PCG64(12))
     for i in range(60):
@@ -141,9 +153,10 @@ def check_brute_force_random(lib):
         M = T + int(rng.integers(0, 3)) + (1 if T == 0 else 0)
         H = 8 * int(rng.integers(1, 4))
         ids = rng.integers(-1, E + 1, size=(T, K)).astype(np.int32)
-        x = rng.integers(0, 1 << 16, size=(T, H), dtype=np.uint16)
+        x = _random_rows(rng, T, H, i)
         wts = rng.standard_normal((T, K)).astype(np.float32)
-        fails += compare_dispatch_with_brute(W, Epr, K, M, H, i % 2, x, ids, wts, lib, f"rand{i}")
+        fails += compare_dispatch_with_brute(W, Epr, K, M, H, (i // 4) % 2, x, ids, wts, lib,
+                                             f"rand{i} {x.dtype}")
         if fails:
             break
     return fails
@@ -524,6 +537,84 @@ def check_reading_fma_and_order(lib):
     return []
 
 
+def check_combine_fp32(lib, names=("tiny", "pr_scale", "epcfg_defaults"), seed=8, h_cap=512):
+    """fp32 rows: identity + one-hot weights returns x bit for bit; the fp64
+    recomputation lies within the fp32 summation bound e (no output rounding
+    on this path); zero weights give +0."""
+    fails = []
+    for name in names:
+        w = workloads.CONFIGS[name]
+        if w.hiddenDim > h_cap:
+            w = w.with_(hiddenDim=h_cap)
+        W, Epr, K, M, H, T = (w.worldSize, w.numExpertPerRank, w.numExpertPerToken,
+                              w.maxTokPerRank, w.hiddenDim, w.numTokens)
+        rng = np.random.Generator(np.random.PCG64(seed))
+        inp = workloads.make_inputs(w, seed, with_y=False)
+        x = rng.standard_normal((T, H)).astype(np.float32)
+        y = rng.standard_normal((W, M, H)).astype(np.float32)
+        wts = (rng.standard_normal((T, K)) * 0.7).astype(np.float32)
+        o = oracle.dispatch(W, H, M, Epr, K, 1, x, inp.expertIds, wts, lib=lib)
+        onehot = np.zeros((T, K), dtype=np.float32)
+        onehot[np.arange(T), rng.integers(0, K, size=T)] = 1.0
+        got = oracle.combine(W, H, M, Epr, K, 1, o.recvX, inp.expertIds, onehot, o.sendMap, lib=lib)
+        if got.dtype != np.float32 or not np.array_equal(got.view(np.uint32), x.view(np.uint32)):
+            fails.append(f"{name}: fp32 one-hot identity combine is not the input")
+        got = oracle.combine(W, H, M, Epr, K, 1, y, inp.expertIds, np.zeros((T, K), np.float32), o.sendMap,
+                             lib=lib)
+        if (got.view(np.uint32) != 0).any():
+            fails.append(f"{name}: fp32 zero weights do not give +0")
+        count, rowOf, _ = brute_dispatch(W, Epr, K, M, inp.expertIds)
+        got = oracle.combine(W, H, M, Epr, K, 1, y, inp.expertIds, wts, o.sendMap, lib=lib)
+        ref = np.zeros((T, H))
+        mag = np.zeros((T, H))
+        E = W * Epr
+        for t in range(T):
+            for k in range(K):
+                e = int(inp.expertIds[t, k])
+                if 0 <= e < E:
+                    row = y[e // Epr, rowOf[(t, e // Epr)]].astype(np.float64)
+                    ref[t] += float(wts[t, k]) * row
+                    mag[t] += abs(float(wts[t, k])) * np.abs(row)
+        bound = (K + 1) * 2.0 ** -24 * mag
+        err = np.abs(got.astype(np.float64) - ref)
+        if (err > bound).any():
+            t, h = np.argwhere(err > bound)[0]
+            fails.append(f"{name}: fp32 out[{t}][{h}] off fp64 by {err[t, h]:.3g} > {bound[t, h]:.3g}")
+    return fails
+
+
+def check_reading_fma_fp32(lib, n=64, seed=31):
+    """fp32 rows expose the fp32 accumulator: two-PE tokens where one fused
+    multiply-add per PE (exact fp64 value, one rounding) differs from a
+    separate multiply and add, so the output must equal the fma chain."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    s = rng.uniform(0.05, 0.9, size=(4 * n, 2)).astype(np.float32)
+    yv = rng.standard_normal((4 * n, 2)).astype(np.float32)
+    a1 = (s[:, 0].astype(np.float64) * yv[:, 0]).astype(np.float32)
+    fma = (s[:, 1].astype(np.float64) * yv[:, 1] + a1.astype(np.float64)).astype(np.float32)
+    sep = (s[:, 1] * yv[:, 1]).astype(np.float32) + a1
+    keep = np.nonzero(fma != sep)[0][:n]
+    if len(keep) < 8:
+        return ["too few discriminating fp32 cases"]
+    from fractions import Fraction
+    for i in keep:  # the fp64 sums used above are exact
+        ex = Fraction(float(s[i, 1])) * Fraction(float(yv[i, 1])) + Fraction(float(a1[i]))
+        if Fraction(float(s[i, 1].astype(np.float64) * yv[i, 1] + a1[i].astype(np.float64))) != ex:
+            return ["fp32 reading case not exact in fp64"]
+    s, yv, exp = s[keep], yv[keep], fma[keep]
+    T, W, Epr, K, M, H = len(keep), 2, 1, 2, len(keep), 4
+    ids = np.tile(np.array([0, 1], np.int32), (T, 1))
+    o = oracle.dispatch(W, H, M, Epr, K, 1, np.zeros((T, H), np.float32), ids, s, lib=lib)
+    y = np.zeros((W, M, H), np.float32)
+    for t in range(T):
+        for p in range(2):
+            y[p, o.sendMap[t, p] % M, :] = yv[t, p]
+    got = oracle.combine(W, H, M, Epr, K, 1, y, ids, s, o.sendMap, lib=lib)
+    if not np.array_equal(got[:, 0].view(np.uint32), exp.view(np.uint32)):
+        return ["fp32 fma reading: output is not the single-rounding fma chain"]
+    return []
+
+
 ALL_CHECKS = [
     check_worked_example,
     check_brute_force_exhaustive,
@@ -535,4 +626,6 @@ ALL_CHECKS = [
     check_combine_identity_cases,
     check_combine_fp64_bound,
     check_reading_fma_and_order,
+    check_combine_fp32,
+    check_reading_fma_fp32,
 ]

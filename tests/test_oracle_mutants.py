@@ -52,8 +52,17 @@ MUTANTS = [
      "s = s + weights[(int64_t)t * K + k];",
      "s = s + weights[(int64_t)t * K + (K - 1 - k)];"),
     ("combine: returned row read with swapped stride",
-     "const uint16_t *src = y + ((int64_t)p * M + r) * H;",
-     "const uint16_t *src = y + ((int64_t)r * W + p) * H;"),
+     "const int64_t row = (int64_t)p * M + r;",
+     "const int64_t row = (int64_t)r * W + p;"),
+    ("dispatch: row copied as bf16 whatever the element size",
+     "const int64_t rowBytes = (int64_t)H * elemBytes;",
+     "const int64_t rowBytes = (int64_t)H * 2 + 0 * elemBytes;"),
+    ("combine fp32: separate multiply and add",
+     "for (int32_t h = 0; h < H; ++h) acc[h] = fmaf(s, src[h], acc[h]);",
+     "for (int32_t h = 0; h < H; ++h) acc[h] = s * src[h] + acc[h];"),
+    ("combine fp32: output rounded to bf16 precision",
+     "memcpy(outRow, acc, (size_t)H * sizeof(float));",
+     "for (int32_t h = 0; h < H; ++h) ((float *)outRow)[h] = bf16_to_f32(f32_to_bf16_rne(acc[h]));"),
     ("combine: separate multiply and add",
      "acc[h] = fmaf(s, bf16_to_f32(src[h]), acc[h]);",
      "acc[h] = s * bf16_to_f32(src[h]) + acc[h];"),
@@ -74,6 +83,8 @@ MUTANTS = [
 # cheapest checks first
 ORDER = [
     pins.check_worked_example,
+    pins.check_reading_fma_fp32,
+    pins.check_combine_fp32,
     pins.check_brute_force_random,
     pins.check_reading_fma_and_order,
     pins.check_combine_identity_cases,
