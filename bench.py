@@ -40,6 +40,9 @@ def parse_args():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="gen_zipf_h7168")
     ap.add_argument("--seed", type=int, default=1)
+    ap.add_argument("--wire", default="bf16", choices=["bf16", "fp32", "fp8", "fp4x2"],
+                    help="dispatch row type (fp8/fp4x2: narrow wire, hiddenDim in bytes for fp4x2)")
+    ap.add_argument("--combine-dtype", default="bf16", choices=["bf16", "fp32"])
     ap.add_argument("--rotate", type=int, default=3,
                     help="independent buffer sets (inputs and outputs) cycled step by step, so that a "
                          "step never finds its data in the 256 MB Infinity Cache (1 = hot)")
@@ -54,12 +57,15 @@ def parse_args():
 def algorithmic_bytes(w, U):
     """Bytes the method must move (each input read once, each output written
     once); U = unique (token, PE) pairs of the seeded input."""
-    T, K, H, W, s = w.numTokens, w.numExpertPerToken, w.hiddenDim, w.worldSize, 2
+    import workloads
+    T, K, W = w.numTokens, w.numExpertPerToken, w.worldSize
+    xr = w.dispatchHidden * workloads.WIRE_BYTES[w.wire]       # dispatch row bytes
+    yr = w.hiddenDim * workloads.WIRE_BYTES[w.combineDtype]    # combine row bytes
     wt = 1 if w.useWeights else 0
-    disp = (T * H * s + T * K * 4 + wt * T * K * 4            # x, expertIds, weights
-            + U * H * s + U * 4 + U * K * 4 + wt * U * K * 4  # rows, token idx, ids, weights
+    disp = (T * xr + T * K * 4 + wt * T * K * 4               # x, expertIds, weights
+            + U * xr + U * 4 + U * K * 4 + wt * U * K * 4     # rows, token idx, ids, weights
             + T * K * 4 + W * 4)                               # sendMap, recvCount
-    comb = T * K * 4 + wt * (T * K * 4 + T * K * 4) + U * H * s + T * H * s
+    comb = T * K * 4 + wt * (T * K * 4 + T * K * 4) + U * yr + T * yr
     return disp, comb
 
 
@@ -93,8 +99,8 @@ def read_traffic(kernel, workload):
 
 def cpu_baseline(w, inp, budget_s, disp_b, comb_b):
     import oracle
-    step, _ = oracle.timed_step(w.worldSize, w.hiddenDim, w.maxTokPerRank, w.numExpertPerRank,
-                                w.numExpertPerToken, w.useWeights, inp.x, inp.expertIds, inp.weights, inp.y)
+    step, _ = oracle.timed_step(w.worldSize, w.maxTokPerRank, w.numExpertPerRank, w.numExpertPerToken,
+                                w.useWeights, inp.x, inp.expertIds, inp.weights, inp.y)
     step()  # untimed: page in the buffers
     n, t0 = 0, time.perf_counter()
     while True:
@@ -140,6 +146,9 @@ def main():
         del src, dst
 
     w = workloads.CONFIGS[args.workload]
+    if (args.wire, args.combine_dtype) != ("bf16", "bf16"):
+        w = w.with_(name=f"{w.name}_{args.wire}_{args.combine_dtype}", wire=args.wire,
+                    combineDtype=args.combine_dtype)
     print(f"[bench] generating {w.name} seed {args.seed}", file=sys.stderr, flush=True)
     inp = workloads.make_inputs(w, args.seed)
     sets = [GpuRun(w, inp) for _ in range(max(1, args.rotate))]
@@ -209,13 +218,15 @@ def main():
     line = {
         "metric": METRIC, "value": round(value, 1), "unit": "GB/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 5),
-        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": w.wire if w.wire == w.combineDtype else f"{w.wire}+{w.combineDtype}",
         "data": "synthetic",
         "config": {"workload": w.name, "worldSize": w.worldSize, "numExpertPerRank": w.numExpertPerRank,
                    "numTokens": w.numTokens, "maxTokPerRank": w.maxTokPerRank,
                    "numExpertPerToken": w.numExpertPerToken, "hiddenDim": w.hiddenDim,
                    "routing": w.routing + ("(s=1.1)" if w.routing == "zipf" else ""),
                    "useWeights": w.useWeights, "seed": args.seed, "unique_token_pe_pairs": U,
+                   "dispatch_dtype": w.wire, "combine_dtype": w.combineDtype,
                    "bytes_per_step": disp_b + comb_b,
                    "dispatch_us": round(d_ms * 1e3, 2), "combine_us": round(c_ms * 1e3, 2),
                    "buffer_sets_rotated": len(sets), "scratch_clean": scratch_ok,

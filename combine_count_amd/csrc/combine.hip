@@ -1,13 +1,14 @@
-// EP combine for gfx950: gather + weighted reduction, fp32 accumulate,
-// bf16 (round to nearest even) out.
+// EP combine for gfx950: gather + weighted reduction, fp32 accumulate; bf16
+// rows out rounded to nearest even, or fp32 rows out unrounded.
 //
 // MORI JIT v2 design doc, §5 and §9: the HIP backend's combine is a gather
 // (each token pulls the rows its PEs returned); §3.7: combine sums, so it
-// needs an arithmetic dtype (bf16 here).  mori PR #599 "Perf/ep disp 1250
+// needs an arithmetic dtype (bf16 or fp32 here; §5: the HIP backend's combine
+// outputs bf16 or fp32).  mori PR #599 "Perf/ep disp 1250
 // ship", item "meta prefetch": the gather's per-token metadata (token
 // indices, weights) is loaded once, up front.
 //
-// One wave64 per (token, column slab of CPW chunks of 512 elements):
+// One wave64 per (token, column slab of CPW 1 KiB chunks):
 //   * lanes k < K load the token's K sendMap entries, expert ids and weights
 //     once; a ballot over "sendMap >= 0" gives the kept slots, i.e. the
 //     token's PEs in first-appearance order;
@@ -15,7 +16,8 @@
 //     slots on its PE (read from the other lanes by shuffles);
 //   * the PE loop walks the kept slots in ascending order, the next PE's
 //     rows loaded while the current one is reduced (two register buffers);
-//     every lane owns 8 contiguous elements per chunk, one 16-byte access.
+//     every lane owns 16 contiguous bytes per chunk (8 bf16 or 4 fp32
+//     elements), one 16-byte access.
 #include "epdc_internal.h"
 
 namespace epdc {
@@ -43,35 +45,50 @@ __device__ __forceinline__ void fma8(float (&a)[8], float s, u32x4 v) {
     a[7] = __builtin_fmaf(s, bf16hi(v.w), a[7]);
 }
 
-// Loads chunks [slab*CPW, slab*CPW + CPW) of a row; with FULL every chunk is
-// known to be inside the row (H a multiple of 512, chunks a multiple of CPW).
+// Loads chunks [slab*CPW, slab*CPW + CPW) of a row, 16 bytes per lane; with
+// FULL every chunk is known to be inside the row (the row a whole number of
+// 1 KiB chunks, the chunk count a multiple of CPW).
 template <int CPW, bool FULL>
-__device__ __forceinline__ void load_slab(u32x4 (&v)[CPW], const uint16_t *row, int slab, int nChunks,
-                                          int H, int lane) {
+__device__ __forceinline__ void load_slab(u32x4 (&v)[CPW], const uint8_t *row, int slab, int nChunks,
+                                          int rowBytes, int lane) {
 #pragma unroll
     for (int c = 0; c < CPW; ++c) {
         const int gc = slab * CPW + c;
-        const int e = gc * kChunkElems + lane * 8;
-        if (FULL || (gc < nChunks && e < H)) v[c] = load16<EPDC_COMBINE_NT_LOAD>(row + e);
+        const int e = gc * kChunkBytes + lane * 16;
+        if (FULL || (gc < nChunks && e < rowBytes)) v[c] = load16<EPDC_COMBINE_NT_LOAD>(row + e);
+    }
+}
+
+// acc += s * row for one lane's 16 bytes: 8 bf16 or 4 fp32 elements.
+template <bool FP32>
+__device__ __forceinline__ void fma_chunk(float (&a)[8], float s, u32x4 v) {
+    if (FP32) {
+        a[0] = __builtin_fmaf(s, __uint_as_float(v.x), a[0]);
+        a[1] = __builtin_fmaf(s, __uint_as_float(v.y), a[1]);
+        a[2] = __builtin_fmaf(s, __uint_as_float(v.z), a[2]);
+        a[3] = __builtin_fmaf(s, __uint_as_float(v.w), a[3]);
+    } else {
+        fma8(a, s, v);
     }
 }
 
 // acc += sc[j] * row j for j = 0..N-1, in that order; all N rows' chunks are
 // loaded first.
-template <int N, int CPW, bool FULL>
+template <int N, int CPW, bool FULL, bool FP32>
 __device__ __forceinline__ void gather_reduce(float (&acc)[CPW][8], const CombineParams &P,
                                               const int32_t (&fl)[8], const float (&sc)[8], int slab,
                                               int lane) {
     u32x4 v[N][CPW];
 #pragma unroll
-    for (int j = 0; j < N; ++j) load_slab<CPW, FULL>(v[j], P.y + (int64_t)fl[j] * P.H, slab, P.nChunks, P.H, lane);
+    for (int j = 0; j < N; ++j)
+        load_slab<CPW, FULL>(v[j], P.y + (int64_t)fl[j] * P.rowBytes, slab, P.nChunks, P.rowBytes, lane);
 #pragma unroll
     for (int j = 0; j < N; ++j)
 #pragma unroll
-        for (int c = 0; c < CPW; ++c) fma8(acc[c], sc[j], v[j][c]);
+        for (int c = 0; c < CPW; ++c) fma_chunk<FP32>(acc[c], sc[j], v[j][c]);
 }
 
-template <int CPW, bool FULL>
+template <int CPW, bool FULL, bool FP32>
 __global__ __launch_bounds__(256) void combine_kernel(CombineParams P, int nSlabs) {
     const int lane = threadIdx.x & 63;
     const int item = blockIdx.x * 4 + (threadIdx.x >> 6);
@@ -132,57 +149,69 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineParams P, int nSlab
             rem &= rem - 1;
         }
         switch (n) {
-            case 1: gather_reduce<1, CPW, FULL>(acc, P, fl, sc, slab, lane); break;
-            case 2: if constexpr (kGroup >= 2) gather_reduce<2, CPW, FULL>(acc, P, fl, sc, slab, lane); break;
-            case 3: if constexpr (kGroup >= 3) gather_reduce<3, CPW, FULL>(acc, P, fl, sc, slab, lane); break;
-            case 4: if constexpr (kGroup >= 4) gather_reduce<4, CPW, FULL>(acc, P, fl, sc, slab, lane); break;
-            case 5: if constexpr (kGroup >= 5) gather_reduce<5, CPW, FULL>(acc, P, fl, sc, slab, lane); break;
-            case 6: if constexpr (kGroup >= 6) gather_reduce<6, CPW, FULL>(acc, P, fl, sc, slab, lane); break;
-            case 7: if constexpr (kGroup >= 7) gather_reduce<7, CPW, FULL>(acc, P, fl, sc, slab, lane); break;
-            default: if constexpr (kGroup >= 8) gather_reduce<8, CPW, FULL>(acc, P, fl, sc, slab, lane); break;
+            case 1: gather_reduce<1, CPW, FULL, FP32>(acc, P, fl, sc, slab, lane); break;
+            case 2: if constexpr (kGroup >= 2) gather_reduce<2, CPW, FULL, FP32>(acc, P, fl, sc, slab, lane); break;
+            case 3: if constexpr (kGroup >= 3) gather_reduce<3, CPW, FULL, FP32>(acc, P, fl, sc, slab, lane); break;
+            case 4: if constexpr (kGroup >= 4) gather_reduce<4, CPW, FULL, FP32>(acc, P, fl, sc, slab, lane); break;
+            case 5: if constexpr (kGroup >= 5) gather_reduce<5, CPW, FULL, FP32>(acc, P, fl, sc, slab, lane); break;
+            case 6: if constexpr (kGroup >= 6) gather_reduce<6, CPW, FULL, FP32>(acc, P, fl, sc, slab, lane); break;
+            case 7: if constexpr (kGroup >= 7) gather_reduce<7, CPW, FULL, FP32>(acc, P, fl, sc, slab, lane); break;
+            default: if constexpr (kGroup >= 8) gather_reduce<8, CPW, FULL, FP32>(acc, P, fl, sc, slab, lane); break;
         }
     }
 
-    uint16_t *orow = P.out + (int64_t)t * P.H;
+    uint8_t *orow = P.out + (int64_t)t * P.rowBytes;
 #pragma unroll
     for (int c = 0; c < CPW; ++c) {
         const int gc = slab * CPW + c;
-        const int e = gc * kChunkElems + lane * 8;
-        if (FULL || (gc < P.nChunks && e < P.H)) {
+        const int e = gc * kChunkBytes + lane * 16;
+        if (FULL || (gc < P.nChunks && e < P.rowBytes)) {
             u32x4 o;
-            o.x = f32_to_bf16(acc[c][0]) | (f32_to_bf16(acc[c][1]) << 16);
-            o.y = f32_to_bf16(acc[c][2]) | (f32_to_bf16(acc[c][3]) << 16);
-            o.z = f32_to_bf16(acc[c][4]) | (f32_to_bf16(acc[c][5]) << 16);
-            o.w = f32_to_bf16(acc[c][6]) | (f32_to_bf16(acc[c][7]) << 16);
+            if (FP32) {
+                o.x = __float_as_uint(acc[c][0]);
+                o.y = __float_as_uint(acc[c][1]);
+                o.z = __float_as_uint(acc[c][2]);
+                o.w = __float_as_uint(acc[c][3]);
+            } else {
+                o.x = f32_to_bf16(acc[c][0]) | (f32_to_bf16(acc[c][1]) << 16);
+                o.y = f32_to_bf16(acc[c][2]) | (f32_to_bf16(acc[c][3]) << 16);
+                o.z = f32_to_bf16(acc[c][4]) | (f32_to_bf16(acc[c][5]) << 16);
+                o.w = f32_to_bf16(acc[c][6]) | (f32_to_bf16(acc[c][7]) << 16);
+            }
             store16<EPDC_COMBINE_NT_STORE>(orow + e, o);
         }
     }
 }
 
-template <int CPW>
+template <int CPW, bool FP32>
 hipError_t launch(const CombineParams &P, hipStream_t stream) {
     const int nSlabs = ceil_div(P.nChunks, CPW);
     const int64_t waves = (int64_t)P.T * nSlabs;
-    const bool full = (P.H % kChunkElems == 0) && (P.nChunks % CPW == 0);
+    const bool full = (P.rowBytes % kChunkBytes == 0) && (P.nChunks % CPW == 0);
     if (full)
-        hipLaunchKernelGGL((combine_kernel<CPW, true>), dim3(ceil_div(waves, 4)), dim3(256), 0, stream, P,
+        hipLaunchKernelGGL((combine_kernel<CPW, true, FP32>), dim3(ceil_div(waves, 4)), dim3(256), 0, stream, P,
                            nSlabs);
     else
-        hipLaunchKernelGGL((combine_kernel<CPW, false>), dim3(ceil_div(waves, 4)), dim3(256), 0, stream, P,
+        hipLaunchKernelGGL((combine_kernel<CPW, false, FP32>), dim3(ceil_div(waves, 4)), dim3(256), 0, stream, P,
                            nSlabs);
     return hipGetLastError();
 }
 
+template <bool FP32>
+hipError_t launch_dtype(const CombineParams &P, hipStream_t stream) {
+#if EPDC_COMBINE_CPW == 0
+    if (P.nChunks % 2 == 0 && (int64_t)P.T * (P.nChunks / 2) >= 8192) return launch<2, FP32>(P, stream);
+    return launch<1, FP32>(P, stream);
+#else
+    return launch<EPDC_COMBINE_CPW, FP32>(P, stream);
+#endif
+}
+
 }  // namespace
 
-hipError_t launch_combine(const CombineParams &P, hipStream_t stream) {
+hipError_t launch_combine(const CombineParams &P, bool fp32, hipStream_t stream) {
     if (P.T == 0) return hipSuccess;
-#if EPDC_COMBINE_CPW == 0
-    if (P.nChunks % 2 == 0 && (int64_t)P.T * (P.nChunks / 2) >= 8192) return launch<2>(P, stream);
-    return launch<1>(P, stream);
-#else
-    return launch<EPDC_COMBINE_CPW>(P, stream);
-#endif
+    return fp32 ? launch_dtype<true>(P, stream) : launch_dtype<false>(P, stream);
 }
 
 }  // namespace epdc

@@ -76,27 +76,28 @@ __global__ __launch_bounds__(64) void zero_count_kernel(int32_t *recvCount, int3
 }
 
 // Chunks [slab*CPW, slab*CPW + CPW) of one row, 16 bytes per lane.  With
-// FULL every chunk is known to lie inside the row (H a multiple of 512 and
-// the chunk count a multiple of CPW), so there is no per-lane bound check.
+// FULL every chunk is known to lie inside the row (the row a whole number of
+// 1 KiB chunks and the chunk count a multiple of CPW), so there is no
+// per-lane bound check.  Rows are bytes: the wire dtype does not matter.
 template <int CPW, bool FULL>
-__device__ __forceinline__ void load_slab(u32x4 (&v)[CPW], const uint16_t *row, int slab, int nChunks,
-                                          int H, int lane) {
+__device__ __forceinline__ void load_slab(u32x4 (&v)[CPW], const uint8_t *row, int slab, int nChunks,
+                                          int rowBytes, int lane) {
 #pragma unroll
     for (int c = 0; c < CPW; ++c) {
         const int gc = slab * CPW + c;
-        const int e = gc * kChunkElems + lane * 8;
-        if (FULL || (gc < nChunks && e < H)) v[c] = load16<kNtLoad>(row + e);
+        const int e = gc * kChunkBytes + lane * 16;
+        if (FULL || (gc < nChunks && e < rowBytes)) v[c] = load16<kNtLoad>(row + e);
     }
 }
 
 template <int CPW, bool FULL>
-__device__ __forceinline__ void store_slab(const u32x4 (&v)[CPW], uint16_t *row, int slab, int nChunks,
-                                           int H, int lane) {
+__device__ __forceinline__ void store_slab(const u32x4 (&v)[CPW], uint8_t *row, int slab, int nChunks,
+                                           int rowBytes, int lane) {
 #pragma unroll
     for (int c = 0; c < CPW; ++c) {
         const int gc = slab * CPW + c;
-        const int e = gc * kChunkElems + lane * 8;
-        if (FULL || (gc < nChunks && e < H)) store16<kNtStore>(row + e, v[c]);
+        const int e = gc * kChunkBytes + lane * 16;
+        if (FULL || (gc < nChunks && e < rowBytes)) store16<kNtStore>(row + e, v[c]);
     }
 }
 
@@ -116,7 +117,7 @@ __device__ __forceinline__ void store_dest(const DispatchParams &P, const u32x4 
                                            int p, int slab, int lane) {
     const int32_t r = uniform(sPre[p] + __popcll(sBal[p] & lt));
     if (row_ok(P, r))
-        store_slab<CPW, FULL>(v, P.recvX + ((int64_t)p * P.M + r) * P.H, slab, P.nChunks, P.H, lane);
+        store_slab<CPW, FULL>(v, P.recvX + ((int64_t)p * P.M + r) * P.rowBytes, slab, P.nChunks, P.rowBytes, lane);
 }
 
 template <int CPW, bool FULL>
@@ -187,7 +188,7 @@ __global__ __launch_bounds__(256) void dispatch_kernel(DispatchParams P, int nSl
     const int32_t tok0 = tile * kTile;
     const int nTok = min(kTile, P.T - tok0);
     const int iBeg = (sub * 4 + wave) * NTW;  // this wave's tokens: [iBeg, iBeg + NTW) of the tile
-    const uint16_t *xTile = P.x + (int64_t)tok0 * P.H;
+    const uint8_t *xTile = P.x + (int64_t)tok0 * P.rowBytes;
     // A launch of one tile needs no scratch at all (its base rows are 0); a
     // block whose token group lies past the last token only counts itself
     // done.
@@ -202,7 +203,7 @@ __global__ __launch_bounds__(256) void dispatch_kernel(DispatchParams P, int nSl
 #pragma unroll
         for (int j = 0; j < NTW; ++j) {
             const int i = min(iBeg + j, nTok - 1);
-            load_slab<CPW, FULL>(buf[j], xTile + (int64_t)i * P.H, slab, P.nChunks, P.H, lane);
+            load_slab<CPW, FULL>(buf[j], xTile + (int64_t)i * P.rowBytes, slab, P.nChunks, P.rowBytes, lane);
         }
     };
 #if EPDC_DISPATCH_XLOAD_PHASE == 0
@@ -359,7 +360,7 @@ hipError_t launch_fused(const DispatchParams &P, int nTiles, hipStream_t stream)
     const int nSubs = kTile / (4 * NTW);
     const int nSlabs = ceil_div(P.nChunks, CPW);
     const int nBlocks = nTiles * nSubs * nSlabs;
-    if (P.H % kChunkElems == 0 && P.nChunks % CPW == 0)
+    if (P.rowBytes % kChunkBytes == 0 && P.nChunks % CPW == 0)
         hipLaunchKernelGGL((dispatch_kernel<CPW, NTW, true>), dim3(nBlocks), dim3(256), 0, stream, P, nSlabs,
                            nSubs, nBlocks);
     else
@@ -391,15 +392,22 @@ hipError_t launch_dispatch(const DispatchParams &P, hipStream_t stream) {
     return launch_fused<EPDC_DISPATCH_CPW, EPDC_DISPATCH_NTW>(P, nTiles, stream);
 #else
     // Slab width: the widest of 8/7/4/2 chunks that divides the row (a wave
-    // then moves up to 8 KiB of a token with no bound checks); rows that are
-    // not a whole number of chunks use 1-chunk slabs with per-lane checks.
-    if (P.H % kChunkElems == 0) {
+    // then moves up to 8 KiB of a token with no bound checks).  Other rows
+    // (not a whole number of 1 KiB chunks, e.g. 3.5 KiB fp4x2 rows at
+    // hidden 7168) take the narrowest of 1/2/4/7/8 chunks that covers the row
+    // (8 beyond that) with bound checks on the tail.
+    if (P.rowBytes % kChunkBytes == 0) {
         if (P.nChunks % 8 == 0) return launch_cpw<8>(P, nTiles, stream);
         if (P.nChunks % 7 == 0) return launch_cpw<7>(P, nTiles, stream);
         if (P.nChunks % 4 == 0) return launch_cpw<4>(P, nTiles, stream);
         if (P.nChunks % 2 == 0) return launch_cpw<2>(P, nTiles, stream);
+        return launch_cpw<1>(P, nTiles, stream);
     }
-    return launch_cpw<1>(P, nTiles, stream);
+    if (P.nChunks <= 1) return launch_cpw<1>(P, nTiles, stream);
+    if (P.nChunks <= 2) return launch_cpw<2>(P, nTiles, stream);
+    if (P.nChunks <= 4) return launch_cpw<4>(P, nTiles, stream);
+    if (P.nChunks <= 7) return launch_cpw<7>(P, nTiles, stream);
+    return launch_cpw<8>(P, nTiles, stream);
 #endif
 }
 

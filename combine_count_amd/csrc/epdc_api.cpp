@@ -41,10 +41,24 @@ int32_t log2_exact(int32_t v) {
     return s;
 }
 
+// Bytes per element of a row.  Dispatch moves any EpDType (fp8 and fp4x2 are
+// one byte each; for fp4x2 hiddenDim counts bytes); combine sums, so only
+// the arithmetic types bf16 and fp32 (MORI JIT v2 design doc, §3.7 and §5).
+// -1 if the dtype is not allowed on that leg.
+int32_t elem_bytes(int32_t dtype, bool combine) {
+    switch (dtype) {
+        case EPDC_BF16: return 2;
+        case EPDC_FP32: return 4;
+        case EPDC_FP8:
+        case EPDC_FP4X2: return combine ? -1 : 1;
+        default: return -1;
+    }
+}
+
 // Checks shared by both entry points (EpCfg validity: MORI JIT v2 design doc,
 // §3.5 -- 16-byte token rows, topk and worldSize within one wavefront,
 // receive capacity covering the worst case).
-int check_cfg(const epdc_cfg *c, int32_t numTokens) {
+int check_cfg(const epdc_cfg *c, int32_t numTokens, bool combine) {
     if (!c) return fail(EPDC_ERR_NULLPTR, "cfg is NULL");
     if (c->worldSize < 1 || c->worldSize > 64)
         return fail(EPDC_ERR_INVALID_ARG, "worldSize %d outside [1, 64]", c->worldSize);
@@ -61,13 +75,18 @@ int check_cfg(const epdc_cfg *c, int32_t numTokens) {
     if (c->maxTokPerRank < 1) return fail(EPDC_ERR_INVALID_ARG, "maxTokPerRank %d < 1", c->maxTokPerRank);
     if ((int64_t)c->worldSize * c->maxTokPerRank > INT32_MAX)
         return fail(EPDC_ERR_INVALID_ARG, "worldSize*maxTokPerRank overflows the int32 flat index");
-    if (c->dtype != EPDC_BF16)
-        return fail(EPDC_ERR_UNSUPPORTED, "dtype %d not supported (only EPDC_BF16 = 0)", c->dtype);
+    const int32_t eb = elem_bytes(c->dtype, combine);
+    if (eb < 0)
+        return combine ? fail(EPDC_ERR_UNSUPPORTED, "combine sums its rows: dtype %d is not EPDC_BF16 or EPDC_FP32",
+                              c->dtype)
+                       : fail(EPDC_ERR_UNSUPPORTED, "dtype %d is not an EPDC dtype (0..3)", c->dtype);
     if (c->useWeights != 0 && c->useWeights != 1)
         return fail(EPDC_ERR_UNSUPPORTED, "useWeights must be 0 or 1, got %d", c->useWeights);
-    if (((int64_t)c->hiddenDim * 2) % 16 != 0)
-        return fail(EPDC_ERR_ALIGN, "hiddenDim*2 = %lld bytes is not a multiple of 16",
-                    (long long)c->hiddenDim * 2);
+    if (((int64_t)c->hiddenDim * eb) % 16 != 0)
+        return fail(EPDC_ERR_ALIGN, "row of hiddenDim*%d = %lld bytes is not a multiple of 16", eb,
+                    (long long)c->hiddenDim * eb);
+    if ((int64_t)c->hiddenDim * eb > INT32_MAX)
+        return fail(EPDC_ERR_INVALID_ARG, "row of %lld bytes is too long", (long long)c->hiddenDim * eb);
     if (numTokens < 0) return fail(EPDC_ERR_INVALID_ARG, "numTokens %d < 0", numTokens);
     if (numTokens > c->maxTokPerRank)
         return fail(EPDC_ERR_CAPACITY, "numTokens %d > maxTokPerRank %d", numTokens, c->maxTokPerRank);
@@ -90,7 +109,7 @@ extern "C" {
 
 size_t epdc_dispatch_scratch_bytes(const epdc_cfg *cfg) {
     try {
-        if (check_cfg(cfg, 0) != EPDC_OK) return 0;
+        if (check_cfg(cfg, 0, false) != EPDC_OK) return 0;
         return scratch_bytes(cfg);
     } catch (...) {
         return 0;
@@ -103,7 +122,7 @@ int epdc_dispatch(const epdc_cfg *cfg, int32_t numTokens, const void *x, const i
                   size_t scratchBytes, void *stream) {
     try {
         g_lastError.clear();
-        int rc = check_cfg(cfg, numTokens);
+        int rc = check_cfg(cfg, numTokens, false);
         if (rc != EPDC_OK) return rc;
         if (!recvCount) return fail(EPDC_ERR_NULLPTR, "recvCount is NULL");
         if (!aligned(recvCount, 4)) return fail(EPDC_ERR_ALIGN, "recvCount not 4-byte aligned");
@@ -132,11 +151,12 @@ int epdc_dispatch(const epdc_cfg *cfg, int32_t numTokens, const void *x, const i
         P.useWeights = cfg->useWeights;
         P.Wp = pow2_ceil(cfg->worldSize);
         P.eprShift = log2_exact(cfg->numExpertPerRank);
-        P.nChunks = epdc::ceil_div(cfg->hiddenDim, epdc::kChunkElems);
-        P.x = static_cast<const uint16_t *>(x);
+        P.rowBytes = cfg->hiddenDim * elem_bytes(cfg->dtype, false);
+        P.nChunks = epdc::ceil_div(P.rowBytes, epdc::kChunkBytes);
+        P.x = static_cast<const uint8_t *>(x);
         P.expertIds = expertIds;
         P.weights = cfg->useWeights ? weights : nullptr;
-        P.recvX = static_cast<uint16_t *>(recvX);
+        P.recvX = static_cast<uint8_t *>(recvX);
         P.recvTokIdx = recvTokIdx;
         P.recvExpertIds = recvExpertIds;
         P.recvWeights = cfg->useWeights ? recvWeights : nullptr;
@@ -153,7 +173,7 @@ int epdc_combine(const epdc_cfg *cfg, int32_t numTokens, const void *y, const in
                  const float *weights, const int32_t *sendMap, void *out, void *stream) {
     try {
         g_lastError.clear();
-        int rc = check_cfg(cfg, numTokens);
+        int rc = check_cfg(cfg, numTokens, true);
         if (rc != EPDC_OK) return rc;
         if (numTokens == 0) return EPDC_OK;
         if (!y || !expertIds || !sendMap || !out)
@@ -172,13 +192,15 @@ int epdc_combine(const epdc_cfg *cfg, int32_t numTokens, const void *y, const in
         P.T = numTokens;
         P.useWeights = cfg->useWeights;
         P.eprShift = log2_exact(cfg->numExpertPerRank);
-        P.nChunks = epdc::ceil_div(cfg->hiddenDim, epdc::kChunkElems);
-        P.y = static_cast<const uint16_t *>(y);
+        P.rowBytes = cfg->hiddenDim * elem_bytes(cfg->dtype, true);
+        P.nChunks = epdc::ceil_div(P.rowBytes, epdc::kChunkBytes);
+        P.y = static_cast<const uint8_t *>(y);
         P.expertIds = expertIds;
         P.weights = cfg->useWeights ? weights : nullptr;
         P.sendMap = sendMap;
-        P.out = static_cast<uint16_t *>(out);
-        return hip_status(epdc::launch_combine(P, static_cast<hipStream_t>(stream)), "combine launch");
+        P.out = static_cast<uint8_t *>(out);
+        return hip_status(epdc::launch_combine(P, cfg->dtype == EPDC_FP32, static_cast<hipStream_t>(stream)),
+                          "combine launch");
     } catch (...) {
         return fail(EPDC_ERR_HIP, "unexpected C++ exception in epdc_combine");
     }

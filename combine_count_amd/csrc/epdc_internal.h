@@ -62,13 +62,13 @@ __device__ __forceinline__ void wait_vmcnt() {
 
 // 16-byte access, optionally with the non-temporal (streaming) hint.
 template <bool NT>
-__device__ __forceinline__ u32x4 load16(const uint16_t *p) {
+__device__ __forceinline__ u32x4 load16(const uint8_t *p) {
     if (NT) return __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(p));
     return *reinterpret_cast<const u32x4 *>(p);
 }
 
 template <bool NT>
-__device__ __forceinline__ void store16(uint16_t *p, u32x4 v) {
+__device__ __forceinline__ void store16(uint8_t *p, u32x4 v) {
     if (NT)
         __builtin_nontemporal_store(v, reinterpret_cast<u32x4 *>(p));
     else
@@ -77,18 +77,20 @@ __device__ __forceinline__ void store16(uint16_t *p, u32x4 v) {
 
 // Routing tile: 64 tokens, one per lane of a wave64.
 constexpr int kTile = 64;
-// One 16-byte access per lane of a wave64 moves 512 bf16 elements (1 KiB).
-constexpr int kChunkElems = 512;
+// One 16-byte access per lane of a wave64 moves a 1 KiB chunk of a row
+// (512 bf16, 256 fp32 or 1024 one-byte elements).
+constexpr int kChunkBytes = 1024;
 
 struct DispatchParams {
     int32_t W, H, M, Epr, K, T, useWeights;
+    int32_t rowBytes;  // H * element size of the wire dtype (a multiple of 16)
     int32_t Wp;        // W rounded up to a power of two (tile-count row stride)
     int32_t eprShift;  // log2(Epr) when Epr is a power of two, else -1
-    int32_t nChunks;   // ceil(H / kChunkElems)
-    const uint16_t *x;
+    int32_t nChunks;   // ceil(rowBytes / kChunkBytes)
+    const uint8_t *x;
     const int32_t *expertIds;
     const float *weights;
-    uint16_t *recvX;
+    uint8_t *recvX;
     int32_t *recvTokIdx;
     int32_t *recvExpertIds;
     float *recvWeights;
@@ -109,19 +111,20 @@ constexpr int kScratchHeaderWords = kScratchGroupBase + kDoneGroups * kDoneStrid
 
 struct CombineParams {
     int32_t W, H, M, Epr, K, T, useWeights;
+    int32_t rowBytes;  // H * 2 (bf16) or H * 4 (fp32)
     int32_t eprShift;
-    int32_t nChunks;
-    const uint16_t *y;
+    int32_t nChunks;   // ceil(rowBytes / kChunkBytes)
+    const uint8_t *y;
     const int32_t *expertIds;
     const float *weights;
     const int32_t *sendMap;
-    uint16_t *out;
+    uint8_t *out;
 };
 
 __host__ __device__ inline int32_t ceil_div(int64_t a, int64_t b) { return (int32_t)((a + b - 1) / b); }
 
 // Launchers: enqueue on `stream`, return the hipGetLastError() after launch.
 hipError_t launch_dispatch(const DispatchParams &p, hipStream_t stream);
-hipError_t launch_combine(const CombineParams &p, hipStream_t stream);
+hipError_t launch_combine(const CombineParams &p, bool fp32, hipStream_t stream);
 
 }  // namespace epdc

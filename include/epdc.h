@@ -39,8 +39,13 @@
 extern "C" {
 #endif
 
-/* Wire dtype numbering kept equal to the pages' EpDType (MORI JIT v2 design
- * doc, §3.7 and §7: the enum values must match the binding's table). */
+/* Row element types, numbered as the pages' EpDType (MORI JIT v2 design doc,
+ * §3.7 and §7: the enum values must match the binding's table).  Dispatch
+ * only moves rows, so it takes all four: bf16 (2 bytes per element), fp32 (4)
+ * and the one-byte fp8 and fp4x2 (for fp4x2 one element is a byte holding
+ * two e2m1 values, so hiddenDim counts bytes).  Combine sums rows, so it
+ * takes only EPDC_BF16 and EPDC_FP32.  A narrow-wire pair (fp8 or fp4x2
+ * dispatch, bf16 combine) is two calls with two cfgs. */
 typedef enum {
     EPDC_BF16 = 0,
     EPDC_FP32 = 1,
@@ -51,9 +56,9 @@ typedef enum {
 enum {
     EPDC_OK = 0,
     EPDC_ERR_INVALID_ARG = -1, /* a cfg field out of range, numTokens < 0, K > E, W*M too large */
-    EPDC_ERR_UNSUPPORTED = -2, /* dtype other than EPDC_BF16, useWeights not 0/1              */
+    EPDC_ERR_UNSUPPORTED = -2, /* dtype not allowed on this call (see above), useWeights not 0/1 */
     EPDC_ERR_CAPACITY = -3,    /* numTokens > maxTokPerRank                                    */
-    EPDC_ERR_ALIGN = -4,       /* hiddenDim*2 not a multiple of 16, or a misaligned pointer    */
+    EPDC_ERR_ALIGN = -4,       /* row bytes not a multiple of 16, or a misaligned pointer      */
     EPDC_ERR_NULLPTR = -5,     /* a required pointer (or cfg) is NULL                          */
     EPDC_ERR_SCRATCH = -6,     /* scratchBytes below epdc_dispatch_scratch_bytes(cfg)          */
     EPDC_ERR_HIP = -7          /* the HIP runtime reported an error (no device, launch failed) */
@@ -61,12 +66,13 @@ enum {
 
 /* Shape and options of one dispatch/combine pair (EpCfg field names).
  *   worldSize          W, 1..64 (one bit per PE in a 64-lane wavefront)
- *   hiddenDim          H elements per token row; H*2 bytes must be a multiple of 16
+ *   hiddenDim          H elements per token row; the row, H times the element
+ *                      size of dtype, must be a multiple of 16 bytes
  *   maxTokPerRank      M >= 1: capacity of x and of each receive window, in rows;
  *                      W*M must not exceed 2^31-1 (flat indices are int32)
  *   numExpertPerRank   Epr >= 1; expert e lives on PE e / Epr
  *   numExpertPerToken  K, 1..64, K <= E
- *   dtype              EPDC_BF16 only
+ *   dtype              row element type (epdc_dtype; see above for each call)
  *   useWeights         1: dispatch copies the weights, combine applies them; 0: ignored */
 typedef struct epdc_cfg {
     int32_t worldSize;
@@ -95,12 +101,12 @@ size_t epdc_dispatch_scratch_bytes(const epdc_cfg *cfg);
  * Dispatch numTokens tokens (0 <= numTokens <= maxTokPerRank).
  *
  * Inputs (device, read only):
- *   x            [T][H] bf16 token rows, 16-byte aligned
+ *   x            [T][H] token rows of cfg->dtype, 16-byte aligned
  *   expertIds    [T][K] int32 top-k expert ids; an id outside [0, E) marks a
  *                dropped slot (ids are not range-checked on the host)
  *   weights      [T][K] fp32; may be NULL iff useWeights == 0
  * Outputs (device, written):
- *   recvX          [W][M][H] bf16, 16-byte aligned: recvX[p][r] is a bitwise copy
+ *   recvX          [W][M][H] of cfg->dtype, 16-byte aligned: recvX[p][r] is a bitwise copy
  *                  of the r-th token (ascending token order) that reaches PE p
  *   recvTokIdx     [W][M] int32: that token's index
  *   recvExpertIds  [W][M][K] int32: that token's K expert ids
@@ -126,18 +132,20 @@ int epdc_dispatch(const epdc_cfg *cfg, int32_t numTokens,
 /*
  * Combine numTokens tokens from the rows their PEs returned.
  *
+ * cfg->dtype is EPDC_BF16 or EPDC_FP32: the type of y and out.
  * Inputs (device, read only):
- *   y          [W][M][H] bf16, 16-byte aligned: returned rows, indexed like recvX
+ *   y          [W][M][H] of cfg->dtype, 16-byte aligned: returned rows, indexed like recvX
  *   expertIds  [T][K] int32, the ids given to the matching dispatch
  *   weights    [T][K] fp32 or NULL iff useWeights == 0
  *   sendMap    [T][K] int32 as written by the matching dispatch
- * Output (device): out [T][H] bf16, 16-byte aligned.
+ * Output (device): out [T][H] of cfg->dtype, 16-byte aligned.
  *
  * For token t, the PEs of its kept slots (sendMap >= 0) are visited in
  * ascending slot order.  PE p's scale is the fp32 sum, in slot order from +0,
  * of the weights of t's slots whose valid expert lives on p (1 when
- * useWeights == 0).  out[t][h] = bf16_rne(acc), acc = fmaf(scale_p,
- * y[p][r_p][h], acc) over those PEs from acc = +0.  A token with no kept slot
+ * useWeights == 0).  acc = fmaf(scale_p, y[p][r_p][h], acc) over those PEs
+ * from acc = +0 in fp32; out[t][h] = bf16_rne(acc) for bf16 rows (nearest,
+ * ties to even) and acc itself for fp32 rows.  A token with no kept slot
  * yields +0.  A sendMap entry outside [0, W*M) counts as a dropped slot.
  * Results are deterministic and bit-identical run to run.
  */

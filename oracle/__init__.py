@@ -131,29 +131,32 @@ def combine(W, H, M, Epr, K, useWeights, y, expertIds, weights, sendMap, tokens=
     return out
 
 
-def timed_step(W, H, M, Epr, K, useWeights, x, expertIds, weights, y, lib=None):
+def timed_step(W, M, Epr, K, useWeights, x, expertIds, weights, y, lib=None):
     """A callable running one oracle dispatch + combine into preallocated
     buffers (allocation kept out of the timed call), for bench.py's CPU
-    baseline.  Returns (step, outputs)."""
+    baseline.  x: [T][Hd] rows of any 1/2/4-byte type; y: [W][M][Hc] bf16
+    bits (uint16) or float32.  Returns (step, outputs)."""
     lib = lib or load()
-    T = x.shape[0]
+    T, Hd = x.shape
+    Hc = y.shape[2]
+    fp32 = y.dtype == np.float32
     outs = dict(
-        recvX=np.empty((W, M, H), np.uint16), recvTokIdx=np.empty((W, M), np.int32),
+        recvX=np.empty((W, M, Hd), x.dtype), recvTokIdx=np.empty((W, M), np.int32),
         recvExpertIds=np.empty((W, M, K), np.int32), recvWeights=np.empty((W, M, K), np.float32),
         recvCount=np.empty((W,), np.int32), sendMap=np.empty((T, K), np.int32),
-        out=np.empty((T, H), np.uint16), acc=np.empty((H,), np.float32))
-    x = np.ascontiguousarray(x, dtype=np.uint16)
+        out=np.empty((T, Hc), y.dtype), acc=np.empty((Hc,), np.float32))
+    x = np.ascontiguousarray(x)
     expertIds = np.ascontiguousarray(expertIds, dtype=np.int32)
     weights = np.ascontiguousarray(weights, dtype=np.float32) if useWeights else None
-    y = np.ascontiguousarray(y, dtype=np.uint16)
+    y = np.ascontiguousarray(y)
     o = outs
 
     def step():
-        rc = lib.oracle_dispatch(W, H, M, Epr, K, int(useWeights), T, 2, _ptr(x), _ptr(expertIds),
+        rc = lib.oracle_dispatch(W, Hd, M, Epr, K, int(useWeights), T, x.itemsize, _ptr(x), _ptr(expertIds),
                                  _ptr(weights), _ptr(o["recvX"]), _ptr(o["recvTokIdx"]),
                                  _ptr(o["recvExpertIds"]), _ptr(o["recvWeights"]), _ptr(o["recvCount"]),
                                  _ptr(o["sendMap"]))
-        rc |= lib.oracle_combine(W, H, M, Epr, K, int(useWeights), T, 0, _ptr(y), _ptr(expertIds),
+        rc |= lib.oracle_combine(W, Hc, M, Epr, K, int(useWeights), T, int(fp32), _ptr(y), _ptr(expertIds),
                                  _ptr(weights), _ptr(o["sendMap"]), None, T, _ptr(o["acc"]), _ptr(o["out"]))
         if rc:
             raise RuntimeError("oracle step failed")

@@ -13,17 +13,29 @@ import combine_count_amd as epdc
 import oracle
 import workloads
 
-SENT_X = 0xDEAD           # bf16 bits
+SENT_X_BYTE = 0xAD        # every byte of recvX before the dispatch
+SENT_OUT_BYTE = 0x7F
 SENT_I32 = -12345
 SENT_IDS = -777
 SENT_W = -3.5
 SENT_MAP = -99
-FILL = {"recvX": SENT_X, "recvTokIdx": SENT_I32, "recvExpertIds": SENT_IDS, "recvWeights": SENT_W}
+FILL = {"recvX_byte": SENT_X_BYTE, "recvTokIdx": SENT_I32, "recvExpertIds": SENT_IDS, "recvWeights": SENT_W}
 
 
-def cfg_of(w: workloads.Workload) -> epdc.EpCfg:
-    return epdc.EpCfg(w.worldSize, w.hiddenDim, w.maxTokPerRank, w.numExpertPerRank,
-                      w.numExpertPerToken, epdc.EPDC_BF16, w.useWeights)
+def cfg_of(w: workloads.Workload, combine: bool = False) -> epdc.EpCfg:
+    """The dispatch cfg (wire type, hiddenDim in wire elements) or the
+    combine cfg (combine type, logical hiddenDim)."""
+    if combine:
+        return epdc.EpCfg(w.worldSize, w.hiddenDim, w.maxTokPerRank, w.numExpertPerRank, w.numExpertPerToken,
+                          workloads.EPDC_DTYPE[w.combineDtype], w.useWeights)
+    return epdc.EpCfg(w.worldSize, w.dispatchHidden, w.maxTokPerRank, w.numExpertPerRank, w.numExpertPerToken,
+                      workloads.EPDC_DTYPE[w.wire], w.useWeights)
+
+
+def to_dev_bytes(a: np.ndarray, dev="cuda") -> torch.Tensor:
+    """Any numpy array as a device uint8 tensor of the same bytes, rows kept."""
+    a = np.ascontiguousarray(a)
+    return torch.from_numpy(a.view(np.uint8).reshape(*a.shape[:-1], a.shape[-1] * a.itemsize)).to(dev)
 
 
 def bits_to_dev(bits: np.ndarray, dev="cuda") -> torch.Tensor:
@@ -35,18 +47,21 @@ def dev_to_bits(t: torch.Tensor) -> np.ndarray:
 
 
 class GpuRun:
-    """Device copies of one input set plus sentinel-filled dispatch outputs."""
+    """Device copies of one input set plus sentinel-filled dispatch outputs.
+    Payload buffers are raw bytes; their element type is the cfg's."""
 
     def __init__(self, w: workloads.Workload, inp: workloads.Inputs, dev="cuda"):
         self.w = w
         self.cfg = cfg_of(w)
-        W, M, H, K, T = w.worldSize, w.maxTokPerRank, w.hiddenDim, w.numExpertPerToken, w.numTokens
-        self.x = bits_to_dev(inp.x, dev)
+        self.ccfg = cfg_of(w, combine=True)
+        W, M, K, T = w.worldSize, w.maxTokPerRank, w.numExpertPerToken, w.numTokens
+        rowB = w.dispatchHidden * workloads.WIRE_BYTES[w.wire]
+        outB = w.hiddenDim * workloads.WIRE_BYTES[w.combineDtype]
+        self.x = to_dev_bytes(inp.x, dev)
         self.ids = torch.from_numpy(inp.expertIds).to(dev)
         self.wts = torch.from_numpy(inp.weights).to(dev) if w.useWeights else None
-        self.y = bits_to_dev(inp.y, dev) if inp.y is not None else None
-        self.recvX = torch.full((W, M, H), np.int16(np.uint16(SENT_X).view(np.int16)), dtype=torch.int16,
-                                device=dev).view(torch.bfloat16)
+        self.y = to_dev_bytes(inp.y, dev) if inp.y is not None else None
+        self.recvX = torch.full((W, M, rowB), SENT_X_BYTE, dtype=torch.uint8, device=dev)
         self.recvTokIdx = torch.full((W, M), SENT_I32, dtype=torch.int32, device=dev)
         self.recvExpertIds = torch.full((W, M, K), SENT_IDS, dtype=torch.int32, device=dev)
         self.recvWeights = torch.full((W, M, K), SENT_W, dtype=torch.float32, device=dev)
@@ -54,7 +69,7 @@ class GpuRun:
         self.sendMap = torch.full((T, K), SENT_MAP, dtype=torch.int32, device=dev)
         nb = epdc.epdc_dispatch_scratch_bytes(self.cfg)
         self.scratch = torch.zeros(max(nb, 4) // 4 + 1, dtype=torch.int32, device=dev)
-        self.out = torch.full((T, H), 0x7FC1, dtype=torch.int16, device=dev).view(torch.bfloat16)
+        self.out = torch.full((T, outB), SENT_OUT_BYTE, dtype=torch.uint8, device=dev)
 
     def scratch_clean(self) -> bool:
         """After a dispatch the scratch is all zero again (error flag included)."""
@@ -70,12 +85,12 @@ class GpuRun:
     def combine(self, y=None, weights="default", stream=None):
         w = self.w
         wts = self.wts if weights == "default" else weights
-        return epdc.epdc_combine(self.cfg, w.numTokens, self.y if y is None else y, self.ids,
+        return epdc.epdc_combine(self.ccfg, w.numTokens, self.y if y is None else y, self.ids,
                                  wts if w.useWeights else None, self.sendMap, self.out, stream=stream)
 
 
 def oracle_dispatch(w: workloads.Workload, inp: workloads.Inputs):
-    return oracle.dispatch(w.worldSize, w.hiddenDim, w.maxTokPerRank, w.numExpertPerRank,
+    return oracle.dispatch(w.worldSize, w.dispatchHidden, w.maxTokPerRank, w.numExpertPerRank,
                            w.numExpertPerToken, w.useWeights, inp.x, inp.expertIds,
                            inp.weights if w.useWeights else None, fill=FILL)
 
@@ -106,15 +121,24 @@ def assert_dispatch_equal(g: GpuRun, o, tag=""):
         assert np.array_equal(wt.view(np.uint32), o.recvWeights.view(np.uint32)), f"{tag} recvWeights differs"
     else:
         assert (wt == np.float32(SENT_W)).all(), f"{tag} recvWeights written with useWeights=0"
-    rx = dev_to_bits(g.recvX)
-    if not np.array_equal(rx, o.recvX):
-        bad = np.argwhere(rx != o.recvX)[0]
-        raise AssertionError(f"{tag} recvX differs first at {bad.tolist()}")
+    rx = g.recvX.cpu().numpy()
+    ox = o.recvX.view(np.uint8).reshape(rx.shape)
+    if not np.array_equal(rx, ox):
+        bad = np.argwhere(rx != ox)[0]
+        raise AssertionError(f"{tag} recvX differs first at byte {bad.tolist()}")
+
+
+def out_as(g: GpuRun) -> np.ndarray:
+    """The device out rows as the combine type (uint16 bf16 bits or float32)."""
+    dt = np.uint16 if g.w.combineDtype == "bf16" else np.float32
+    return g.out.cpu().numpy().view(dt)
 
 
 def assert_bits_equal(got: np.ndarray, exp: np.ndarray, tag=""):
-    if not np.array_equal(got, exp):
-        bad = np.argwhere(got != exp)
+    gb = got.view(np.uint16 if got.dtype == np.uint16 else np.uint32)
+    eb = exp.view(gb.dtype)
+    if not np.array_equal(gb, eb):
+        bad = np.argwhere(gb != eb)
         t, h = bad[0]
         raise AssertionError(f"{tag} {len(bad)} elements differ; first out[{t}][{h}] = "
-                             f"{hex(int(got[t, h]))} vs oracle {hex(int(exp[t, h]))}")
+                             f"{hex(int(gb[t, h]))} vs oracle {hex(int(eb[t, h]))}")

@@ -85,11 +85,14 @@ REJECT = [
     ("maxTokPerRank 0", dict(maxTokPerRank=0), 0, {}, -1),
     ("flat index overflow", dict(worldSize=64, maxTokPerRank=40_000_000), 8, {}, -1),
     ("negative tokens", {}, -1, {}, -1),
-    ("dtype fp8", dict(dtype=2), 8, {}, -2),
-    ("dtype fp32", dict(dtype=1), 8, {}, -2),
+    ("dtype 4", dict(dtype=4), 8, {}, -2),
+    ("dtype -1", dict(dtype=-1), 8, {}, -2),
     ("useWeights 2", dict(useWeights=2), 8, {}, -2),
     ("capacity", {}, 4097, {}, -3),
     ("row bytes not 16-aligned", dict(hiddenDim=7164), 8, {}, -4),
+    ("fp32 row of 24 bytes", dict(hiddenDim=6, dtype=1), 8, {}, -4),
+    ("fp8 row of 8 bytes", dict(hiddenDim=8, dtype=2), 8, {}, -4),
+    ("fp4x2 row of 7160 bytes", dict(hiddenDim=7160, dtype=3), 8, {}, -4),
     ("x misaligned", {}, 8, dict(x=P16 + 8), -4),
     ("recvX misaligned", {}, 8, dict(recvX=P16 + 4), -4),
     ("ids misaligned", {}, 8, dict(expertIds=P16 + 2), -4),
@@ -111,7 +114,10 @@ def test_dispatch_rejects(what, over, T, ptrs, code):
 
 COMBINE_REJECT = [
     ("worldSize 65", dict(worldSize=65), 8, {}, -1),
-    ("dtype fp8", dict(dtype=2), 8, {}, -2),
+    ("dtype fp8 cannot be summed", dict(dtype=2), 8, {}, -2),
+    ("dtype fp4x2 cannot be summed", dict(dtype=3), 8, {}, -2),
+    ("dtype 4", dict(dtype=4), 8, {}, -2),
+    ("fp32 row of 24 bytes", dict(hiddenDim=6, dtype=1), 8, {}, -4),
     ("capacity", {}, 4097, {}, -3),
     ("out misaligned", {}, 8, dict(out=P16 + 8), -4),
     ("y misaligned", {}, 8, dict(y=P16 + 2), -4),
@@ -136,6 +142,19 @@ def test_unweighted_accepts_null_weights_without_gpu():
     assert _dispatch(c, 8, weights=None, recvWeights=None) == -7
     assert _combine(c, 8, weights=None) == -7
     assert "dispatch" in epdc.epdc_last_error() or "combine" in epdc.epdc_last_error()
+
+
+def test_every_wire_dtype_passes_dispatch_checks_without_gpu():
+    """bf16, fp32, fp8 and fp4x2 rows pass every host check of dispatch (the
+    launch then reports EPDC_ERR_HIP on a host with no GPU); combine accepts
+    only bf16 and fp32."""
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("host without a GPU only")
+    for dt, h in ((0, 7168), (1, 7168), (2, 7168), (3, 3584), (2, 16), (1, 4)):
+        assert _dispatch(cfg(dtype=dt, hiddenDim=h), 8) == -7, (dt, h, epdc.epdc_last_error())
+    for dt in (0, 1):
+        assert _combine(cfg(dtype=dt), 8) == -7
 
 
 def test_zero_tokens_needs_only_recvcount_without_gpu():

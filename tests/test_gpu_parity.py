@@ -16,8 +16,7 @@ import torch
 
 import combine_count_amd as epdc
 import workloads
-from gpu_harness import (GpuRun, assert_bits_equal, assert_dispatch_equal, dev_to_bits, oracle_combine,
-                         oracle_dispatch)
+from gpu_harness import GpuRun, assert_bits_equal, assert_dispatch_equal, oracle_combine, oracle_dispatch, out_as
 
 pytestmark = pytest.mark.gpu
 
@@ -48,12 +47,13 @@ def _check_case(w: workloads.Workload, inp: workloads.Inputs, tag: str):
     g.combine()
     torch.cuda.synchronize()
     exp = oracle_combine(w, inp.y, inp, o.sendMap)
-    assert_bits_equal(dev_to_bits(g.out), exp, f"{tag} combine")
+    assert_bits_equal(out_as(g), exp, f"{tag} combine")
     # identity expert: the returned rows are the dispatched rows
-    g.combine(y=g.recvX)
-    torch.cuda.synchronize()
-    exp = oracle_combine(w, o.recvX, inp, o.sendMap)
-    assert_bits_equal(dev_to_bits(g.out), exp, f"{tag} identity combine")
+    if w.wire == w.combineDtype:
+        g.combine(y=g.recvX)
+        torch.cuda.synchronize()
+        exp = oracle_combine(w, o.recvX, inp, o.sendMap)
+        assert_bits_equal(out_as(g), exp, f"{tag} identity combine")
 
 
 @pytest.mark.parametrize("name,seed", CONFIG_SEEDS, ids=[f"{n}-s{s}" for n, s in CONFIG_SEEDS])
@@ -80,6 +80,10 @@ EDGE = [
     ("t9000_ragged", 8, 32, 9000, 9000, 8, 7168, "uniform", 1),
     ("two_tokens_per_wave_t40000", 8, 32, 40000, 40000, 8, 512, "uniform", 0),
     ("slab2_h1024", 8, 32, 700, 700, 8, 1024, "zipf", 0),
+    # rows that are not a whole number of 1 KiB chunks, one per tail-checked slab width
+    ("ragged_rows_1p5k", 4, 8, 300, 257, 5, 768, "uniform", 1),
+    ("ragged_rows_5p5k", 8, 16, 300, 300, 8, 2816, "zipf", 1),
+    ("ragged_rows_9p5k", 8, 16, 200, 130, 8, 4864, "uniform", 0),
 ]
 
 
@@ -88,6 +92,31 @@ def test_edge_parity(case):
     name, W, Epr, M, T, K, H, routing, useW = case
     w = workloads.Workload(name, W, Epr, M, T, K, H, routing, useW)
     _check_case(w, workloads.make_inputs(w, 5), name)
+
+
+DTYPES = [
+    # name, base workload, wire (dispatch row type), combine row type
+    ("fp8_wire_bf16_combine_h7168", "gen_zipf_h7168", "fp8", "bf16"),
+    ("fp4x2_wire_bf16_combine_h7168", "gen_zipf_h7168", "fp4x2", "bf16"),
+    ("fp32_both_pr_scale", "pr_scale", "fp32", "fp32"),
+    ("bf16_wire_fp32_combine_defaults", "epcfg_defaults", "bf16", "fp32"),
+    ("fp8_wire_fp32_combine_tiny", "tiny", "fp8", "fp32"),
+    ("fp4x2_wire_ragged", None, "fp4x2", "bf16"),
+    ("fp32_both_ragged", None, "fp32", "fp32"),
+    ("fp8_wire_large", "large_weighted", "fp8", "bf16"),
+]
+
+
+@pytest.mark.parametrize("case", DTYPES, ids=[d[0] for d in DTYPES])
+def test_dtype_parity(case):
+    """Dispatch of every wire type is a bitwise row copy; combine reduces bf16
+    or fp32 rows (a narrow-wire pair is two calls with two cfgs)."""
+    name, base, wire, comb = case
+    if base is None:  # ragged: rows that are not a whole number of 1 KiB chunks, non-pow2 W/Epr
+        w = workloads.Workload(name, 5, 3, 700, 650, 7, 1056, "uniform", 1, wire=wire, combineDtype=comb)
+    else:
+        w = workloads.CONFIGS[base].with_(name=name, wire=wire, combineDtype=comb)
+    _check_case(w, workloads.make_inputs(w, 4), name)
 
 
 def test_invalid_expert_ids():

@@ -39,10 +39,18 @@ class Workload:
     routing: str          # "uniform" or "zipf"
     useWeights: int
     zipf_s: float = 1.1
+    wire: str = "bf16"          # dispatch row type: bf16, fp32, fp8 or fp4x2
+    combineDtype: str = "bf16"  # combine row type: bf16 or fp32
 
     @property
     def numExperts(self) -> int:
         return self.worldSize * self.numExpertPerRank
+
+    @property
+    def dispatchHidden(self) -> int:
+        """hiddenDim of the dispatch call: fp4x2 packs two values per byte and
+        counts bytes (MORI JIT v2 design doc, §3.7)."""
+        return self.hiddenDim // 2 if self.wire == "fp4x2" else self.hiddenDim
 
     def with_(self, **kw) -> "Workload":
         return dataclasses.replace(self, **kw)
@@ -110,6 +118,31 @@ def softmax_weights(rng: np.random.Generator, w: Workload) -> np.ndarray:
     return (z / z.sum(axis=1, keepdims=True)).astype(np.float32)
 
 
+WIRE_BYTES = {"bf16": 2, "fp32": 4, "fp8": 1, "fp4x2": 1}
+EPDC_DTYPE = {"bf16": 0, "fp32": 1, "fp8": 2, "fp4x2": 3}
+
+# e2m1 magnitudes of the 3-bit codes 0..7 (bit 3 is the sign)
+_E2M1 = np.array([0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0])
+
+
+def rows_of(rng: np.random.Generator, shape, kind: str) -> np.ndarray:
+    """N(0,1) rows in one of the row types.  bf16 -> uint16 bits; fp32 ->
+    float32; fp8 -> uint8 e4m3 codes (torch's cast); fp4x2 -> uint8, two e2m1
+    codes per byte (nearest magnitude, low nibble first), shape[-1] halved."""
+    if kind == "bf16":
+        return bf16_normal_bits(rng, shape)
+    f = rng.standard_normal(shape, dtype=np.float32)
+    if kind == "fp32":
+        return f
+    if kind == "fp8":
+        return torch.from_numpy(f).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    if kind == "fp4x2":
+        mag = np.abs(f)[..., None]
+        code = np.argmin(np.abs(mag - _E2M1), axis=-1).astype(np.uint8) | (np.signbit(f).astype(np.uint8) << 3)
+        return (code[..., 0::2] | (code[..., 1::2] << 4)).astype(np.uint8)
+    raise ValueError(kind)
+
+
 def bf16_normal_bits(rng: np.random.Generator, shape) -> np.ndarray:
     """bf16 bit patterns (uint16) of N(0,1) samples.
 
@@ -123,22 +156,23 @@ def bf16_normal_bits(rng: np.random.Generator, shape) -> np.ndarray:
 class Inputs:
     w: Workload
     seed: int
-    x: np.ndarray          # uint16 [T][H]     bf16 bits of the token rows
+    x: np.ndarray          # [T][dispatchHidden] token rows of the wire type
     expertIds: np.ndarray  # int32  [T][K]
     weights: np.ndarray    # fp32   [T][K]
-    y: np.ndarray | None   # uint16 [W][M][H] bf16 bits of the returned rows
+    y: np.ndarray | None   # [W][M][H] returned rows of the combine type
 
 
 def make_inputs(w: Workload, seed: int, with_y: bool = True) -> Inputs:
     rng = np.random.Generator(np.random.PCG64(seed))
     ids = draw_expert_ids(rng, w)
     weights = softmax_weights(rng, w)
-    x = bf16_normal_bits(rng, (w.numTokens, w.hiddenDim))
+    x = rows_of(rng, (w.numTokens, w.hiddenDim), w.wire)
     y = None
     if with_y:
-        y = np.empty((w.worldSize, w.maxTokPerRank, w.hiddenDim), dtype=np.uint16)
+        ydt = np.uint16 if w.combineDtype == "bf16" else np.float32
+        y = np.empty((w.worldSize, w.maxTokPerRank, w.hiddenDim), dtype=ydt)
         for p in range(w.worldSize):
-            y[p] = bf16_normal_bits(rng, (w.maxTokPerRank, w.hiddenDim))
+            y[p] = rows_of(rng, (w.maxTokPerRank, w.hiddenDim), w.combineDtype)
     return Inputs(w, seed, x, ids, weights, y)
 
 
