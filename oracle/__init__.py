@@ -46,6 +46,10 @@ def load(path: str | None = None) -> ctypes.CDLL:
     lib.oracle_dispatch.argtypes = [i32] * 8 + [p] * 9
     lib.oracle_combine.restype = i32
     lib.oracle_combine.argtypes = [i32] * 8 + [p] * 5 + [i32, p, p]
+    lib.oracle_combine_push.restype = i32
+    lib.oracle_combine_push.argtypes = [i32] * 8 + [p] * 6
+    lib.oracle_combine_reduce.restype = i32
+    lib.oracle_combine_reduce.argtypes = [i32] * 8 + [p] * 5 + [i32, p, p]
     _lib_cache[path] = lib
     return lib
 
@@ -128,6 +132,65 @@ def combine(W, H, M, Epr, K, useWeights, y, expertIds, weights, sendMap, tokens=
                             _ptr(tok), n, _ptr(acc), _ptr(out))
     if rc != 0:
         raise ValueError(f"oracle_combine rejected its arguments ({rc})")
+    return out
+
+
+def landing_rows(W, K, T):
+    """Landing capacity of the scatter combine: one row per (token, PE), at
+    most min(W, K) PEs per token."""
+    return T * min(W, K)
+
+
+def combine_push(W, H, M, Epr, K, useWeights, T, y, recvExpertIds, recvWeights, recvCount, *,
+                 fill_byte=0xA5, scale_fill=-3.25, lib=None):
+    """Run the oracle push half of the scatter combine.  ``y``: [W][M][H]
+    bf16 bits (uint16) or float32.  Returns (landing [T*min(W,K)][H] of y's
+    dtype, landScale [T*min(W,K)] float32); rows not landed keep the fill."""
+    lib = lib or load()
+    fp32 = y.dtype == np.float32
+    y = np.ascontiguousarray(y, dtype=np.float32 if fp32 else np.uint16)
+    assert y.shape == (W, M, H)
+    cap = landing_rows(W, K, T)
+    landing = np.empty((cap, H), dtype=y.dtype)
+    landing.view(np.uint8)[...] = fill_byte
+    landScale = np.full((cap,), scale_fill, dtype=np.float32)
+    recvExpertIds = np.ascontiguousarray(recvExpertIds, dtype=np.int32)
+    recvCount = np.ascontiguousarray(recvCount, dtype=np.int32)
+    if useWeights:
+        recvWeights = np.ascontiguousarray(recvWeights, dtype=np.float32)
+    rc = lib.oracle_combine_push(W, H, M, Epr, K, int(useWeights), T, int(fp32), _ptr(y), _ptr(recvExpertIds),
+                                 _ptr(recvWeights) if useWeights else None, _ptr(recvCount),
+                                 _ptr(landing), _ptr(landScale))
+    if rc != 0:
+        raise ValueError(f"oracle_combine_push rejected its arguments ({rc})")
+    return landing, landScale
+
+
+def combine_reduce(W, H, M, Epr, K, useWeights, landing, landScale, recvCount, sendMap, tokens=None,
+                   lib=None):
+    """Run the oracle reduce half of the scatter combine over the landing rows
+    (bf16 bits or float32); returns rows of the same dtype, one per token (or
+    per entry of ``tokens``)."""
+    lib = lib or load()
+    T = sendMap.shape[0]
+    fp32 = landing.dtype == np.float32
+    landing = np.ascontiguousarray(landing, dtype=np.float32 if fp32 else np.uint16)
+    assert landing.shape == (landing_rows(W, K, T), H)
+    landScale = np.ascontiguousarray(landScale, dtype=np.float32)
+    recvCount = np.ascontiguousarray(recvCount, dtype=np.int32)
+    sendMap = np.ascontiguousarray(sendMap, dtype=np.int32)
+    tok = None
+    n = T
+    if tokens is not None:
+        tok = np.ascontiguousarray(np.asarray(tokens, dtype=np.int32))
+        n = tok.shape[0]
+    out = np.empty((n, H), dtype=landing.dtype)
+    acc = np.empty((H,), dtype=np.float32)
+    rc = lib.oracle_combine_reduce(W, H, M, Epr, K, int(useWeights), T, int(fp32), _ptr(landing),
+                                   _ptr(landScale), _ptr(recvCount), _ptr(sendMap), _ptr(tok), n,
+                                   _ptr(acc), _ptr(out))
+    if rc != 0:
+        raise ValueError(f"oracle_combine_reduce rejected its arguments ({rc})")
     return out
 
 

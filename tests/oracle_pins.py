@@ -21,7 +21,11 @@ What pins what:
   * combine vs an fp64 recomputation from the brute-force rows, within the
     fp32 summation error bound plus half a bf16 ulp;
   * two reading pins with exact answers: the per-PE fused multiply-add
-    (single rounding) and the first-appearance slot order of the PEs.
+    (single rounding) and the first-appearance slot order of the PEs;
+  * scatter (push) combine: the landing rows and forwarded scales written out
+    from the source side (brute-force rows) on random tiny inputs, routing
+    that fills the T*min(W, K) landing rows exactly, and push + reduce equal
+    to the gather combine bit for bit.
 """
 from __future__ import annotations
 
@@ -615,6 +619,141 @@ def check_reading_fma_fp32(lib, n=64, seed=31):
     return []
 
 
+# --------------------------------------------------------------------------
+# scatter (push) combine
+# --------------------------------------------------------------------------
+def _f32_slot_sum(ids, wts, t, p, Epr, E):
+    """Sum, in slot order from +0 and in fp32 arithmetic, of token t's weights
+    whose valid expert lives on PE p."""
+    s = np.float32(0.0)
+    for k in range(ids.shape[1]):
+        e = int(ids[t, k])
+        if 0 <= e < E and e // Epr == p:
+            s = np.float32(s + wts[t, k])
+    return s
+
+
+def _push_case(lib, W, Epr, K, T, M, H, fp32, useW, ids, wts, y, tag):
+    """Compare the oracle push with the landing layout written out from the
+    source side: for each token, each PE it reaches (brute-force rows), the
+    landing row is (rows of lower PEs) + (its row on that PE)."""
+    E = W * Epr
+    count, rowOf, firstSlot = brute_dispatch(W, Epr, K, M, ids)
+    # the metadata a dispatch delivers with each window row
+    rIds = np.full((W, M, K), -555, np.int32)
+    rWts = np.full((W, M, K), 9.75, np.float32)
+    for (t, p), r in rowOf.items():
+        rIds[p, r] = ids[t]
+        rWts[p, r] = wts[t]
+    cnt = np.array(count, np.int32)
+    fill, sfill = 0xA5, np.float32(-3.25)
+    landing, scale = oracle.combine_push(W, H, M, Epr, K, useW, T, y, rIds, rWts if useW else None, cnt,
+                                         fill_byte=fill, scale_fill=float(sfill), lib=lib)
+    U = int(cnt.sum())
+    fails = []
+    seen = set()
+    for (t, p), r in rowOf.items():
+        L = int(cnt[:p].sum()) + r
+        seen.add(L)
+        if not np.array_equal(landing[L].view(np.uint8), y[p, r].view(np.uint8)):
+            fails.append(f"{tag}: landing[{L}] is not y[{p}][{r}] (token {t})")
+        if useW:
+            want = _f32_slot_sum(ids, wts, t, p, Epr, E)
+            if scale[L].view(np.uint32) != want.view(np.uint32):
+                fails.append(f"{tag}: landScale[{L}] = {scale[L]!r} != {want!r} (token {t}, PE {p})")
+        if fails:
+            return fails
+    if seen != set(range(U)):
+        fails.append(f"{tag}: landed rows {sorted(seen)} are not 0..{U - 1}")
+    if not (landing[U:].view(np.uint8) == fill).all():
+        fails.append(f"{tag}: landing rows past U={U} were written")
+    untouched = scale if not useW else scale[U:]
+    if not (untouched.view(np.uint32) == sfill.view(np.uint32)).all():
+        fails.append(f"{tag}: landScale written past U or without useWeights")
+    return fails
+
+
+def check_push_landing_brute(lib):
+    """Landing rows and forwarded scales of the push half on random small
+    shapes (invalid ids, W and K not powers of two, K above and below W),
+    bf16 and fp32 rows, both useWeights."""
+    fails = []
+    rng = np.random.Generator(np.random.PCG64(41))
+    for i in range(48):
+        W = int(rng.integers(1, 9))
+        Epr = int(rng.integers(1, 4))
+        E = W * Epr
+        K = int(rng.integers(1, min(E, 9) + 1))
+        T = int(rng.integers(0, 30))
+        M = T + int(rng.integers(0, 3)) + (1 if T == 0 else 0)
+        H = 8 * int(rng.integers(1, 3))
+        ids = rng.integers(-1, E + 1, size=(T, K)).astype(np.int32)
+        wts = rng.standard_normal((T, K)).astype(np.float32)
+        fp32 = i % 2
+        y = (rng.standard_normal((W, M, H)).astype(np.float32) if fp32
+             else rng.integers(0, 1 << 16, size=(W, M, H), dtype=np.uint16))
+        fails += _push_case(lib, W, Epr, K, T, M, H, fp32, (i // 2) % 2, ids, wts, y,
+                            f"push rand{i} W{W} Epr{Epr} K{K} T{T}")
+        if fails:
+            break
+    return fails
+
+
+def check_push_capacity(lib):
+    """Routing where every token reaches min(W, K) PEs fills the landing
+    buffer of T*min(W, K) rows exactly (K = W, K > W, K < W)."""
+    fails = []
+    rng = np.random.Generator(np.random.PCG64(43))
+    for W, Epr, K, T in [(4, 1, 4, 5), (3, 2, 6, 4), (8, 1, 2, 6), (1, 3, 3, 3)]:
+        E = W * Epr
+        M = T
+        ids = np.stack([rng.permutation(E)[:K] for _ in range(T)]).astype(np.int32)
+        if K >= W:  # make sure every PE is hit: put one expert of each PE first
+            for t in range(T):
+                ids[t, :W] = np.arange(W) * Epr + rng.integers(0, Epr, W)
+                rest = [e for e in rng.permutation(E) if e not in ids[t, :W]]
+                ids[t, W:] = rest[:K - W]
+        else:  # K distinct PEs
+            for t in range(T):
+                ids[t] = rng.permutation(W)[:K] * Epr
+        wts = rng.standard_normal((T, K)).astype(np.float32)
+        y = rng.integers(0, 1 << 16, size=(W, M, 8), dtype=np.uint16)
+        count, _, _ = brute_dispatch(W, Epr, K, M, ids)
+        if sum(count) != T * min(W, K):
+            fails.append(f"capacity case W{W} K{K}: U = {sum(count)} != T*min(W,K) (test construction)")
+            continue
+        fails += _push_case(lib, W, Epr, K, T, M, 8, 0, 1, ids, wts, y, f"capacity W{W} Epr{Epr} K{K} T{T}")
+    return fails
+
+
+def check_push_reduce_matches_gather(lib, names=("tiny", "pr_scale", "epcfg_defaults", "gen_zipf_h2048"),
+                                     seed=5, h_cap=256):
+    """Push then reduce gives the gather combine's bits (the gather is pinned
+    on its own above), for bf16 and fp32 rows and both useWeights."""
+    fails = []
+    for name in names:
+        w0 = workloads.CONFIGS[name]
+        H = min(w0.hiddenDim, h_cap)
+        for useW in (1, 0):
+            for fp32 in (0, 1):
+                w = w0.with_(hiddenDim=H, useWeights=useW)
+                inp = workloads.make_inputs(w, seed, with_y=False)
+                rng = np.random.Generator(np.random.PCG64(seed + 100))
+                y = workloads.rows_of(rng, (w.worldSize, w.maxTokPerRank, H), "fp32" if fp32 else "bf16")
+                W, M, Epr, K, T = w.worldSize, w.maxTokPerRank, w.numExpertPerRank, w.numExpertPerToken, w.numTokens
+                wts = inp.weights if useW else None
+                o = oracle.dispatch(W, H, M, Epr, K, useW, inp.x[:, :H].copy(), inp.expertIds, wts, lib=lib)
+                g = oracle.combine(W, H, M, Epr, K, useW, y, inp.expertIds, wts, o.sendMap, lib=lib)
+                land, sc = oracle.combine_push(W, H, M, Epr, K, useW, T, y, o.recvExpertIds,
+                                               o.recvWeights if useW else None, o.recvCount, lib=lib)
+                r = oracle.combine_reduce(W, H, M, Epr, K, useW, land, sc, o.recvCount, o.sendMap, lib=lib)
+                if not np.array_equal(r.view(np.uint8), g.view(np.uint8)):
+                    bad = int(np.argmax((r.view(np.uint8) != g.view(np.uint8)).reshape(T, -1).any(axis=1)))
+                    fails.append(f"{name} useWeights={useW} fp32={fp32}: push+reduce differs from the gather "
+                                 f"combine (first at token {bad})")
+    return fails
+
+
 ALL_CHECKS = [
     check_worked_example,
     check_brute_force_exhaustive,
@@ -628,4 +767,7 @@ ALL_CHECKS = [
     check_reading_fma_and_order,
     check_combine_fp32,
     check_reading_fma_fp32,
+    check_push_landing_brute,
+    check_push_capacity,
+    check_push_reduce_matches_gather,
 ]

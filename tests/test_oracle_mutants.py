@@ -67,10 +67,34 @@ MUTANTS = [
      "acc[h] = fmaf(s, bf16_to_f32(src[h]), acc[h]);",
      "acc[h] = s * bf16_to_f32(src[h]) + acc[h];"),
     ("combine: PEs in reverse slot order",
-     "for (int32_t k0 = 0; k0 < K; ++k0) {",
-     "for (int32_t k0 = K - 1; k0 >= 0; --k0) {"),
+     "    for (int32_t k0 = 0; k0 < K; ++k0) {\n        int32_t flat",
+     "    for (int32_t k0 = K - 1; k0 >= 0; --k0) {\n        int32_t flat"),
     ("combine: accumulator not cleared per token",
      "for (int32_t h = 0; h < H; ++h) acc[h] = 0.0f;",
+     ";"),
+    ("push: rows of a window land in reverse order",
+     "const int64_t L = landOff + r;",
+     "const int64_t L = landOff + (n - 1 - r);"),
+    ("push: landing offset not advanced past a window",
+     "landOff += n;",
+     "landOff += 0 * n;"),
+    ("push: scale over every valid slot, not only the PE's",
+     "if (dest_pe(recvExpertIds[src * K + k], W, Epr) == p)",
+     "if (dest_pe(recvExpertIds[src * K + k], W, Epr) >= 0)"),
+    ("push: scale from the first slot on the PE only",
+     "s = s + recvWeights[src * K + k];",
+     "{ s = s + recvWeights[src * K + k]; break; }"),
+    ("reduce: forwarded scale ignored",
+     "float s = useWeights ? landScale[L] : 1.0f;",
+     "float s = useWeights ? 1.0f : 1.0f;"),
+    ("reduce: slots in reverse order",
+     "        for (int32_t k0 = 0; k0 < K; ++k0) {\n            int32_t flat",
+     "        for (int32_t k0 = K - 1; k0 >= 0; --k0) {\n            int32_t flat"),
+    ("reduce: landing row from the window row only",
+     "int64_t L = landOff[p] + r;",
+     "int64_t L = r;"),
+    ("reduce: accumulator not cleared per token",
+     "memset(acc, 0, (size_t)H * sizeof(float)); /* +0.0f */",
      ";"),
     ("bf16 rounding by truncation",
      "u += 0x7fffu + lsb;",
@@ -86,8 +110,11 @@ ORDER = [
     pins.check_reading_fma_fp32,
     pins.check_combine_fp32,
     pins.check_brute_force_random,
+    pins.check_push_landing_brute,
+    pins.check_push_capacity,
     pins.check_reading_fma_and_order,
     pins.check_combine_identity_cases,
+    pins.check_push_reduce_matches_gather,
     pins.check_combine_fp64_bound,
     pins.check_brute_force_exhaustive,
     pins.check_invariants,
