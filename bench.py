@@ -9,9 +9,9 @@ Zipf(1.1) expert popularity, softmax weights).
 
 Prints one JSON line: whole-job HBM throughput from the algorithmic bytes of
 a step and the time per step (events around the timed loop only), a roofline
-entry for the dominant kernel (HIP events around each launch, in a second
-pass over the same steps) and the CPU oracle timed on a bounded sample of the
-same workload.
+entry for the dominant kernel (each kernel then timed alone over the same
+number of back-to-back launches, HIP events on the launch stream) and the CPU
+oracle timed on a bounded sample of the same workload.
 """
 from __future__ import annotations
 
@@ -30,7 +30,7 @@ METRIC = "dispatch+combine µs and achieved HBM GB/s (% of peak), 1×MI355X"
 HBM_PEAK_GBPS = 8000.0
 PROFILES = os.path.join(ROOT, "profiles")
 KERNEL_SOURCES = [os.path.join(ROOT, "combine_count_amd", "csrc", f)
-                  for f in ("dispatch.hip", "combine.hip", "epdc_internal.h")]
+                  for f in ("dispatch.hip", "combine.hip", "combine_push.hip", "epdc_internal.h")]
 
 
 def parse_args():
@@ -43,6 +43,8 @@ def parse_args():
     ap.add_argument("--wire", default="bf16", choices=["bf16", "fp32", "fp8", "fp4x2"],
                     help="dispatch row type (fp8/fp4x2: narrow wire, hiddenDim in bytes for fp4x2)")
     ap.add_argument("--combine-dtype", default="bf16", choices=["bf16", "fp32"])
+    ap.add_argument("--combine", default="gather", choices=["gather", "push"],
+                    help="gather combine (one kernel) or scatter combine (push + reduce kernels)")
     ap.add_argument("--rotate", type=int, default=3,
                     help="independent buffer sets (inputs and outputs) cycled step by step, so that a "
                          "step never finds its data in the 256 MB Infinity Cache (1 = hot)")
@@ -67,6 +69,20 @@ def algorithmic_bytes(w, U):
             + T * K * 4 + W * 4)                               # sendMap, recvCount
     comb = T * K * 4 + wt * (T * K * 4 + T * K * 4) + U * yr + T * yr
     return disp, comb
+
+
+def push_bytes(w, U):
+    """Algorithmic bytes of the scatter combine's two kernels.  Push: each
+    landed row read and written once, with (weighted) its K ids and weights
+    read and one scale written; the W counts.  Reduce: the token's sendMap,
+    the counts, each landed row and scale read once, the out row written."""
+    import workloads
+    T, K, W = w.numTokens, w.numExpertPerToken, w.worldSize
+    yr = w.hiddenDim * workloads.WIRE_BYTES[w.combineDtype]
+    wt = 1 if w.useWeights else 0
+    push = 2 * U * yr + wt * (U * K * 8 + U * 4) + W * 4
+    red = T * K * 4 + W * 4 + U * yr + wt * U * 4 + T * yr
+    return push, red
 
 
 def kernel_source_hash():
@@ -97,10 +113,10 @@ def read_traffic(kernel, workload):
         return None
 
 
-def cpu_baseline(w, inp, budget_s, disp_b, comb_b):
+def cpu_baseline(w, inp, budget_s, step_bytes, push):
     import oracle
     step, _ = oracle.timed_step(w.worldSize, w.maxTokPerRank, w.numExpertPerRank, w.numExpertPerToken,
-                                w.useWeights, inp.x, inp.expertIds, inp.weights, inp.y)
+                                w.useWeights, inp.x, inp.expertIds, inp.weights, inp.y, push=push)
     step()  # untimed: page in the buffers
     n, t0 = 0, time.perf_counter()
     while True:
@@ -109,9 +125,10 @@ def cpu_baseline(w, inp, budget_s, disp_b, comb_b):
         el = time.perf_counter() - t0
         if el >= budget_s or n >= 1000:
             break
-    return {"value": round((disp_b + comb_b) * n / el / 1e9, 3), "unit": "GB/s", "cores": 1,
+    what = "dispatch+push+reduce" if push else "dispatch+combine"
+    return {"value": round(step_bytes * n / el / 1e9, 3), "unit": "GB/s", "cores": 1,
             "kind": "oracle",
-            "sample": f"{n} full dispatch+combine steps of {w.name} (seed {inp.seed}), single-threaded C "
+            "sample": f"{n} full {what} steps of {w.name} (seed {inp.seed}), single-threaded C "
                       f"oracle, {el:.1f} s wall",
             "ms_per_step": round(el / n * 1e3, 2)}
 
@@ -149,21 +166,37 @@ def main():
     if (args.wire, args.combine_dtype) != ("bf16", "bf16"):
         w = w.with_(name=f"{w.name}_{args.wire}_{args.combine_dtype}", wire=args.wire,
                     combineDtype=args.combine_dtype)
+    if args.combine == "push":
+        w = w.with_(name=f"{w.name}_push")
     print(f"[bench] generating {w.name} seed {args.seed}", file=sys.stderr, flush=True)
     inp = workloads.make_inputs(w, args.seed)
     sets = [GpuRun(w, inp) for _ in range(max(1, args.rotate))]
+    push = args.combine == "push"
+    if push:
+        for s in sets:
+            s.alloc_landing()
     g = sets[0]
     g.dispatch()
-    g.combine()
     torch.cuda.synchronize()
     U = int(g.recvCount.sum().item())
     disp_b, comb_b = algorithmic_bytes(w, U)
-    stream = torch.cuda.current_stream()
+    # The kernels of one step, in order: (name, launch on a buffer set, algorithmic bytes per launch).
+    if push:
+        push_b, red_b = push_bytes(w, U)
+        stages = [("dispatch", lambda s: s.dispatch(), disp_b), ("push", lambda s: s.push(), push_b),
+                  ("reduce", lambda s: s.reduce(), red_b)]
+    else:
+        stages = [("dispatch", lambda s: s.dispatch(), disp_b), ("combine", lambda s: s.combine(), comb_b)]
+    step_b = sum(b for _, _, b in stages)
 
+    def step(s):
+        for _, run, _ in stages:
+            run(s)
+
+    stream = torch.cuda.current_stream()
     print(f"[bench] warmup {args.warmup}", file=sys.stderr, flush=True)
     for i in range(args.warmup):
-        sets[i % len(sets)].dispatch()
-        sets[i % len(sets)].combine()
+        step(sets[i % len(sets)])
     torch.cuda.synchronize()
 
     # Timed region: exactly `steps` steps between two events, nothing else on
@@ -173,36 +206,55 @@ def main():
     torch.cuda.synchronize()
     t_start.record(stream)
     for i in range(args.steps):
-        s = sets[i % len(sets)]
-        s.dispatch()
-        s.combine()
+        step(sets[i % len(sets)])
     t_end.record(stream)
     torch.cuda.synchronize()
     ms_step = t_start.elapsed_time(t_end) / args.steps
 
-    # Per-kernel durations: the same steps again, with HIP events around each
-    # launch on the launch stream.
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    # Per-kernel durations: each kernel alone, `steps` launches back to back
+    # over the same rotating buffer sets, between two HIP events on the launch
+    # stream (an event pair around every launch adds ~2 us to each reading).
+    def per_launch_ms(run):
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        a.record(stream)
+        for i in range(args.steps):
+            run(sets[i % len(sets)])
+        b.record(stream)
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / args.steps
+
+    kern_ms = {name: per_launch_ms(run) for name, run, _ in stages}
+
+    # Launch latency: the same `steps` steps captured once into a HIP graph
+    # and replayed, which takes the per-launch host cost (Python, ctypes, the
+    # HIP launch call) out of the step; at a few tokens that cost is the step.
+    graph = torch.cuda.CUDAGraph()
+    cap = torch.cuda.Stream()
+    cap.wait_stream(stream)
+    with torch.cuda.stream(cap):
+        with torch.cuda.graph(graph, stream=cap):
+            for i in range(args.steps):
+                step(sets[i % len(sets)])
+    stream.wait_stream(cap)
+    graph.replay()
     torch.cuda.synchronize()
-    for i in range(args.steps):
-        s = sets[i % len(sets)]
-        ev[i][0].record(stream)
-        s.dispatch()
-        ev[i][1].record(stream)
-        s.combine()
-        ev[i][2].record(stream)
+    g0, g1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    g0.record(stream)
+    graph.replay()
+    g1.record(stream)
     torch.cuda.synchronize()
-    d_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in ev]))
-    c_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in ev]))
+    graph_ms = g0.elapsed_time(g1) / args.steps
+    del graph
     scratch_ok = all(s.scratch_clean() for s in sets)
-    print(f"[bench] U={U} dispatch {d_ms * 1e3:.1f} us ({disp_b / d_ms / 1e6:.0f} GB/s), combine "
-          f"{c_ms * 1e3:.1f} us ({comb_b / c_ms / 1e6:.0f} GB/s), step {ms_step * 1e3:.1f} us",
+    print(f"[bench] U={U} " + ", ".join(f"{n} {kern_ms[n] * 1e3:.1f} us ({b / kern_ms[n] / 1e6:.0f} GB/s)"
+                                        for n, _, b in stages)
+          + f", step {ms_step * 1e3:.1f} us, graph-replayed step {graph_ms * 1e3:.1f} us",
           file=sys.stderr, flush=True)
 
-    if d_ms >= c_ms:
-        dom, dom_b, dom_ms = "dispatch", disp_b, d_ms
-    else:
-        dom, dom_b, dom_ms = "combine", comb_b, c_ms
+    dom, _, dom_b = max(stages, key=lambda st: kern_ms[st[0]])
+    dom_ms = kern_ms[dom]
     achieved = dom_b / dom_ms / 1e6
     roofline = {"bound": "hbm", "kernel": dom, "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS,
                 "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
@@ -212,25 +264,28 @@ def main():
     cpu = None
     if args.cpu_seconds > 0:
         print("[bench] timing the CPU oracle", file=sys.stderr, flush=True)
-        cpu = cpu_baseline(w, inp, args.cpu_seconds, disp_b, comb_b)
+        cpu = cpu_baseline(w, inp, args.cpu_seconds, step_b, push)
 
-    value = (disp_b + comb_b) / (ms_step * 1e-3) / 1e9
+    value = step_b / (ms_step * 1e-3) / 1e9
+    config = {"workload": w.name, "worldSize": w.worldSize, "numExpertPerRank": w.numExpertPerRank,
+              "numTokens": w.numTokens, "maxTokPerRank": w.maxTokPerRank,
+              "numExpertPerToken": w.numExpertPerToken, "hiddenDim": w.hiddenDim,
+              "routing": w.routing + ("(s=1.1)" if w.routing == "zipf" else ""),
+              "useWeights": w.useWeights, "seed": args.seed, "unique_token_pe_pairs": U,
+              "dispatch_dtype": w.wire, "combine_dtype": w.combineDtype,
+              "combine": "scatter (push + reduce)" if push else "gather",
+              "bytes_per_step": step_b}
+    config.update({f"{n}_us": round(kern_ms[n] * 1e3, 2) for n, _, _ in stages})
+    config.update({"graph_replay_step_us": round(graph_ms * 1e3, 2),
+                   "buffer_sets_rotated": len(sets), "scratch_clean": scratch_ok,
+                   "frac_of_hbm_peak": round(value / HBM_PEAK_GBPS, 4)})
     line = {
         "metric": METRIC, "value": round(value, 1), "unit": "GB/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 5),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": w.wire if w.wire == w.combineDtype else f"{w.wire}+{w.combineDtype}",
         "data": "synthetic",
-        "config": {"workload": w.name, "worldSize": w.worldSize, "numExpertPerRank": w.numExpertPerRank,
-                   "numTokens": w.numTokens, "maxTokPerRank": w.maxTokPerRank,
-                   "numExpertPerToken": w.numExpertPerToken, "hiddenDim": w.hiddenDim,
-                   "routing": w.routing + ("(s=1.1)" if w.routing == "zipf" else ""),
-                   "useWeights": w.useWeights, "seed": args.seed, "unique_token_pe_pairs": U,
-                   "dispatch_dtype": w.wire, "combine_dtype": w.combineDtype,
-                   "bytes_per_step": disp_b + comb_b,
-                   "dispatch_us": round(d_ms * 1e3, 2), "combine_us": round(c_ms * 1e3, 2),
-                   "buffer_sets_rotated": len(sets), "scratch_clean": scratch_ok,
-                   "frac_of_hbm_peak": round(value / HBM_PEAK_GBPS, 4)},
+        "config": config,
         "roofline": roofline,
         "cpu_baseline": cpu,
     }

@@ -13,7 +13,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libepdc.so")
-SOURCES = ["epdc_api.cpp", "dispatch.hip", "combine.hip"]
+SOURCES = ["epdc_api.cpp", "dispatch.hip", "combine.hip", "combine_push.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 COMMON = [

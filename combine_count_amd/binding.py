@@ -24,7 +24,8 @@ ERRORS = {
     -6: "EPDC_ERR_SCRATCH",
     -7: "EPDC_ERR_HIP",
 }
-EXPORTS = ("epdc_dispatch_scratch_bytes", "epdc_dispatch", "epdc_combine", "epdc_last_error")
+EXPORTS = ("epdc_dispatch_scratch_bytes", "epdc_dispatch", "epdc_combine", "epdc_landing_rows",
+           "epdc_combine_push", "epdc_combine_reduce", "epdc_last_error")
 
 
 class EpdcError(RuntimeError):
@@ -68,6 +69,12 @@ def load_library() -> ctypes.CDLL:
     lib.epdc_dispatch.argtypes = [cfgp, i32] + [p] * 10 + [sz, p]
     lib.epdc_combine.restype = ctypes.c_int
     lib.epdc_combine.argtypes = [cfgp, i32] + [p] * 5 + [p]
+    lib.epdc_landing_rows.restype = i32
+    lib.epdc_landing_rows.argtypes = [cfgp, i32]
+    lib.epdc_combine_push.restype = ctypes.c_int
+    lib.epdc_combine_push.argtypes = [cfgp, i32] + [p] * 6 + [p]
+    lib.epdc_combine_reduce.restype = ctypes.c_int
+    lib.epdc_combine_reduce.argtypes = [cfgp, i32] + [p] * 5 + [p]
     lib.epdc_last_error.restype = ctypes.c_char_p
     lib.epdc_last_error.argtypes = []
     _lib = lib
@@ -121,5 +128,25 @@ def epdc_combine(cfg: EpCfg, numTokens: int, y, expertIds, weights, sendMap, out
                  check: bool = True) -> int:
     rc = load_library().epdc_combine(
         ctypes.byref(cfg), int(numTokens), _ptr(y), _ptr(expertIds), _ptr(weights), _ptr(sendMap),
+        _ptr(out), _stream(stream))
+    return _check(rc, check)
+
+
+def epdc_landing_rows(cfg: EpCfg, numTokens: int) -> int:
+    return load_library().epdc_landing_rows(ctypes.byref(cfg), int(numTokens))
+
+
+def epdc_combine_push(cfg: EpCfg, numTokens: int, y, recvExpertIds, recvWeights, recvCount, landing, landScale,
+                      stream=None, check: bool = True) -> int:
+    rc = load_library().epdc_combine_push(
+        ctypes.byref(cfg), int(numTokens), _ptr(y), _ptr(recvExpertIds), _ptr(recvWeights), _ptr(recvCount),
+        _ptr(landing), _ptr(landScale), _stream(stream))
+    return _check(rc, check)
+
+
+def epdc_combine_reduce(cfg: EpCfg, numTokens: int, landing, landScale, recvCount, sendMap, out, stream=None,
+                        check: bool = True) -> int:
+    rc = load_library().epdc_combine_reduce(
+        ctypes.byref(cfg), int(numTokens), _ptr(landing), _ptr(landScale), _ptr(recvCount), _ptr(sendMap),
         _ptr(out), _stream(stream))
     return _check(rc, check)

@@ -14,10 +14,13 @@
 //     token's PEs in first-appearance order;
 //   * lane k0 of a kept slot sums, in slot order from +0, the weights of the
 //     slots on its PE (read from the other lanes by shuffles);
-//   * the PE loop walks the kept slots in ascending order, the next PE's
-//     rows loaded while the current one is reduced (two register buffers);
-//     every lane owns 16 contiguous bytes per chunk (8 bf16 or 4 fp32
-//     elements), one 16-byte access.
+//   * the PE loop walks the kept slots in ascending order, a group of up to
+//     EPDC_COMBINE_GROUP rows at a time: all of a group's row loads are issued
+//     before its first FMA; every lane owns 16 contiguous bytes per chunk
+//     (8 bf16 or 4 fp32 elements), one 16-byte access.
+// The same kernel (LAND = true) is the reduce half of the scatter combine:
+// the rows come from the packed landing rows the push wrote and each row's
+// scale from the push's forwarded scales (combine_push.hip).
 #include "epdc_internal.h"
 
 namespace epdc {
@@ -55,7 +58,9 @@ __device__ __forceinline__ void load_slab(u32x4 (&v)[CPW], const uint8_t *row, i
     for (int c = 0; c < CPW; ++c) {
         const int gc = slab * CPW + c;
         const int e = gc * kChunkBytes + lane * 16;
-        if (FULL || (gc < nChunks && e < rowBytes)) v[c] = load16<EPDC_COMBINE_NT_LOAD>(row + e);
+        // A lane past the row's end loads the row's first 16 bytes (in
+        // bounds; its sums are never stored): no branch or wait per load.
+        v[c] = load16<EPDC_COMBINE_NT_LOAD>(row + ((FULL || (gc < nChunks && e < rowBytes)) ? e : 0));
     }
 }
 
@@ -88,7 +93,11 @@ __device__ __forceinline__ void gather_reduce(float (&acc)[CPW][8], const Combin
         for (int c = 0; c < CPW; ++c) fma_chunk<FP32>(acc[c], sc[j], v[j][c]);
 }
 
-template <int CPW, bool FULL, bool FP32>
+// LAND = false: the gather combine over the returned rows y[W][M].
+// LAND = true: the reduce half of the scatter combine over the landing rows
+// (combine_push.hip), with the scale each landed row carries; same order,
+// same arithmetic, so the same bits.
+template <int CPW, bool FULL, bool FP32, bool LAND>
 __global__ __launch_bounds__(256) void combine_kernel(CombineParams P, int nSlabs) {
     const int lane = threadIdx.x & 63;
     const int item = blockIdx.x * 4 + (threadIdx.x >> 6);
@@ -96,30 +105,55 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineParams P, int nSlab
     const int slab = item - t * nSlabs;
     if (t >= P.T) return;  // whole wave
 
-    // Per-token metadata, one slot per lane.
-    const int32_t E = P.W * P.Epr;
-    int32_t flat = -1, pe = -1;
-    float w = 0.0f;
-    if (lane < P.K) {
-        const int64_t o = (int64_t)t * P.K + lane;
-        flat = P.sendMap[o];
-        const int32_t e = P.expertIds[o];
-        if (e >= 0 && e < E) pe = P.eprShift >= 0 ? (e >> P.eprShift) : (e / P.Epr);
-        if (P.useWeights) w = P.weights[o];
-    }
-    // Kept slots; an entry outside [0, W*M) (not written by a dispatch of
-    // this cfg) counts as dropped rather than being read out of bounds.
-    const uint64_t kept = __ballot(lane < P.K && flat >= 0 && flat < P.W * P.M);
-
-    // Scale of each kept slot's PE: sum of the token's weights on that PE,
-    // in slot order starting from +0.
+    // Per-token metadata, one slot per lane; `flat` becomes the row index
+    // into P.y of each kept slot and `s` its PE's scale.
+    int32_t flat = -1;
+    uint64_t kept;
     float s = 1.0f;
-    if (P.useWeights) {
-        s = 0.0f;
-        for (int k = 0; k < P.K; ++k) {
-            const int32_t pk = __shfl(pe, k);
-            const float wk = __shfl(w, k);
-            if (k >= lane && pe >= 0 && pk == pe) s = s + wk;
+    if constexpr (LAND) {
+        // Landing offsets: exclusive prefix sums of the counts (each clamped
+        // to [0, M]) in PE order; rows at or past the landed total (or the
+        // landing capacity) were never written and count as dropped.
+        int32_t c = 0;
+        if (lane < P.W) {
+            c = P.recvCount[lane];
+            c = c < 0 ? 0 : (c > P.M ? P.M : c);
+        }
+        const int32_t incl = wave_incl_scan(c);
+        const int32_t landed = min(uniform(__shfl(incl, 63)), P.landRows);
+        int32_t f = -1;
+        if (lane < P.K) f = P.sendMap[(int64_t)t * P.K + lane];
+        bool ok = lane < P.K && f >= 0 && f < P.W * P.M;
+        const int32_t p = ok ? f / P.M : 0;
+        const int32_t L = __shfl(incl - c, p) + (f - p * P.M);
+        ok = ok && L < landed;
+        kept = __ballot(ok);
+        flat = L;
+        if (P.useWeights && ok) s = P.landScale[L];
+    } else {
+        const int32_t E = P.W * P.Epr;
+        int32_t pe = -1;
+        float w = 0.0f;
+        if (lane < P.K) {
+            const int64_t o = (int64_t)t * P.K + lane;
+            flat = P.sendMap[o];
+            const int32_t e = P.expertIds[o];
+            if (e >= 0 && e < E) pe = P.eprShift >= 0 ? (e >> P.eprShift) : (e / P.Epr);
+            if (P.useWeights) w = P.weights[o];
+        }
+        // Kept slots; an entry outside [0, W*M) (not written by a dispatch
+        // of this cfg) counts as dropped rather than being read out of bounds.
+        kept = __ballot(lane < P.K && flat >= 0 && flat < P.W * P.M);
+
+        // Scale of each kept slot's PE: sum of the token's weights on that
+        // PE, in slot order starting from +0.
+        if (P.useWeights) {
+            s = 0.0f;
+            for (int k = 0; k < P.K; ++k) {
+                const int32_t pk = __shfl(pe, k);
+                const float wk = __shfl(w, k);
+                if (k >= lane && pe >= 0 && pk == pe) s = s + wk;
+            }
         }
     }
 
@@ -183,35 +217,36 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineParams P, int nSlab
     }
 }
 
-template <int CPW, bool FP32>
+template <int CPW, bool FP32, bool LAND>
 hipError_t launch(const CombineParams &P, hipStream_t stream) {
     const int nSlabs = ceil_div(P.nChunks, CPW);
     const int64_t waves = (int64_t)P.T * nSlabs;
+    if (waves > INT32_MAX - 3) return hipErrorInvalidConfiguration;
+    const dim3 grid((uint32_t)ceil_div(waves, 4));
     const bool full = (P.rowBytes % kChunkBytes == 0) && (P.nChunks % CPW == 0);
     if (full)
-        hipLaunchKernelGGL((combine_kernel<CPW, true, FP32>), dim3(ceil_div(waves, 4)), dim3(256), 0, stream, P,
-                           nSlabs);
+        hipLaunchKernelGGL((combine_kernel<CPW, true, FP32, LAND>), grid, dim3(256), 0, stream, P, nSlabs);
     else
-        hipLaunchKernelGGL((combine_kernel<CPW, false, FP32>), dim3(ceil_div(waves, 4)), dim3(256), 0, stream, P,
-                           nSlabs);
+        hipLaunchKernelGGL((combine_kernel<CPW, false, FP32, LAND>), grid, dim3(256), 0, stream, P, nSlabs);
     return hipGetLastError();
 }
 
-template <bool FP32>
+template <bool FP32, bool LAND>
 hipError_t launch_dtype(const CombineParams &P, hipStream_t stream) {
 #if EPDC_COMBINE_CPW == 0
-    if (P.nChunks % 2 == 0 && (int64_t)P.T * (P.nChunks / 2) >= 8192) return launch<2, FP32>(P, stream);
-    return launch<1, FP32>(P, stream);
+    if (P.nChunks % 2 == 0 && (int64_t)P.T * (P.nChunks / 2) >= 8192) return launch<2, FP32, LAND>(P, stream);
+    return launch<1, FP32, LAND>(P, stream);
 #else
-    return launch<EPDC_COMBINE_CPW, FP32>(P, stream);
+    return launch<EPDC_COMBINE_CPW, FP32, LAND>(P, stream);
 #endif
 }
 
 }  // namespace
 
-hipError_t launch_combine(const CombineParams &P, bool fp32, hipStream_t stream) {
+hipError_t launch_combine(const CombineParams &P, bool fp32, bool landing, hipStream_t stream) {
     if (P.T == 0) return hipSuccess;
-    return fp32 ? launch_dtype<true>(P, stream) : launch_dtype<false>(P, stream);
+    if (landing) return fp32 ? launch_dtype<true, true>(P, stream) : launch_dtype<false, true>(P, stream);
+    return fp32 ? launch_dtype<true, false>(P, stream) : launch_dtype<false, false>(P, stream);
 }
 
 }  // namespace epdc

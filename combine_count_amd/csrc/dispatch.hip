@@ -86,7 +86,9 @@ __device__ __forceinline__ void load_slab(u32x4 (&v)[CPW], const uint8_t *row, i
     for (int c = 0; c < CPW; ++c) {
         const int gc = slab * CPW + c;
         const int e = gc * kChunkBytes + lane * 16;
-        if (FULL || (gc < nChunks && e < rowBytes)) v[c] = load16<kNtLoad>(row + e);
+        // A lane past the row's end loads the row's first 16 bytes (in
+        // bounds, never stored): unconditional loads need no branch or wait.
+        v[c] = load16<kNtLoad>(row + ((FULL || (gc < nChunks && e < rowBytes)) ? e : 0));
     }
 }
 

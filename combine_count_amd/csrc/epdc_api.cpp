@@ -98,6 +98,13 @@ size_t scratch_bytes(const epdc_cfg *c) {
     return (size_t)((epdc::kScratchHeaderWords + 2 * nTiles * pow2_ceil(c->worldSize)) * sizeof(uint32_t));
 }
 
+// Landing rows of the scatter combine: one per (token, PE), at most
+// min(W, K) PEs per token.  numTokens <= M and W*M fits int32, so this does.
+int32_t landing_rows(const epdc_cfg *c, int32_t numTokens) {
+    const int32_t perToken = c->worldSize < c->numExpertPerToken ? c->worldSize : c->numExpertPerToken;
+    return numTokens * perToken;
+}
+
 int hip_status(hipError_t e, const char *what) {
     if (e == hipSuccess) return EPDC_OK;
     return fail(EPDC_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
@@ -199,10 +206,95 @@ int epdc_combine(const epdc_cfg *cfg, int32_t numTokens, const void *y, const in
         P.weights = cfg->useWeights ? weights : nullptr;
         P.sendMap = sendMap;
         P.out = static_cast<uint8_t *>(out);
-        return hip_status(epdc::launch_combine(P, cfg->dtype == EPDC_FP32, static_cast<hipStream_t>(stream)),
+        return hip_status(epdc::launch_combine(P, cfg->dtype == EPDC_FP32, false, static_cast<hipStream_t>(stream)),
                           "combine launch");
     } catch (...) {
         return fail(EPDC_ERR_HIP, "unexpected C++ exception in epdc_combine");
+    }
+}
+
+int32_t epdc_landing_rows(const epdc_cfg *cfg, int32_t numTokens) {
+    try {
+        if (check_cfg(cfg, numTokens, true) != EPDC_OK) return -1;
+        return landing_rows(cfg, numTokens);
+    } catch (...) {
+        return -1;
+    }
+}
+
+int epdc_combine_push(const epdc_cfg *cfg, int32_t numTokens, const void *y, const int32_t *recvExpertIds,
+                      const float *recvWeights, const int32_t *recvCount, void *landing, float *landScale,
+                      void *stream) {
+    try {
+        g_lastError.clear();
+        int rc = check_cfg(cfg, numTokens, true);
+        if (rc != EPDC_OK) return rc;
+        if (numTokens == 0) return EPDC_OK;
+        if (!y || !recvCount || !landing) return fail(EPDC_ERR_NULLPTR, "a required push pointer is NULL");
+        if (cfg->useWeights && (!recvExpertIds || !recvWeights || !landScale))
+            return fail(EPDC_ERR_NULLPTR, "useWeights=1 needs recvExpertIds, recvWeights and landScale");
+        if (!aligned(y, 16) || !aligned(landing, 16))
+            return fail(EPDC_ERR_ALIGN, "y and landing must be 16-byte aligned");
+        if (!aligned(recvCount, 4) ||
+            (cfg->useWeights && (!aligned(recvExpertIds, 4) || !aligned(recvWeights, 4) || !aligned(landScale, 4))))
+            return fail(EPDC_ERR_ALIGN, "int32/fp32 arrays must be 4-byte aligned");
+        epdc::PushParams P{};
+        P.W = cfg->worldSize;
+        P.M = cfg->maxTokPerRank;
+        P.Epr = cfg->numExpertPerRank;
+        P.K = cfg->numExpertPerToken;
+        P.useWeights = cfg->useWeights;
+        P.rowBytes = cfg->hiddenDim * elem_bytes(cfg->dtype, true);
+        P.eprShift = log2_exact(cfg->numExpertPerRank);
+        P.nChunks = epdc::ceil_div(P.rowBytes, epdc::kChunkBytes);
+        P.landRows = landing_rows(cfg, numTokens);
+        P.y = static_cast<const uint8_t *>(y);
+        P.recvExpertIds = cfg->useWeights ? recvExpertIds : nullptr;
+        P.recvWeights = cfg->useWeights ? recvWeights : nullptr;
+        P.recvCount = recvCount;
+        P.landing = static_cast<uint8_t *>(landing);
+        P.landScale = cfg->useWeights ? landScale : nullptr;
+        return hip_status(epdc::launch_combine_push(P, static_cast<hipStream_t>(stream)), "push launch");
+    } catch (...) {
+        return fail(EPDC_ERR_HIP, "unexpected C++ exception in epdc_combine_push");
+    }
+}
+
+int epdc_combine_reduce(const epdc_cfg *cfg, int32_t numTokens, const void *landing, const float *landScale,
+                        const int32_t *recvCount, const int32_t *sendMap, void *out, void *stream) {
+    try {
+        g_lastError.clear();
+        int rc = check_cfg(cfg, numTokens, true);
+        if (rc != EPDC_OK) return rc;
+        if (numTokens == 0) return EPDC_OK;
+        if (!landing || !recvCount || !sendMap || !out)
+            return fail(EPDC_ERR_NULLPTR, "a required reduce pointer is NULL");
+        if (cfg->useWeights && !landScale) return fail(EPDC_ERR_NULLPTR, "useWeights=1 needs landScale");
+        if (!aligned(landing, 16) || !aligned(out, 16))
+            return fail(EPDC_ERR_ALIGN, "landing and out must be 16-byte aligned");
+        if (!aligned(recvCount, 4) || !aligned(sendMap, 4) || (cfg->useWeights && !aligned(landScale, 4)))
+            return fail(EPDC_ERR_ALIGN, "int32/fp32 arrays must be 4-byte aligned");
+        epdc::CombineParams P{};
+        P.W = cfg->worldSize;
+        P.H = cfg->hiddenDim;
+        P.M = cfg->maxTokPerRank;
+        P.Epr = cfg->numExpertPerRank;
+        P.K = cfg->numExpertPerToken;
+        P.T = numTokens;
+        P.useWeights = cfg->useWeights;
+        P.eprShift = log2_exact(cfg->numExpertPerRank);
+        P.rowBytes = cfg->hiddenDim * elem_bytes(cfg->dtype, true);
+        P.nChunks = epdc::ceil_div(P.rowBytes, epdc::kChunkBytes);
+        P.y = static_cast<const uint8_t *>(landing);
+        P.sendMap = sendMap;
+        P.out = static_cast<uint8_t *>(out);
+        P.landScale = cfg->useWeights ? landScale : nullptr;
+        P.recvCount = recvCount;
+        P.landRows = landing_rows(cfg, numTokens);
+        return hip_status(epdc::launch_combine(P, cfg->dtype == EPDC_FP32, true, static_cast<hipStream_t>(stream)),
+                          "reduce launch");
+    } catch (...) {
+        return fail(EPDC_ERR_HIP, "unexpected C++ exception in epdc_combine_reduce");
     }
 }
 

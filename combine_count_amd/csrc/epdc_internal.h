@@ -1,5 +1,6 @@
 // Internal interface between the host entry points (epdc_api.cpp) and the
-// kernel launchers (dispatch.hip, combine.hip).  Not part of the C ABI.
+// kernel launchers (dispatch.hip, combine.hip, combine_push.hip).  Not part
+// of the C ABI.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -19,6 +20,17 @@ __device__ __forceinline__ uint64_t uniform64(uint64_t v) {
     const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
     const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
     return ((uint64_t)hi << 32) | lo;
+}
+
+// Inclusive prefix sum over the lanes of a wave64: lane i gets v_0 + ... + v_i.
+__device__ __forceinline__ int32_t wave_incl_scan(int32_t v) {
+    const int lane = threadIdx.x & 63;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+        const int32_t o = __shfl_up(v, d);
+        if (lane >= d) v += o;
+    }
+    return v;
 }
 
 // s_waitcnt vmcnt(N) with no lgkm/exp wait (gfx9 encoding: vmcnt in bits
@@ -58,6 +70,15 @@ __device__ __forceinline__ void wait_vmcnt() {
 #endif
 #ifndef EPDC_COMBINE_CPW
 #define EPDC_COMBINE_CPW 0  // 0: chosen from the shape
+#endif
+#ifndef EPDC_PUSH_NT_LOAD
+#define EPDC_PUSH_NT_LOAD 1  // non-temporal loads of the returned rows the push moves
+#endif
+#ifndef EPDC_PUSH_NT_STORE
+#define EPDC_PUSH_NT_STORE 1  // non-temporal stores of landing rows
+#endif
+#ifndef EPDC_PUSH_CPW
+#define EPDC_PUSH_CPW 0  // 0: chosen from the shape
 #endif
 
 // 16-byte access, optionally with the non-temporal (streaming) hint.
@@ -114,17 +135,37 @@ struct CombineParams {
     int32_t rowBytes;  // H * 2 (bf16) or H * 4 (fp32)
     int32_t eprShift;
     int32_t nChunks;   // ceil(rowBytes / kChunkBytes)
-    const uint8_t *y;
-    const int32_t *expertIds;
-    const float *weights;
+    const uint8_t *y;  // returned rows [W][M] (gather) or landing rows [landRows] (reduce)
+    const int32_t *expertIds;  // gather only
+    const float *weights;      // gather only
     const int32_t *sendMap;
     uint8_t *out;
+    // reduce over landing rows (scatter combine) only
+    const float *landScale;    // [landRows], NULL without useWeights
+    const int32_t *recvCount;  // [W]: landing offsets are its exclusive prefix sums
+    int32_t landRows;          // T * min(W, K)
+};
+
+// Push half of the scatter combine: window rows -> packed landing rows.
+struct PushParams {
+    int32_t W, M, Epr, K, useWeights;
+    int32_t rowBytes;  // H * 2 (bf16) or H * 4 (fp32)
+    int32_t eprShift;
+    int32_t nChunks;
+    int32_t landRows;  // T * min(W, K)
+    const uint8_t *y;  // [W][M] returned rows
+    const int32_t *recvExpertIds;  // [W][M][K]
+    const float *recvWeights;      // [W][M][K], NULL without useWeights
+    const int32_t *recvCount;      // [W]
+    uint8_t *landing;              // [landRows] rows
+    float *landScale;              // [landRows], NULL without useWeights
 };
 
 __host__ __device__ inline int32_t ceil_div(int64_t a, int64_t b) { return (int32_t)((a + b - 1) / b); }
 
 // Launchers: enqueue on `stream`, return the hipGetLastError() after launch.
 hipError_t launch_dispatch(const DispatchParams &p, hipStream_t stream);
-hipError_t launch_combine(const CombineParams &p, bool fp32, hipStream_t stream);
+hipError_t launch_combine(const CombineParams &p, bool fp32, bool landing, hipStream_t stream);
+hipError_t launch_combine_push(const PushParams &p, hipStream_t stream);
 
 }  // namespace epdc

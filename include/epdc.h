@@ -12,6 +12,12 @@
  *             (MORI JIT v2 design doc, §3.7).
  *   combine   MORI JIT v2 design doc, §5 and §9: a gather combine -- each token
  *             pulls the rows its PEs returned and reduces them.
+ *   scatter combine (push + reduce)  MORI JIT v2 design doc, §5 and §9 (the
+ *             FlyDSL backend's scatter combine) with the landing rows sized
+ *             in the aiter MegaMoE commits on the mori PR #599 page: each
+ *             destination pushes its returned rows into per-(token, PE)
+ *             landing rows at offsets the dispatch hands over, then the
+ *             source reduces them.  Same result as the gather combine.
  *
  * Argument names follow EpCfg (MORI JIT v2 design doc, §3.2).  The geometry
  * fields of EpCfg (blockNum, warpPerBlock, waveSize) are not part of the ABI:
@@ -152,6 +158,63 @@ int epdc_dispatch(const epdc_cfg *cfg, int32_t numTokens,
 int epdc_combine(const epdc_cfg *cfg, int32_t numTokens,
                  const void *y, const int32_t *expertIds, const float *weights,
                  const int32_t *sendMap, void *out, void *stream);
+
+/* Landing rows of the scatter combine for numTokens tokens: numTokens *
+ * min(W, K), one per (token, PE) a token can reach.  -1 if cfg (with a
+ * combine dtype) or numTokens is invalid. */
+int32_t epdc_landing_rows(const epdc_cfg *cfg, int32_t numTokens);
+
+/*
+ * Scatter combine, push half: what the destination PEs do.  Every window's
+ * returned rows move into packed landing rows, each with a forwarded scale.
+ *
+ * cfg->dtype is EPDC_BF16 or EPDC_FP32: the type of y and landing.
+ * numTokens is the source's token count of the matching dispatch; it sizes
+ * the landing buffer (R = epdc_landing_rows(cfg, numTokens) rows).
+ * Inputs (device, read only):
+ *   y              [W][M][H] returned rows, indexed like recvX, 16-byte aligned
+ *   recvExpertIds  [W][M][K] int32 and
+ *   recvWeights    [W][M][K] fp32, as the matching dispatch wrote them; both
+ *                  are read only when useWeights == 1 (else may be NULL)
+ *   recvCount      [W] int32 as the matching dispatch wrote it
+ * Outputs (device):
+ *   landing    [R][H] of cfg->dtype, 16-byte aligned: row r < recvCount[p] of
+ *              window p lands at row landOff[p] + r, landOff[p] being the sum
+ *              of recvCount[q] over q < p (each count taken in [0, M]);
+ *              rows from the total count on, and rows that would fall at or
+ *              past R, are not written
+ *   landScale  [R] fp32, written only when useWeights == 1 (else may be
+ *              NULL): for each landed row, the fp32 sum, in slot order from
+ *              +0, of its token's weights (recvWeights) whose valid expert
+ *              (recvExpertIds) lives on p -- the scale the gather combine
+ *              gives PE p for that token
+ * A recvCount from the matching dispatch never exceeds R rows in total.
+ */
+int epdc_combine_push(const epdc_cfg *cfg, int32_t numTokens,
+                      const void *y, const int32_t *recvExpertIds, const float *recvWeights,
+                      const int32_t *recvCount, void *landing, float *landScale, void *stream);
+
+/*
+ * Scatter combine, reduce half: what the source does with its landing rows.
+ *
+ * cfg->dtype is EPDC_BF16 or EPDC_FP32: the type of landing and out.
+ * Inputs (device, read only):
+ *   landing    [R][H], landScale [R] (NULL iff useWeights == 0): as written by
+ *              epdc_combine_push with the same cfg, numTokens and recvCount
+ *   recvCount  [W] int32 and sendMap [T][K] int32 from the matching dispatch
+ * Output (device): out [T][H] of cfg->dtype, 16-byte aligned.
+ *
+ * For token t, the kept slots (sendMap >= 0) in ascending order give (p, r)
+ * = (sendMap / M, sendMap % M) and so landing row landOff[p] + r;
+ * acc = fmaf(scale, landing[row][h], acc) from +0 in fp32, scale = landScale
+ * of that row (1 when useWeights == 0); out as in epdc_combine.  This is the
+ * gather combine's order and arithmetic, so out is bit-identical to
+ * epdc_combine's on the same rows.  A slot whose row lies outside the landed
+ * rows (or outside [0, W*M)) counts as dropped.
+ */
+int epdc_combine_reduce(const epdc_cfg *cfg, int32_t numTokens,
+                        const void *landing, const float *landScale, const int32_t *recvCount,
+                        const int32_t *sendMap, void *out, void *stream);
 
 /* Message for the last failing call on this thread ("" if none).  The
  * pointer stays valid until the next epdc_* call on the same thread. */

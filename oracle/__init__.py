@@ -194,11 +194,12 @@ def combine_reduce(W, H, M, Epr, K, useWeights, landing, landScale, recvCount, s
     return out
 
 
-def timed_step(W, M, Epr, K, useWeights, x, expertIds, weights, y, lib=None):
+def timed_step(W, M, Epr, K, useWeights, x, expertIds, weights, y, push=False, lib=None):
     """A callable running one oracle dispatch + combine into preallocated
     buffers (allocation kept out of the timed call), for bench.py's CPU
-    baseline.  x: [T][Hd] rows of any 1/2/4-byte type; y: [W][M][Hc] bf16
-    bits (uint16) or float32.  Returns (step, outputs)."""
+    baseline; with ``push`` the combine is the scatter combine's push then
+    reduce.  x: [T][Hd] rows of any 1/2/4-byte type; y: [W][M][Hc] bf16 bits
+    (uint16) or float32.  Returns (step, outputs)."""
     lib = lib or load()
     T, Hd = x.shape
     Hc = y.shape[2]
@@ -207,7 +208,9 @@ def timed_step(W, M, Epr, K, useWeights, x, expertIds, weights, y, lib=None):
         recvX=np.empty((W, M, Hd), x.dtype), recvTokIdx=np.empty((W, M), np.int32),
         recvExpertIds=np.empty((W, M, K), np.int32), recvWeights=np.empty((W, M, K), np.float32),
         recvCount=np.empty((W,), np.int32), sendMap=np.empty((T, K), np.int32),
-        out=np.empty((T, Hc), y.dtype), acc=np.empty((Hc,), np.float32))
+        out=np.empty((T, Hc), y.dtype), acc=np.empty((Hc,), np.float32),
+        landing=np.empty((landing_rows(W, K, T) if push else 0, Hc), y.dtype),
+        landScale=np.empty((landing_rows(W, K, T) if push else 0,), np.float32))
     x = np.ascontiguousarray(x)
     expertIds = np.ascontiguousarray(expertIds, dtype=np.int32)
     weights = np.ascontiguousarray(weights, dtype=np.float32) if useWeights else None
@@ -219,8 +222,16 @@ def timed_step(W, M, Epr, K, useWeights, x, expertIds, weights, y, lib=None):
                                  _ptr(weights), _ptr(o["recvX"]), _ptr(o["recvTokIdx"]),
                                  _ptr(o["recvExpertIds"]), _ptr(o["recvWeights"]), _ptr(o["recvCount"]),
                                  _ptr(o["sendMap"]))
-        rc |= lib.oracle_combine(W, Hc, M, Epr, K, int(useWeights), T, int(fp32), _ptr(y), _ptr(expertIds),
-                                 _ptr(weights), _ptr(o["sendMap"]), None, T, _ptr(o["acc"]), _ptr(o["out"]))
+        if push:
+            rc |= lib.oracle_combine_push(W, Hc, M, Epr, K, int(useWeights), T, int(fp32), _ptr(y),
+                                          _ptr(o["recvExpertIds"]), _ptr(o["recvWeights"]), _ptr(o["recvCount"]),
+                                          _ptr(o["landing"]), _ptr(o["landScale"]))
+            rc |= lib.oracle_combine_reduce(W, Hc, M, Epr, K, int(useWeights), T, int(fp32), _ptr(o["landing"]),
+                                            _ptr(o["landScale"]), _ptr(o["recvCount"]), _ptr(o["sendMap"]),
+                                            None, T, _ptr(o["acc"]), _ptr(o["out"]))
+        else:
+            rc |= lib.oracle_combine(W, Hc, M, Epr, K, int(useWeights), T, int(fp32), _ptr(y), _ptr(expertIds),
+                                     _ptr(weights), _ptr(o["sendMap"]), None, T, _ptr(o["acc"]), _ptr(o["out"]))
         if rc:
             raise RuntimeError("oracle step failed")
 

@@ -19,6 +19,8 @@ SENT_I32 = -12345
 SENT_IDS = -777
 SENT_W = -3.5
 SENT_MAP = -99
+SENT_LAND_BYTE = 0xA5     # landing rows before the push (the oracle's fill too)
+SENT_SCALE = -3.25
 FILL = {"recvX_byte": SENT_X_BYTE, "recvTokIdx": SENT_I32, "recvExpertIds": SENT_IDS, "recvWeights": SENT_W}
 
 
@@ -71,6 +73,27 @@ class GpuRun:
         self.scratch = torch.zeros(max(nb, 4) // 4 + 1, dtype=torch.int32, device=dev)
         self.out = torch.full((T, outB), SENT_OUT_BYTE, dtype=torch.uint8, device=dev)
 
+    def alloc_landing(self, dev="cuda"):
+        """Landing rows and scales of the scatter combine, sentinel-filled."""
+        w = self.w
+        rows = epdc.epdc_landing_rows(self.ccfg, w.numTokens)
+        outB = w.hiddenDim * workloads.WIRE_BYTES[w.combineDtype]
+        self.landing = torch.full((rows, outB), SENT_LAND_BYTE, dtype=torch.uint8, device=dev)
+        self.landScale = torch.full((rows,), SENT_SCALE, dtype=torch.float32, device=dev)
+
+    def push(self, y=None, stream=None):
+        w = self.w
+        return epdc.epdc_combine_push(self.ccfg, w.numTokens, self.y if y is None else y,
+                                      self.recvExpertIds if w.useWeights else None,
+                                      self.recvWeights if w.useWeights else None, self.recvCount,
+                                      self.landing, self.landScale if w.useWeights else None, stream=stream)
+
+    def reduce(self, stream=None):
+        w = self.w
+        return epdc.epdc_combine_reduce(self.ccfg, w.numTokens, self.landing,
+                                        self.landScale if w.useWeights else None, self.recvCount, self.sendMap,
+                                        self.out, stream=stream)
+
     def scratch_clean(self) -> bool:
         """After a dispatch the scratch is all zero again (error flag included)."""
         return bool((self.scratch == 0).all().item())
@@ -100,6 +123,33 @@ def oracle_combine(w: workloads.Workload, y_bits, inp: workloads.Inputs, sendMap
     return oracle.combine(w.worldSize, w.hiddenDim, w.maxTokPerRank, w.numExpertPerRank,
                           w.numExpertPerToken, w.useWeights, y_bits, inp.expertIds,
                           wts if w.useWeights else None, sendMap, tokens=tokens)
+
+
+def oracle_push(w: workloads.Workload, y, o):
+    """The oracle push over returned rows y, from the oracle dispatch o."""
+    return oracle.combine_push(w.worldSize, w.hiddenDim, w.maxTokPerRank, w.numExpertPerRank,
+                               w.numExpertPerToken, w.useWeights, w.numTokens, y, o.recvExpertIds,
+                               o.recvWeights if w.useWeights else None, o.recvCount,
+                               fill_byte=SENT_LAND_BYTE, scale_fill=SENT_SCALE)
+
+
+def oracle_reduce(w: workloads.Workload, landing, landScale, o, tokens=None):
+    return oracle.combine_reduce(w.worldSize, w.hiddenDim, w.maxTokPerRank, w.numExpertPerRank,
+                                 w.numExpertPerToken, w.useWeights, landing, landScale, o.recvCount, o.sendMap,
+                                 tokens=tokens)
+
+
+def assert_landing_equal(g: GpuRun, landing, landScale, tag=""):
+    """Every landing row (landed or sentinel) and every scale, bit for bit."""
+    gl = g.landing.cpu().numpy()
+    ol = landing.view(np.uint8).reshape(gl.shape)
+    if not np.array_equal(gl, ol):
+        bad = np.argwhere(gl != ol)[0]
+        raise AssertionError(f"{tag} landing differs first at byte {bad.tolist()}")
+    gs = g.landScale.cpu().numpy()
+    if not np.array_equal(gs.view(np.uint32), landScale.view(np.uint32)):
+        bad = int(np.argwhere(gs.view(np.uint32) != landScale.view(np.uint32))[0, 0])
+        raise AssertionError(f"{tag} landScale[{bad}] = {gs[bad]!r} vs oracle {landScale[bad]!r}")
 
 
 def assert_dispatch_equal(g: GpuRun, o, tag=""):

@@ -132,6 +132,93 @@ def test_combine_rejects(what, over, T, ptrs, code):
     assert epdc.epdc_last_error() != ""
 
 
+def _push(c, T, **ptrs):
+    args = dict(y=P16, recvExpertIds=P16, recvWeights=P16, recvCount=P16, landing=P16, landScale=P16)
+    args.update(ptrs)
+    return epdc.epdc_combine_push(c, T, args["y"], args["recvExpertIds"], args["recvWeights"], args["recvCount"],
+                                  args["landing"], args["landScale"], stream=0, check=False)
+
+
+def _reduce(c, T, **ptrs):
+    args = dict(landing=P16, landScale=P16, recvCount=P16, sendMap=P16, out=P16)
+    args.update(ptrs)
+    return epdc.epdc_combine_reduce(c, T, args["landing"], args["landScale"], args["recvCount"], args["sendMap"],
+                                    args["out"], stream=0, check=False)
+
+
+PUSH_REJECT = [
+    ("worldSize 0", dict(worldSize=0), 8, {}, -1),
+    ("dtype fp8 cannot be summed", dict(dtype=2), 8, {}, -2),
+    ("dtype fp4x2 cannot be summed", dict(dtype=3), 8, {}, -2),
+    ("capacity", {}, 4097, {}, -3),
+    ("negative tokens", {}, -1, {}, -1),
+    ("row bytes not 16-aligned", dict(hiddenDim=7164), 8, {}, -4),
+    ("y misaligned", {}, 8, dict(y=P16 + 8), -4),
+    ("landing misaligned", {}, 8, dict(landing=P16 + 4), -4),
+    ("recvCount misaligned", {}, 8, dict(recvCount=P16 + 2), -4),
+    ("landScale misaligned", {}, 8, dict(landScale=P16 + 2), -4),
+    ("y null", {}, 8, dict(y=None), -5),
+    ("recvCount null", {}, 8, dict(recvCount=None), -5),
+    ("landing null", {}, 8, dict(landing=None), -5),
+    ("recvWeights null with useWeights", {}, 8, dict(recvWeights=None), -5),
+    ("recvExpertIds null with useWeights", {}, 8, dict(recvExpertIds=None), -5),
+    ("landScale null with useWeights", {}, 8, dict(landScale=None), -5),
+]
+
+
+@pytest.mark.parametrize("what,over,T,ptrs,code", PUSH_REJECT, ids=[r[0] for r in PUSH_REJECT])
+def test_push_rejects(what, over, T, ptrs, code):
+    assert _push(cfg(**over), T, **ptrs) == code
+    assert epdc.epdc_last_error() != ""
+
+
+REDUCE_REJECT = [
+    ("topk 0", dict(numExpertPerToken=0), 8, {}, -1),
+    ("dtype fp8 cannot be summed", dict(dtype=2), 8, {}, -2),
+    ("capacity", {}, 4097, {}, -3),
+    ("landing misaligned", {}, 8, dict(landing=P16 + 8), -4),
+    ("out misaligned", {}, 8, dict(out=P16 + 8), -4),
+    ("sendMap misaligned", {}, 8, dict(sendMap=P16 + 1), -4),
+    ("landing null", {}, 8, dict(landing=None), -5),
+    ("sendMap null", {}, 8, dict(sendMap=None), -5),
+    ("recvCount null", {}, 8, dict(recvCount=None), -5),
+    ("landScale null with useWeights", {}, 8, dict(landScale=None), -5),
+]
+
+
+@pytest.mark.parametrize("what,over,T,ptrs,code", REDUCE_REJECT, ids=[r[0] for r in REDUCE_REJECT])
+def test_reduce_rejects(what, over, T, ptrs, code):
+    assert _reduce(cfg(**over), T, **ptrs) == code
+    assert epdc.epdc_last_error() != ""
+
+
+def test_landing_rows():
+    assert epdc.epdc_landing_rows(cfg(), 4096) == 4096 * 8
+    assert epdc.epdc_landing_rows(cfg(worldSize=4, numExpertPerToken=6, numExpertPerRank=32), 512) == 512 * 4
+    assert epdc.epdc_landing_rows(cfg(numExpertPerToken=2), 100) == 200
+    assert epdc.epdc_landing_rows(cfg(), 0) == 0
+    assert epdc.epdc_landing_rows(cfg(dtype=2), 8) == -1   # combine dtypes only
+    assert epdc.epdc_landing_rows(cfg(), 4097) == -1       # numTokens > maxTokPerRank
+
+
+def test_push_and_reduce_without_gpu():
+    """Valid arguments pass every host check (the launch then reports
+    EPDC_ERR_HIP with no GPU); no tokens is a no-op that needs no pointers;
+    without useWeights the metadata and scale pointers may be NULL."""
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("host without a GPU only")
+    assert _push(cfg(), 8) == -7
+    assert _reduce(cfg(), 8) == -7
+    assert _push(cfg(dtype=1), 8) == -7
+    c = cfg(useWeights=0)
+    assert _push(c, 8, recvExpertIds=None, recvWeights=None, landScale=None) == -7
+    assert _reduce(c, 8, landScale=None) == -7
+    n = dict(y=None, recvExpertIds=None, recvWeights=None, recvCount=None, landing=None, landScale=None)
+    assert _push(cfg(), 0, **n) == 0
+    assert _reduce(cfg(), 0, landing=None, landScale=None, recvCount=None, sendMap=None, out=None) == 0
+
+
 def test_unweighted_accepts_null_weights_without_gpu():
     """Valid unweighted arguments pass every host check; with no GPU the
     launch itself reports EPDC_ERR_HIP instead of crashing."""
