@@ -6,8 +6,8 @@ ABI in include/epdc.h; this package is its Python binding.
 from .binding import (EPDC_BF16, EXPORTS, EpCfg, EpdcError, epdc_combine, epdc_combine_push,
                       epdc_combine_reduce, epdc_dispatch, epdc_dispatch_scratch_bytes, epdc_landing_rows,
                       epdc_last_error, load_library)
-from .buffers import DispatchBuffers
+from .buffers import DispatchBuffers, LandingBuffers
 
 __all__ = ["EPDC_BF16", "EXPORTS", "EpCfg", "EpdcError", "epdc_combine", "epdc_combine_push",
            "epdc_combine_reduce", "epdc_dispatch", "epdc_dispatch_scratch_bytes", "epdc_landing_rows",
-           "epdc_last_error", "load_library", "DispatchBuffers"]
+           "epdc_last_error", "load_library", "DispatchBuffers", "LandingBuffers"]

@@ -1,0 +1,31 @@
+"""bench.py's command-line contract that holds without a GPU."""
+import os
+import subprocess
+import sys
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def test_more_than_one_gpu_is_refused_with_a_message():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"], capture_output=True,
+                       text=True, timeout=120)
+    assert r.returncode == 2
+    assert "single GPU" in r.stderr
+    assert r.stdout == ""
+
+
+def test_algorithmic_bytes_of_the_default_workload():
+    """Per-kernel byte counts of the 4096-token h7168 workload at U = 13,020
+    unique (token, PE) pairs (the seed-1 value), written out term by term."""
+    sys.path.insert(0, ROOT)
+    sys.path.insert(0, os.path.join(ROOT, "tests"))
+    import bench
+    import workloads
+    w = workloads.CONFIGS["gen_zipf_h7168"]
+    U, T, K, W, row = 13020, 4096, 8, 8, 7168 * 2
+    d, c = bench.algorithmic_bytes(w, U)
+    assert d == T * row + 3 * T * K * 4 + U * row + U * 4 + 2 * U * K * 4 + W * 4 == 246653584
+    assert c == 3 * T * K * 4 + U * row + T * row == 245768192
+    p, r = bench.push_bytes(w, U)
+    assert p == 2 * U * row + U * K * 8 + U * 4 + W * 4
+    assert r == T * K * 4 + W * 4 + U * row + U * 4 + T * row

@@ -196,3 +196,33 @@ def test_push_reduce_graph_replay():
         got = {"landing": g.landing[:U], "landScale": g.landScale[:U], "out": g.out}
         for k, v in ref.items():
             assert torch.equal(got[k], v), f"graph replay {rep} differs from eager: {k}"
+
+
+def test_buffer_helpers_drive_every_call():
+    """DispatchBuffers / LandingBuffers give buffers every call accepts:
+    dispatch, gather combine, push and reduce on them match the oracle."""
+    w = workloads.CONFIGS["epcfg_defaults"]
+    inp = workloads.cached_inputs("epcfg_defaults", 1)
+    c = epdc.EpCfg(w.worldSize, w.hiddenDim, w.maxTokPerRank, w.numExpertPerRank, w.numExpertPerToken,
+                   epdc.EPDC_BF16, w.useWeights)
+    b = epdc.DispatchBuffers(c)
+    lb = epdc.LandingBuffers(c, w.numTokens)
+    x = torch.from_numpy(inp.x.view(np.int16)).cuda().view(torch.bfloat16)
+    y = torch.from_numpy(inp.y.view(np.int16)).cuda().view(torch.bfloat16)
+    ids = torch.from_numpy(inp.expertIds).cuda()
+    wts = torch.from_numpy(inp.weights).cuda()
+    out_g = torch.empty((w.numTokens, w.hiddenDim), dtype=torch.bfloat16, device="cuda")
+    out_r = torch.empty_like(out_g)
+    epdc.epdc_dispatch(c, w.numTokens, x, ids, wts, b.recvX, b.recvTokIdx, b.recvExpertIds, b.recvWeights,
+                       b.recvCount, b.sendMap, b.scratch)
+    epdc.epdc_combine(c, w.numTokens, y, ids, wts, b.sendMap, out_g)
+    epdc.epdc_combine_push(c, w.numTokens, y, b.recvExpertIds, b.recvWeights, b.recvCount, lb.landing, lb.landScale)
+    epdc.epdc_combine_reduce(c, w.numTokens, lb.landing, lb.landScale, b.recvCount, b.sendMap, out_r)
+    torch.cuda.synchronize()
+    o = oracle_dispatch(w, inp)
+    assert np.array_equal(b.sendMap[:w.numTokens].cpu().numpy(), o.sendMap)
+    exp = oracle_combine(w, inp.y, inp, o.sendMap)
+    got_g = out_g.view(torch.int16).cpu().numpy().view(np.uint16)
+    got_r = out_r.view(torch.int16).cpu().numpy().view(np.uint16)
+    assert_bits_equal(got_g, exp, "helpers gather")
+    assert_bits_equal(got_r, exp, "helpers reduce")
