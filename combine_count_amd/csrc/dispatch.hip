@@ -148,14 +148,15 @@ __device__ __forceinline__ void store_token(const DispatchParams &P, const u32x4
 // has 4 waves and copies the 4*NTW tokens [sub*4*NTW, (sub+1)*4*NTW) of a
 // 64-token tile -- NTW consecutive tokens per wave -- over chunks
 // [slab*CPW, (slab+1)*CPW).
-//   1. Each wave requests all of its NTW x slabs.
-//   2. COUNT (wave 0): the tile's PE masks and per-PE ballots; the tile's
+//   1. COUNT (wave 0): the tile's PE masks and per-PE ballots; the tile's
 //      leader (its first block: sub 0, slab 0) publishes the per-PE counts
 //      as count+1.
-//   3. SCAN: the leader sums the published counts of all earlier tiles into
+//   2. SCAN: the leader sums the published counts of all earlier tiles into
 //      the tile's base row on each PE and publishes it as base+1; the
 //      tile's other blocks wait for that single line (so polling traffic
 //      does not grow with the number of blocks per tile).
+//   3. Loads: the slab-0 waves' metadata rows, then every wave's NTW x
+//      slabs (after the SCAN by default: EPDC_DISPATCH_XLOAD_PHASE).
 //   4. FINALIZE: one wait for the wave's loads, then every store of its NTW
 //      tokens to every destination, with no further wait (vmcnt is one
 //      in-order counter for loads and stores on this ISA, so waiting on a
@@ -341,6 +342,10 @@ __global__ __launch_bounds__(256) void dispatch_kernel(DispatchParams P, int nSl
     if (!multiTile) return;
     __syncthreads();
     if (tid == 0) {
+        // Every publish of this block (counts and base rows) was made by
+        // wave 0 with agent-scope stores; they have retired before its done
+        // count, so the last block's clearing stores come after all of them.
+        wait_vmcnt<0>();
         const int g = b % kDoneGroups;
         const int nGroups = min(nBlocks, kDoneGroups);
         const uint32_t inGroup = (uint32_t)((nBlocks - 1 - g) / kDoneGroups + 1);
