@@ -89,10 +89,24 @@ def _ptr(a):
     return a.data_ptr()
 
 
+_current_stream = None
+
+
 def _stream(s):
+    """hipStream_t of `s`: an int passes through, a torch stream gives its
+    handle, None gives torch's current stream on the current device (through
+    torch's raw-handle query when it has one: no Stream object per call)."""
+    global _current_stream
     if s is None:
-        import torch
-        return torch.cuda.current_stream().cuda_stream
+        if _current_stream is None:
+            import torch
+            raw = getattr(torch._C, "_cuda_getCurrentRawStream", None)
+            dev = getattr(torch._C, "_cuda_getDevice", None)
+            if raw is not None and dev is not None:
+                _current_stream = lambda: raw(dev())
+            else:
+                _current_stream = lambda: torch.cuda.current_stream().cuda_stream
+        return _current_stream()
     if isinstance(s, int):
         return s
     return s.cuda_stream
@@ -117,7 +131,7 @@ def epdc_dispatch(cfg: EpCfg, numTokens: int, x, expertIds, weights, recvX, recv
                   stream=None, check: bool = True) -> int:
     if scratchBytes is None:
         scratchBytes = 0 if scratch is None or isinstance(scratch, int) else scratch.numel() * scratch.element_size()
-    rc = load_library().epdc_dispatch(
+    rc = (_lib or load_library()).epdc_dispatch(
         ctypes.byref(cfg), int(numTokens), _ptr(x), _ptr(expertIds), _ptr(weights), _ptr(recvX),
         _ptr(recvTokIdx), _ptr(recvExpertIds), _ptr(recvWeights), _ptr(recvCount), _ptr(sendMap),
         _ptr(scratch), int(scratchBytes), _stream(stream))
@@ -126,7 +140,7 @@ def epdc_dispatch(cfg: EpCfg, numTokens: int, x, expertIds, weights, recvX, recv
 
 def epdc_combine(cfg: EpCfg, numTokens: int, y, expertIds, weights, sendMap, out, stream=None,
                  check: bool = True) -> int:
-    rc = load_library().epdc_combine(
+    rc = (_lib or load_library()).epdc_combine(
         ctypes.byref(cfg), int(numTokens), _ptr(y), _ptr(expertIds), _ptr(weights), _ptr(sendMap),
         _ptr(out), _stream(stream))
     return _check(rc, check)
@@ -138,7 +152,7 @@ def epdc_landing_rows(cfg: EpCfg, numTokens: int) -> int:
 
 def epdc_combine_push(cfg: EpCfg, numTokens: int, y, recvExpertIds, recvWeights, recvCount, landing, landScale,
                       stream=None, check: bool = True) -> int:
-    rc = load_library().epdc_combine_push(
+    rc = (_lib or load_library()).epdc_combine_push(
         ctypes.byref(cfg), int(numTokens), _ptr(y), _ptr(recvExpertIds), _ptr(recvWeights), _ptr(recvCount),
         _ptr(landing), _ptr(landScale), _stream(stream))
     return _check(rc, check)
@@ -146,7 +160,7 @@ def epdc_combine_push(cfg: EpCfg, numTokens: int, y, recvExpertIds, recvWeights,
 
 def epdc_combine_reduce(cfg: EpCfg, numTokens: int, landing, landScale, recvCount, sendMap, out, stream=None,
                         check: bool = True) -> int:
-    rc = load_library().epdc_combine_reduce(
+    rc = (_lib or load_library()).epdc_combine_reduce(
         ctypes.byref(cfg), int(numTokens), _ptr(landing), _ptr(landScale), _ptr(recvCount), _ptr(sendMap),
         _ptr(out), _stream(stream))
     return _check(rc, check)
