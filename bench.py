@@ -136,7 +136,7 @@ def cpu_baseline(w, inp, budget_s, step_bytes, push):
 def main():
     args = parse_args()
     if args.gpus != 1:
-        print(f"bench.py: --gpus {args.gpus}: this build runs one GPU's share of dispatch/combine on a "
+        print(f"bench.py: --gpus {args.gpus}: the library runs one GPU's share of dispatch/combine on a "
               "single GPU; multi-GPU runs are not part of it.", file=sys.stderr)
         return 2
     import numpy as np
@@ -144,7 +144,7 @@ def main():
 
     import combine_count_amd as epdc
     import workloads
-    from gpu_harness import GpuRun
+    from gpu_harness import DeviceRun
 
     if args.copy_calibration:
         n = args.copy_calibration * (1 << 20)
@@ -170,7 +170,7 @@ def main():
         w = w.with_(name=f"{w.name}_push")
     print(f"[bench] generating {w.name} seed {args.seed}", file=sys.stderr, flush=True)
     inp = workloads.make_inputs(w, args.seed)
-    sets = [GpuRun(w, inp) for _ in range(max(1, args.rotate))]
+    sets = [DeviceRun(w, inp) for _ in range(max(1, args.rotate))]
     push = args.combine == "push"
     if push:
         for s in sets:

@@ -48,7 +48,7 @@ def dev_to_bits(t: torch.Tensor) -> np.ndarray:
     return t.view(torch.int16).cpu().numpy().view(np.uint16)
 
 
-class GpuRun:
+class DeviceRun:
     """Device copies of one input set plus sentinel-filled dispatch outputs.
     Payload buffers are raw bytes; their element type is the cfg's."""
 
@@ -139,7 +139,7 @@ def oracle_reduce(w: workloads.Workload, landing, landScale, o, tokens=None):
                                  tokens=tokens)
 
 
-def assert_landing_equal(g: GpuRun, landing, landScale, tag=""):
+def assert_landing_equal(g: DeviceRun, landing, landScale, tag=""):
     """Every landing row (landed or sentinel) and every scale, bit for bit."""
     gl = g.landing.cpu().numpy()
     ol = landing.view(np.uint8).reshape(gl.shape)
@@ -152,7 +152,7 @@ def assert_landing_equal(g: GpuRun, landing, landScale, tag=""):
         raise AssertionError(f"{tag} landScale[{bad}] = {gs[bad]!r} vs oracle {landScale[bad]!r}")
 
 
-def assert_dispatch_equal(g: GpuRun, o, tag=""):
+def assert_dispatch_equal(g: DeviceRun, o, tag=""):
     """Every dispatch output, whole buffers, bit for bit."""
     w = g.w
     cnt = g.recvCount.cpu().numpy()
@@ -178,7 +178,7 @@ def assert_dispatch_equal(g: GpuRun, o, tag=""):
         raise AssertionError(f"{tag} recvX differs first at byte {bad.tolist()}")
 
 
-def out_as(g: GpuRun) -> np.ndarray:
+def out_as(g: DeviceRun) -> np.ndarray:
     """The device out rows as the combine type (uint16 bf16 bits or float32)."""
     dt = np.uint16 if g.w.combineDtype == "bf16" else np.float32
     return g.out.cpu().numpy().view(dt)

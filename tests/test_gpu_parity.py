@@ -16,7 +16,7 @@ import torch
 
 import combine_count_amd as epdc
 import workloads
-from gpu_harness import GpuRun, assert_bits_equal, assert_dispatch_equal, oracle_combine, oracle_dispatch, out_as
+from gpu_harness import DeviceRun, assert_bits_equal, assert_dispatch_equal, oracle_combine, oracle_dispatch, out_as
 
 pytestmark = pytest.mark.gpu
 
@@ -35,7 +35,7 @@ CONFIG_SEEDS = [
 
 def _check_case(w: workloads.Workload, inp: workloads.Inputs, tag: str):
     print(f"[parity] {tag}: {w}", flush=True)
-    g = GpuRun(w, inp)
+    g = DeviceRun(w, inp)
     g.dispatch()
     torch.cuda.synchronize()
     o = oracle_dispatch(w, inp)
@@ -139,7 +139,7 @@ def test_deterministic_and_graph_replay():
     replayed several times (eager work and syncs in between) equals eager."""
     w = workloads.CONFIGS["pr_scale"]
     inp = workloads.cached_inputs("pr_scale", 1)
-    g = GpuRun(w, inp)
+    g = DeviceRun(w, inp)
     g.dispatch()
     g.combine()
     torch.cuda.synchronize()

@@ -17,7 +17,7 @@ import torch
 
 import combine_count_amd as epdc
 import workloads
-from gpu_harness import (SENT_LAND_BYTE, GpuRun, assert_bits_equal, assert_dispatch_equal, assert_landing_equal,
+from gpu_harness import (SENT_LAND_BYTE, DeviceRun, assert_bits_equal, assert_dispatch_equal, assert_landing_equal,
                          oracle_combine, oracle_dispatch, oracle_push, oracle_reduce, out_as)
 
 pytestmark = pytest.mark.gpu
@@ -25,7 +25,7 @@ pytestmark = pytest.mark.gpu
 
 def _check_push(w: workloads.Workload, inp: workloads.Inputs, tag: str):
     print(f"[push] {tag}: {w}", flush=True)
-    g = GpuRun(w, inp)
+    g = DeviceRun(w, inp)
     g.alloc_landing()
     g.dispatch()
     torch.cuda.synchronize()
@@ -102,7 +102,7 @@ def test_push_counts_past_capacity_stay_in_bounds():
     the windows' rows in the clamped layout."""
     w = workloads.Workload("push_clamp", 4, 2, 64, 40, 2, 512, "uniform", 1)
     inp = workloads.make_inputs(w, 3)
-    g = GpuRun(w, inp)
+    g = DeviceRun(w, inp)
     rows = epdc.epdc_landing_rows(g.ccfg, w.numTokens)
     assert rows == 80
     rowB = w.hiddenDim * 2
@@ -134,7 +134,7 @@ def test_reduce_treats_out_of_window_entries_as_dropped():
     on the sendMap with those entries nulled."""
     w = workloads.CONFIGS["pr_scale"]
     inp = workloads.cached_inputs("pr_scale", 1)
-    g = GpuRun(w, inp)
+    g = DeviceRun(w, inp)
     g.alloc_landing()
     g.dispatch()
     g.push()
@@ -166,7 +166,7 @@ def test_push_reduce_graph_replay():
     (eager work and syncs in between) equal the eager results."""
     w = workloads.CONFIGS["pr_scale"]
     inp = workloads.cached_inputs("pr_scale", 2)
-    g = GpuRun(w, inp)
+    g = DeviceRun(w, inp)
     g.alloc_landing()
     g.dispatch()
     g.push()

@@ -11,7 +11,7 @@ import pytest
 import torch
 
 import workloads
-from gpu_harness import (GpuRun, assert_bits_equal, assert_dispatch_equal, assert_landing_equal, oracle_combine,
+from gpu_harness import (DeviceRun, assert_bits_equal, assert_dispatch_equal, assert_landing_equal, oracle_combine,
                          oracle_dispatch, oracle_push, oracle_reduce, out_as)
 
 pytestmark = pytest.mark.gpu
@@ -52,7 +52,7 @@ def test_random_shape_parity(case):
     inp = dataclasses.replace(inp, expertIds=ids.astype(np.int32))
     tag = f"random{i} W{W} Epr{Epr} M{M} T{T} K{K} H{H} {dt} w{useW} {routing}"
     print(f"[random] {tag}", flush=True)
-    g = GpuRun(w, inp)
+    g = DeviceRun(w, inp)
     g.alloc_landing()
     g.dispatch()
     torch.cuda.synchronize()
