@@ -366,7 +366,9 @@ hipError_t launch_fused(const DispatchParams &P, int nTiles, hipStream_t stream)
     static_assert(kTile % (4 * NTW) == 0, "a block's tokens must tile the 64-token tile");
     const int nSubs = kTile / (4 * NTW);
     const int nSlabs = ceil_div(P.nChunks, CPW);
-    const int nBlocks = nTiles * nSubs * nSlabs;
+    const int64_t blocks = (int64_t)nTiles * nSubs * nSlabs;
+    if (blocks > INT32_MAX) return hipErrorInvalidConfiguration;
+    const int nBlocks = (int)blocks;
     if (P.rowBytes % kChunkBytes == 0 && P.nChunks % CPW == 0)
         hipLaunchKernelGGL((dispatch_kernel<CPW, NTW, true>), dim3(nBlocks), dim3(256), 0, stream, P, nSlabs,
                            nSubs, nBlocks);
