@@ -272,7 +272,7 @@ def main():
               "numExpertPerToken": w.numExpertPerToken, "hiddenDim": w.hiddenDim,
               "routing": w.routing + ("(s=1.1)" if w.routing == "zipf" else ""),
               "useWeights": w.useWeights, "seed": args.seed, "unique_token_pe_pairs": U,
-              "dispatch_dtype": w.wire, "combine_dtype": w.combineDtype,
+              "dispatch_dtype": w.wire, "combine_dtype": w.combineDtype, "combine_accumulate": "fp32",
               "combine": "scatter (push + reduce)" if push else "gather",
               "bytes_per_step": step_b}
     config.update({f"{n}_us": round(kern_ms[n] * 1e3, 2) for n, _, _ in stages})
