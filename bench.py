@@ -211,6 +211,23 @@ def main():
     torch.cuda.synchronize()
     ms_step = t_start.elapsed_time(t_end) / args.steps
 
+    # Spread and cache state, reported beside `value` (which is the loop above
+    # alone): the same cold loop four more times, then `steps` steps on one
+    # buffer set, whose ~490 MB then partly sit in the 256 MB Infinity Cache.
+    def loop_ms(sel):
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        a.record(stream)
+        for i in range(args.steps):
+            step(sel(i))
+        b.record(stream)
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / args.steps
+
+    repeats = [ms_step] + [loop_ms(lambda i: sets[i % len(sets)]) for _ in range(4)]
+    hot_ms = loop_ms(lambda i: sets[0])
+
     # Per-kernel durations: each kernel alone, `steps` launches back to back
     # over the same rotating buffer sets, between two HIP events on the launch
     # stream (an event pair around every launch adds ~2 us to each reading).
@@ -276,7 +293,9 @@ def main():
               "combine": "scatter (push + reduce)" if push else "gather",
               "bytes_per_step": step_b}
     config.update({f"{n}_us": round(kern_ms[n] * 1e3, 2) for n, _, _ in stages})
-    config.update({"graph_replay_step_us": round(graph_ms * 1e3, 2),
+    config.update({"step_us_cold_repeats": [round(m * 1e3, 2) for m in repeats],
+                   "step_us_hot": round(hot_ms * 1e3, 2),
+                   "graph_replay_step_us": round(graph_ms * 1e3, 2),
                    "buffer_sets_rotated": len(sets), "scratch_clean": scratch_ok,
                    "frac_of_hbm_peak": round(value / HBM_PEAK_GBPS, 4)})
     line = {
