@@ -80,6 +80,8 @@ EDGE = [
     ("t9000_ragged", 8, 32, 9000, 9000, 8, 7168, "uniform", 1),
     ("two_tokens_per_wave_t40000", 8, 32, 40000, 40000, 8, 512, "uniform", 0),
     ("slab2_h1024", 8, 32, 700, 700, 8, 1024, "zipf", 0),
+    # 32 KiB rows (four 8-chunk slabs per row)
+    ("h16384_rows", 8, 16, 600, 600, 8, 16384, "zipf", 1),
     # rows that are not a whole number of 1 KiB chunks, one per tail-checked slab width
     ("ragged_rows_1p5k", 4, 8, 300, 257, 5, 768, "uniform", 1),
     ("ragged_rows_5p5k", 8, 16, 300, 300, 8, 2816, "zipf", 1),
@@ -132,6 +134,34 @@ def test_invalid_expert_ids():
     ids[3, :] = -1  # a token with no valid slot combines to +0
     inp = dataclasses.replace(inp, expertIds=ids)
     _check_case(w, inp, "invalid_ids")
+
+
+DEGENERATE = ["all_to_one_pe", "all_slots_invalid", "all_to_every_pe", "half_tokens_invalid"]
+
+
+@pytest.mark.parametrize("kind", DEGENERATE)
+def test_degenerate_routings(kind):
+    """Routings at the edges: every token to PE 3 only (one window full, the
+    others empty); every slot invalid (no rows, all nulls, +0 combine);
+    every token to all 8 PEs (U = 8T, the window maximum per PE); every
+    other token with no valid slot."""
+    W, Epr, K, T = 8, 4, 6, 700
+    w = workloads.Workload(f"degenerate_{kind}", W, Epr, T, T, K, 1536, "uniform", 1)
+    inp = workloads.make_inputs(w, 13)
+    rng = np.random.Generator(np.random.PCG64(77))
+    if kind == "all_to_one_pe":
+        ids = (3 * Epr + rng.integers(0, Epr, size=(T, K))).astype(np.int32)
+    elif kind == "all_slots_invalid":
+        ids = np.full((T, K), -1, np.int32)
+    elif kind == "all_to_every_pe":
+        w = w.with_(numExpertPerToken=8)
+        inp = workloads.make_inputs(w, 13)
+        ids = np.stack([rng.permutation(W) * Epr + rng.integers(0, Epr, W) for _ in range(T)]).astype(np.int32)
+    else:
+        ids = inp.expertIds.copy()
+        ids[::2] = W * Epr + 1
+    inp = dataclasses.replace(inp, expertIds=ids)
+    _check_case(w, inp, kind)
 
 
 def test_deterministic_and_graph_replay():
