@@ -105,10 +105,11 @@ __device__ __forceinline__ void store_slab(const u32x4 (&v)[CPW], uint8_t *row, 
 
 // Stores one token's slab to every destination PE in its mask (the "ballot
 // walk": only live destinations are visited), all uniform scalar control.
-// A row at or past maxTokPerRank can only come from a scratch that was not
-// zero at launch; it is flagged and skipped rather than written.
+// A row outside [0, maxTokPerRank) can only come from a scratch that was not
+// zero at launch (its counts then sum to anything, negative included); it is
+// flagged and skipped rather than written.
 __device__ __forceinline__ bool row_ok(const DispatchParams &P, int32_t r) {
-    if (r < P.M) return true;
+    if ((uint32_t)r < (uint32_t)P.M) return true;
     __hip_atomic_store(P.scratch + kScratchError, 2u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     return false;
 }
@@ -117,7 +118,7 @@ template <int CPW, bool FULL>
 __device__ __forceinline__ void store_dest(const DispatchParams &P, const u32x4 (&v)[CPW],
                                            const uint64_t *sBal, const int32_t *sPre, uint64_t lt,
                                            int p, int slab, int lane) {
-    const int32_t r = uniform(sPre[p] + __popcll(sBal[p] & lt));
+    const int32_t r = uniform((int32_t)((uint32_t)sPre[p] + (uint32_t)__popcll(sBal[p] & lt)));
     if (row_ok(P, r))
         store_slab<CPW, FULL>(v, P.recvX + ((int64_t)p * P.M + r) * P.rowBytes, slab, P.nChunks, P.rowBytes, lane);
 }
@@ -314,7 +315,7 @@ __global__ __launch_bounds__(256) void dispatch_kernel(DispatchParams P, int nSl
                 while (m) {
                     const int p = __builtin_ctzll(m);
                     m &= m - 1;
-                    const int32_t r = uniform(sPre[p] + __popcll(sBal[p] & lt));
+                    const int32_t r = uniform((int32_t)((uint32_t)sPre[p] + (uint32_t)__popcll(sBal[p] & lt)));
                     if (!row_ok(P, r)) continue;
                     const int32_t f = p * P.M + r;
                     const uint64_t onP = __ballot(lane < P.K && pe == p);
@@ -329,7 +330,7 @@ __global__ __launch_bounds__(256) void dispatch_kernel(DispatchParams P, int nSl
             }
         }
         if (sub == 0 && wave == 0 && tok0 + kTile >= P.T && lane < P.W)
-            P.recvCount[lane] = sPre[lane] + __popcll(sBal[lane]);
+            P.recvCount[lane] = (int32_t)((uint32_t)sPre[lane] + (uint32_t)__popcll(sBal[lane]));
     }
 
     }  // active

@@ -164,6 +164,34 @@ def test_degenerate_routings(kind):
     _check_case(w, inp, kind)
 
 
+def test_dirty_scratch_is_flagged_and_stays_in_bounds():
+    """A scratch the caller did not zero (its published words hold garbage,
+    the header is zero) makes the base rows wrong -- summed garbage can wrap
+    to negative rows.  The dispatch must then skip every row outside
+    [0, maxTokPerRank), set the scratch error word, and write nothing outside
+    its windows: guard rows on both sides of recvX and recvTokIdx stay as
+    they were.  (Outputs are invalid in this case; only safety is checked.)"""
+    W, Epr, M, T, K, H = 4, 8, 512, 512, 6, 1024
+    w = workloads.Workload("dirty_scratch", W, Epr, M, T, K, H, "uniform", 1)
+    inp = workloads.make_inputs(w, 21)
+    g = DeviceRun(w, inp)
+    guard, rowB = 16, H * 2
+    big_x = torch.full((W * M + 2 * guard, rowB), 0x5A, dtype=torch.uint8, device="cuda")
+    big_t = torch.full((W * M + 2 * guard,), -424242, dtype=torch.int32, device="cuda")
+    g.recvX = big_x[guard:guard + W * M].view(W, M, rowB)
+    g.recvTokIdx = big_t[guard:guard + W * M].view(W, M)
+    header_words = 4224 // 4
+    g.scratch.zero_()
+    g.scratch[header_words:] = 0x7FFFFFF0
+    torch.cuda.synchronize()
+    g.dispatch()
+    torch.cuda.synchronize()
+    bx, bt = big_x.cpu().numpy(), big_t.cpu().numpy()
+    assert (bx[:guard] == 0x5A).all() and (bx[guard + W * M:] == 0x5A).all(), "recvX guard rows written"
+    assert (bt[:guard] == -424242).all() and (bt[guard + W * M:] == -424242).all(), "recvTokIdx guard written"
+    assert int(g.scratch[2].item()) != 0, "a dirty scratch was not flagged in the error word"
+
+
 def test_deterministic_and_graph_replay():
     """Two eager runs are bitwise equal; a captured dispatch+combine graph
     replayed several times (eager work and syncs in between) equals eager."""
