@@ -293,6 +293,10 @@ def main():
               "combine": "scatter (push + reduce)" if push else "gather",
               "bytes_per_step": step_b}
     config.update({f"{n}_us": round(kern_ms[n] * 1e3, 2) for n, _, _ in stages})
+    config["kernels"] = {n: {"us": round(kern_ms[n] * 1e3, 2), "algorithmic_bytes": b,
+                             "GB/s": round(b / kern_ms[n] / 1e6, 1),
+                             "frac": round(b / kern_ms[n] / 1e6 / HBM_PEAK_GBPS, 4),
+                             "traffic": read_traffic(n, w.name)} for n, _, b in stages}
     config.update({"step_us_cold_repeats": [round(m * 1e3, 2) for m in repeats],
                    "step_us_hot": round(hot_ms * 1e3, 2),
                    "graph_replay_step_us": round(graph_ms * 1e3, 2),
