@@ -226,3 +226,55 @@ def test_buffer_helpers_drive_every_call():
     got_r = out_r.view(torch.int16).cpu().numpy().view(np.uint16)
     assert_bits_equal(got_g, exp, "helpers gather")
     assert_bits_equal(got_r, exp, "helpers reduce")
+
+
+@pytest.mark.parametrize("combine_dtype", ["bf16", "fp32"])
+def test_non_finite_rows(combine_dtype):
+    """Returned rows holding +-Inf and quiet / signalling NaNs, and zero
+    weights (so 0 * Inf makes NaN): every finite or infinite result is bit
+    for bit the oracle's, and every NaN result is a NaN on both sides (its
+    payload may differ between the CPU's and the GPU's fused multiply-add),
+    for the gather combine and for push + reduce."""
+    base = workloads.CONFIGS["pr_scale"]
+    w = base.with_(name=f"non_finite_{combine_dtype}", hiddenDim=512, wire=combine_dtype,
+                   combineDtype=combine_dtype)
+    inp = workloads.make_inputs(w, 31)
+    rng = np.random.Generator(np.random.PCG64(32))
+    y = inp.y.copy()
+    pick = rng.random(y.shape) < 0.01
+    if combine_dtype == "bf16":
+        specials = np.array([0x7F80, 0xFF80, 0x7FC0, 0x7F81, 0xFFC1], dtype=np.uint16)
+    else:
+        specials = np.array([0x7F800000, 0xFF800000, 0x7FC00000, 0x7F800001, 0xFFC00001],
+                            dtype=np.uint32).view(np.float32)
+    y[pick] = rng.choice(specials, size=int(pick.sum()))
+    wts = inp.weights.copy()
+    wts[rng.random(wts.shape) < 0.1] = 0.0
+    inp = dataclasses.replace(inp, y=y, weights=wts)
+    g = DeviceRun(w, inp)
+    g.alloc_landing()
+    g.dispatch()
+    torch.cuda.synchronize()
+    o = oracle_dispatch(w, inp)
+    assert_dispatch_equal(g, o, w.name)
+    exp = oracle_combine(w, y, inp, o.sendMap)
+    land, sc = oracle_push(w, y, o)
+    g.combine()
+    torch.cuda.synchronize()
+    got_g = out_as(g).copy()
+    g.push()
+    g.reduce()
+    torch.cuda.synchronize()
+    got_r = out_as(g).copy()
+    ef = exp.astype(np.float32) if combine_dtype == "fp32" else \
+        (exp.astype(np.uint32) << 16).view(np.float32)
+    nan = np.isnan(ef)
+    assert nan.any() and np.isinf(ef).any(), "the case should produce NaN and Inf results"
+    for got, what in ((got_g, "gather"), (got_r, "reduce")):
+        gf = got.astype(np.float32) if combine_dtype == "fp32" else (got.astype(np.uint32) << 16).view(np.float32)
+        assert np.isnan(gf[nan]).all(), f"{what}: a NaN result is not NaN on the GPU"
+        assert not np.isnan(gf[~nan]).any(), f"{what}: a NaN where the oracle has none"
+        eb = exp.view(np.uint16 if combine_dtype == "bf16" else np.uint32)
+        gb = got.view(eb.dtype)
+        bad = (gb != eb) & ~nan
+        assert not bad.any(), f"{what}: {int(bad.sum())} non-NaN results differ from the oracle"
