@@ -135,6 +135,9 @@ def cpu_baseline(w, inp, budget_s, step_bytes, push):
 
 def main():
     args = parse_args()
+    if args.steps < 1 or args.warmup < 0:
+        print("bench.py: --steps must be >= 1 and --warmup >= 0", file=sys.stderr)
+        return 2
     if args.gpus != 1:
         print(f"bench.py: --gpus {args.gpus}: the library runs one GPU's share of dispatch/combine on a "
               "single GPU; multi-GPU runs are not part of it.", file=sys.stderr)
