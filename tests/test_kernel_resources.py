@@ -1,0 +1,78 @@
+"""Build guard on the gfx950 code itself (CPU: hipcc cross-compiles with the
+library's own flags): no kernel spills to scratch, the variants the default
+workloads run keep the occupancy they were tuned at, payload rows move as
+16-byte non-temporal accesses, and no packed-fp32 instruction is emitted."""
+import os
+import re
+import subprocess
+
+import pytest
+
+from combine_count_amd import _build as B
+
+SOURCES = ["dispatch.hip", "combine.hip", "combine_push.hip"]
+
+
+def _compile(src, tmpdir):
+    asm = os.path.join(tmpdir, src + ".s")
+    cmd = [B.HIPCC, *B.DEVICE, *B.COMMON, "--cuda-device-only", "-S", os.path.join(B.CSRC, src), "-o", asm,
+           "-Rpass-analysis=kernel-resource-usage"]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr[-2000:]
+    res, cur = {}, None
+    for line in r.stderr.splitlines():
+        m = re.search(r"remark: Function Name: (\S+)", line)
+        if m:
+            cur = res.setdefault(m.group(1), {})
+            continue
+        m = re.search(r"remark:\s+([A-Za-z ]+?)(?: \[[^\]]*\])?: (\d+)", line)
+        if m and cur is not None:
+            cur[m.group(1).strip()] = int(m.group(2))
+    return res, open(asm).read()
+
+
+@pytest.fixture(scope="module")
+def compiled(tmp_path_factory):
+    d = str(tmp_path_factory.mktemp("isa"))
+    return {src: _compile(src, d) for src in SOURCES}
+
+
+def _kernel(res, pattern):
+    hits = [k for k in res if re.search(pattern, k)]
+    assert len(hits) == 1, (pattern, hits)
+    return res[hits[0]]
+
+
+def test_no_scratch_and_no_spills(compiled):
+    for src, (res, _) in compiled.items():
+        assert res, f"{src}: no resource remarks parsed"
+        for name, r in res.items():
+            assert r.get("ScratchSize", 0) == 0, (src, name, r)
+            # (SGPR spills go to VGPR lanes, not memory: allowed)
+            assert r.get("VGPRs Spill", 0) == 0, (src, name, r)
+
+
+def test_default_variants_keep_their_occupancy(compiled):
+    d, c, p = compiled["dispatch.hip"][0], compiled["combine.hip"][0], compiled["combine_push.hip"][0]
+    # 4096 tokens x h7168 bf16: dispatch 7-chunk slabs, 1 token per wave, no bound checks
+    assert _kernel(d, r"dispatch_kernelILi7ELi1ELb1EE")["Occupancy"] >= 7
+    # gather combine, 2-chunk slabs, bf16, and its landing-row twin
+    assert _kernel(c, r"combine_kernelILi2ELb1ELb0ELb0EE")["Occupancy"] >= 5
+    assert _kernel(c, r"combine_kernelILi2ELb1ELb0ELb1EE")["Occupancy"] >= 5
+    assert _kernel(p, r"push_kernelILi7ELb1EE")["Occupancy"] == 8
+    for src, (res, _) in compiled.items():
+        for name, r in res.items():
+            if "Occupancy" in r and "kernel" in name:
+                assert r["Occupancy"] >= 3, (src, name, r)
+
+
+def test_rows_move_as_16_byte_non_temporal_accesses(compiled):
+    d, c, p = (compiled[s][1] for s in SOURCES)
+    assert re.search(r"global_store_dwordx4 .* nt", d), "dispatch row stores"
+    assert re.search(r"global_load_dwordx4 .* nt", c) and re.search(r"global_store_dwordx4 .* nt", c), "combine"
+    assert re.search(r"global_load_dwordx4 .* nt", p) and re.search(r"global_store_dwordx4 .* nt", p), "push"
+
+
+def test_no_packed_fp32_instructions(compiled):
+    for src, (_, asm) in compiled.items():
+        assert not re.search(r"\bv_pk_(fma|mul|add)_f32\b", asm), src
