@@ -66,7 +66,7 @@ __device__ __forceinline__ void wait_vmcnt() {
 #define EPDC_DISPATCH_XLOAD_PHASE 2  // 0: x loads before COUNT, 1: after publishing, 2: after SCAN
 #endif
 #ifndef EPDC_COMBINE_GROUP
-#define EPDC_COMBINE_GROUP 4  // returned rows requested together per wave (1..8)
+#define EPDC_COMBINE_GROUP 8  // returned rows requested together per wave (1..8)
 #endif
 #ifndef EPDC_COMBINE_CPW
 #define EPDC_COMBINE_CPW 0  // 0: chosen from the shape
