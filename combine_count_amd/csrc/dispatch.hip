@@ -149,6 +149,8 @@ __device__ __forceinline__ void store_token(const DispatchParams &P, const u32x4
 // has 4 waves and copies the 4*NTW tokens [sub*4*NTW, (sub+1)*4*NTW) of a
 // 64-token tile -- NTW consecutive tokens per wave -- over chunks
 // [slab*CPW, (slab+1)*CPW).
+//   0. Launches of at most EPDC_DISPATCH_LOCAL_SCAN_TILES tiles request all
+//      their loads first and scan locally (step 2); the others:
 //   1. COUNT (wave 0): the tile's PE masks and per-PE ballots; the tile's
 //      leader (its first block: sub 0, slab 0) publishes the per-PE counts
 //      as count+1.
@@ -167,7 +169,7 @@ __device__ __forceinline__ void store_token(const DispatchParams &P, const u32x4
 //   5. The last block to finish clears the published counts; the done
 //      counters wrap to zero by themselves, so the scratch is zero again for
 //      the next call (and for every replay of a captured graph).
-template <int CPW, int NTW, bool FULL>
+template <int CPW, int NTW, bool FULL, bool LOCAL>
 __global__ __launch_bounds__(256) void dispatch_kernel(DispatchParams P, int nSlabs, int nSubs, int nBlocks) {
     __shared__ uint64_t sMask[kTile];  // destination-PE set of each token of the tile
     __shared__ uint64_t sBal[64];      // per PE: which tokens of the tile go there
@@ -193,15 +195,21 @@ __global__ __launch_bounds__(256) void dispatch_kernel(DispatchParams P, int nSl
     const int nTok = min(kTile, P.T - tok0);
     const int iBeg = (sub * 4 + wave) * NTW;  // this wave's tokens: [iBeg, iBeg + NTW) of the tile
     const uint8_t *xTile = P.x + (int64_t)tok0 * P.rowBytes;
-    // A launch of one tile needs no scratch at all (its base rows are 0); a
+    // LOCAL (launches of at most EPDC_DISPATCH_LOCAL_SCAN_TILES tiles): every
+    // block counts the earlier tiles' tokens itself (their ids are a few KB,
+    // read from L2), so there is no publishing, no cross-block wait and no
+    // scratch, and every load can be issued up front -- small launches are
+    // bound by round trips, not bytes.  (One tile: its base rows are 0.)  A
+    // separate instantiation, so the scratch path compiles as if alone.  A
     // block whose token group lies past the last token only counts itself
     // done.
-    const bool multiTile = nTilesAll > 1;
+    constexpr bool localScan = LOCAL;
     const bool active = sub * 4 * NTW < nTok;
     if (active) {
 
-    // 1. Request every x slab of this wave (a token past the end of the tile
-    // re-reads the last one; it is not stored).
+    // Every x slab of this wave (a token past the end of the tile re-reads
+    // the last one; it is not stored), and the slab-0 waves' metadata rows
+    // (lanes are slots).
     u32x4 buf[NTW][CPW];
     auto load_x = [&]() {
 #pragma unroll
@@ -210,9 +218,27 @@ __global__ __launch_bounds__(256) void dispatch_kernel(DispatchParams P, int nSl
             load_slab<CPW, FULL>(buf[j], xTile + (int64_t)i * P.rowBytes, slab, P.nChunks, P.rowBytes, lane);
         }
     };
-#if EPDC_DISPATCH_XLOAD_PHASE == 0
-    load_x();
-#endif
+    int32_t mid[NTW];
+    float mwt[NTW];
+    auto load_meta = [&]() {
+#pragma unroll
+        for (int j = 0; j < NTW; ++j) {
+            mid[j] = -1;
+            mwt[j] = 0.0f;
+            const int i = iBeg + j;
+            if (slab == 0 && i < nTok && lane < P.K) {
+                const int64_t o = (int64_t)(tok0 + i) * P.K + lane;
+                mid[j] = P.expertIds[o];
+                if (P.useWeights) mwt[j] = P.weights[o];
+            }
+        }
+    };
+    if constexpr (localScan) {
+        load_x();
+        load_meta();
+    } else if (EPDC_DISPATCH_XLOAD_PHASE == 0) {
+        load_x();
+    }
 
     // 2. COUNT for this tile (wave 0); the tile's leader block (sub 0,
     // slab 0: the first block of the tile) publishes the per-PE counts.
@@ -227,21 +253,29 @@ __global__ __launch_bounds__(256) void dispatch_kernel(DispatchParams P, int nSl
             if (lane == 0) sBal[p] = bal;
             if (lane == p) cnt = __popcll(bal);
         }
-        if (multiTile && leader && lane < P.Wp)
+        if (!localScan && leader && lane < P.Wp)
             __hip_atomic_store(published + (int64_t)tile * P.Wp + lane, (uint32_t)cnt + 1u, __ATOMIC_RELAXED,
                                __HIP_MEMORY_SCOPE_AGENT);
     }
 
-#if EPDC_DISPATCH_XLOAD_PHASE == 1
-    load_x();
-#endif
+    if constexpr (!localScan && EPDC_DISPATCH_XLOAD_PHASE == 1) load_x();
 
     // 3. SCAN: exclusive base of this tile on each PE.  The leader sums the
     // published counts of all earlier tiles (the row stride Wp is a power of
     // two dividing 256, so thread tid only ever sums PE tid % Wp) and
     // publishes the result; the tile's other blocks wait for that one line.
-    // Tile 0's base rows are 0: nothing to sum, publish or wait for.
-    if (tile > 0 && leader) {
+    // Tile 0's base rows are 0: nothing to sum, publish or wait for.  A
+    // local scan counts the earlier tiles (all full) in this block instead,
+    // the 4 waves taking tiles wave, wave + 4, ...
+    if constexpr (localScan) {
+        for (int j = wave; j < tile; j += 4) {
+            const uint64_t m = token_pe_mask(P, j * kTile + lane);
+            for (int p = 0; p < P.W; ++p) {
+                const uint64_t bal = __ballot((m >> p) & 1ull);
+                if (lane == p && bal) atomicAdd(&sPre[p], (int32_t)__popcll(bal));
+            }
+        }
+    } else if (tile > 0 && leader) {
         const int n = tile * P.Wp;
         uint32_t acc = 0;
         int idx = tid;
@@ -271,26 +305,15 @@ __global__ __launch_bounds__(256) void dispatch_kernel(DispatchParams P, int nSl
     }
     __syncthreads();
 
-    // Metadata rows of this wave's tokens (slab-0 blocks only; lanes are
-    // slots), requested before x so that no wait below follows a store.
+    // Scanning through the scratch, the metadata rows and then (by default)
+    // the x slabs are requested only now: issued before the SCAN, the x
+    // flood would delay the SCAN's own small reads.  Either way no wait
+    // below follows a store.
     const int32_t E = P.W * P.Epr;
-    int32_t mid[NTW];
-    float mwt[NTW];
-#pragma unroll
-    for (int j = 0; j < NTW; ++j) {
-        mid[j] = -1;
-        mwt[j] = 0.0f;
-        const int i = iBeg + j;
-        if (slab == 0 && i < nTok && lane < P.K) {
-            const int64_t o = (int64_t)(tok0 + i) * P.K + lane;
-            mid[j] = P.expertIds[o];
-            if (P.useWeights) mwt[j] = P.weights[o];
-        }
+    if constexpr (!localScan) {
+        load_meta();
+        if (EPDC_DISPATCH_XLOAD_PHASE == 2) load_x();
     }
-
-#if EPDC_DISPATCH_XLOAD_PHASE == 2
-    load_x();
-#endif
 
     // 4. FINALIZE payload: one wait for every load above, then only stores.
     wait_vmcnt<0>();
@@ -340,7 +363,7 @@ __global__ __launch_bounds__(256) void dispatch_kernel(DispatchParams P, int nSl
     // done, so the last one may clear them.
     // Two-level count so that no counter takes more than ~nBlocks/32 atomics:
     // the last block of each group (b % 32) counts its group done.
-    if (!multiTile) return;
+    if constexpr (localScan) return;
     __syncthreads();
     if (tid == 0) {
         // Every publish of this block (counts and base rows) was made by
@@ -370,12 +393,22 @@ hipError_t launch_fused(const DispatchParams &P, int nTiles, hipStream_t stream)
     const int64_t blocks = (int64_t)nTiles * nSubs * nSlabs;
     if (blocks > INT32_MAX) return hipErrorInvalidConfiguration;
     const int nBlocks = (int)blocks;
-    if (P.rowBytes % kChunkBytes == 0 && P.nChunks % CPW == 0)
-        hipLaunchKernelGGL((dispatch_kernel<CPW, NTW, true>), dim3(nBlocks), dim3(256), 0, stream, P, nSlabs,
-                           nSubs, nBlocks);
-    else
-        hipLaunchKernelGGL((dispatch_kernel<CPW, NTW, false>), dim3(nBlocks), dim3(256), 0, stream, P, nSlabs,
-                           nSubs, nBlocks);
+    const bool full = P.rowBytes % kChunkBytes == 0 && P.nChunks % CPW == 0;
+    const dim3 grid(nBlocks);
+    if (nTiles <= EPDC_DISPATCH_LOCAL_SCAN_TILES) {
+        if (full)
+            hipLaunchKernelGGL((dispatch_kernel<CPW, NTW, true, true>), grid, dim3(256), 0, stream, P, nSlabs, nSubs,
+                               nBlocks);
+        else
+            hipLaunchKernelGGL((dispatch_kernel<CPW, NTW, false, true>), grid, dim3(256), 0, stream, P, nSlabs,
+                               nSubs, nBlocks);
+    } else if (full) {
+        hipLaunchKernelGGL((dispatch_kernel<CPW, NTW, true, false>), grid, dim3(256), 0, stream, P, nSlabs, nSubs,
+                           nBlocks);
+    } else {
+        hipLaunchKernelGGL((dispatch_kernel<CPW, NTW, false, false>), grid, dim3(256), 0, stream, P, nSlabs, nSubs,
+                           nBlocks);
+    }
     return hipGetLastError();
 }
 

@@ -65,6 +65,9 @@ __device__ __forceinline__ void wait_vmcnt() {
 #ifndef EPDC_DISPATCH_XLOAD_PHASE
 #define EPDC_DISPATCH_XLOAD_PHASE 2  // 0: x loads before COUNT, 1: after publishing, 2: after SCAN
 #endif
+#ifndef EPDC_DISPATCH_LOCAL_SCAN_TILES
+#define EPDC_DISPATCH_LOCAL_SCAN_TILES 8  // launches of up to this many 64-token tiles scan in every block
+#endif
 #ifndef EPDC_COMBINE_GROUP
 #define EPDC_COMBINE_GROUP 8  // returned rows requested together per wave (1..8)
 #endif

@@ -80,6 +80,9 @@ EDGE = [
     ("t9000_ragged", 8, 32, 9000, 9000, 8, 7168, "uniform", 1),
     ("two_tokens_per_wave_t40000", 8, 32, 40000, 40000, 8, 512, "uniform", 0),
     ("slab2_h1024", 8, 32, 700, 700, 8, 1024, "zipf", 0),
+    # at the edge of the local scan (8 tiles) and just past it (9 tiles)
+    ("local_scan_8_tiles", 8, 8, 512, 512, 8, 2048, "uniform", 1),
+    ("scratch_scan_9_tiles", 8, 8, 600, 520, 8, 2048, "zipf", 1),
     # 32 KiB rows (four 8-chunk slabs per row)
     ("h16384_rows", 8, 16, 600, 600, 8, 16384, "zipf", 1),
     # rows that are not a whole number of 1 KiB chunks, one per tail-checked slab width
@@ -171,7 +174,7 @@ def test_dirty_scratch_is_flagged_and_stays_in_bounds():
     [0, maxTokPerRank), set the scratch error word, and write nothing outside
     its windows: guard rows on both sides of recvX and recvTokIdx stay as
     they were.  (Outputs are invalid in this case; only safety is checked.)"""
-    W, Epr, M, T, K, H = 4, 8, 512, 512, 6, 1024
+    W, Epr, M, T, K, H = 4, 8, 1024, 1024, 6, 1024  # 16 tiles: scanned through the scratch
     w = workloads.Workload("dirty_scratch", W, Epr, M, T, K, H, "uniform", 1)
     inp = workloads.make_inputs(w, 21)
     g = DeviceRun(w, inp)

@@ -54,8 +54,10 @@ def test_no_scratch_and_no_spills(compiled):
 
 def test_default_variants_keep_their_occupancy(compiled):
     d, c, p = compiled["dispatch.hip"][0], compiled["combine.hip"][0], compiled["combine_push.hip"][0]
-    # 4096 tokens x h7168 bf16: dispatch 7-chunk slabs, 1 token per wave, no bound checks
-    assert _kernel(d, r"dispatch_kernelILi7ELi1ELb1EE")["Occupancy"] >= 7
+    # 4096 tokens x h7168 bf16: dispatch 7-chunk slabs, 1 token per wave, no bound checks,
+    # scan through the scratch; and the same for launches of at most 8 tiles (local scan)
+    assert _kernel(d, r"dispatch_kernelILi7ELi1ELb1ELb0EE")["Occupancy"] >= 7
+    assert _kernel(d, r"dispatch_kernelILi7ELi1ELb1ELb1EE")["Occupancy"] >= 7
     # gather combine, 2-chunk slabs, bf16 (up to 8 rows in flight), and its landing-row twin
     assert _kernel(c, r"combine_kernelILi2ELb1ELb0ELb0EE")["Occupancy"] >= 4
     assert _kernel(c, r"combine_kernelILi2ELb1ELb0ELb1EE")["Occupancy"] >= 4
