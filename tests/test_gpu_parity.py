@@ -240,3 +240,33 @@ def test_library_is_in_tree():
     lib = epdc.load_library()
     assert lib._name.endswith("combine_count_amd/libepdc.so")
     assert torch.cuda.is_available()
+
+
+def test_one_scratch_across_varying_token_counts():
+    """A serving loop: one scratch buffer, dispatches of different token
+    counts (local and scratch-scanned launches mixed, the large ones first)
+    enqueued back to back with no sync in between; every call matches the
+    oracle and the scratch ends all zero."""
+    base = workloads.Workload("varying_T", 8, 32, 4096, 4096, 8, 1024, "zipf", 1)
+    counts = [4096, 777, 65, 4096, 1, 2000, 512, 3000]
+    runs = []
+    shared = None
+    for i, T in enumerate(counts):
+        w = base.with_(name=f"varying_T{T}", numTokens=T)
+        inp = workloads.make_inputs(w, 40 + i)
+        g = DeviceRun(w, inp)
+        if shared is None:
+            shared = g.scratch
+        g.scratch = shared
+        runs.append((w, inp, g))
+    torch.cuda.synchronize()
+    for w, inp, g in runs:
+        g.dispatch()
+        g.combine()
+    torch.cuda.synchronize()
+    for w, inp, g in runs:
+        tag = f"T={w.numTokens}"
+        o = oracle_dispatch(w, inp)
+        assert_dispatch_equal(g, o, tag)
+        assert_bits_equal(out_as(g), oracle_combine(w, inp.y, inp, o.sendMap), f"{tag} combine")
+    assert bool((shared == 0).all().item()), "the shared scratch is not all zero after the calls"
