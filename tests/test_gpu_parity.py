@@ -195,11 +195,23 @@ def test_dirty_scratch_is_flagged_and_stays_in_bounds():
     assert int(g.scratch[2].item()) != 0, "a dirty scratch was not flagged in the error word"
 
 
-def test_deterministic_and_graph_replay():
+GRAPH_CASES = [
+    ("pr_scale", None),  # 8 tiles: local scan, scratch untouched
+    ("gen_zipf_h2048", dict(numTokens=1024, maxTokPerRank=1024)),  # 16 tiles: scan through the scratch
+]
+
+
+@pytest.mark.parametrize("name,over", GRAPH_CASES, ids=[c[0] for c in GRAPH_CASES])
+def test_deterministic_and_graph_replay(name, over):
     """Two eager runs are bitwise equal; a captured dispatch+combine graph
-    replayed several times (eager work and syncs in between) equals eager."""
-    w = workloads.CONFIGS["pr_scale"]
-    inp = workloads.cached_inputs("pr_scale", 1)
+    replayed several times (eager work and syncs in between) equals eager,
+    and the scratch is zero after every replay."""
+    w = workloads.CONFIGS[name]
+    if over:
+        w = w.with_(**over)
+        inp = workloads.make_inputs(w, 1)
+    else:
+        inp = workloads.cached_inputs(name, 1)
     g = DeviceRun(w, inp)
     g.dispatch()
     g.combine()
