@@ -74,11 +74,14 @@ EDGE = [
     ("topk1", 8, 4, 200, 129, 1, 2048, "uniform", 1),
     ("m_gt_t", 8, 32, 4096, 777, 8, 7168, "zipf", 1),
     ("one_token_full_row", 8, 32, 64, 1, 8, 7168, "uniform", 0),
-    # geometry paths: 8-chunk slabs (1 and 2 per row), 2 tokens per wave
+    # geometry paths: 8-chunk slabs (1 and 2 per row); 625 tiles; 2 and 4 tokens per
+    # wave (11 KiB rows: eleven 1-chunk slabs, so 94 / 188 tiles pass 16384 / 32768 blocks)
     ("slab8_h4096", 8, 32, 1000, 1000, 8, 4096, "zipf", 1),
     ("slab8_h8192_two_slabs", 4, 16, 300, 300, 6, 8192, "uniform", 1),
     ("t9000_ragged", 8, 32, 9000, 9000, 8, 7168, "uniform", 1),
-    ("two_tokens_per_wave_t40000", 8, 32, 40000, 40000, 8, 512, "uniform", 0),
+    ("t40000_h512", 8, 32, 40000, 40000, 8, 512, "uniform", 0),
+    ("two_tokens_per_wave_t6000", 2, 4, 6000, 6000, 4, 5632, "uniform", 1),
+    ("four_tokens_per_wave_t12000", 2, 4, 12000, 11990, 3, 5632, "zipf", 0),
     ("slab2_h1024", 8, 32, 700, 700, 8, 1024, "zipf", 0),
     # at the edge of the local scan (8 tiles) and just past it (9 tiles)
     ("local_scan_8_tiles", 8, 8, 512, 512, 8, 2048, "uniform", 1),
