@@ -83,6 +83,8 @@ EDGE = [
     ("two_tokens_per_wave_t6000", 2, 4, 6000, 6000, 4, 5632, "uniform", 1),
     ("four_tokens_per_wave_t12000", 2, 4, 12000, 11990, 3, 5632, "zipf", 0),
     ("slab2_h1024", 8, 32, 700, 700, 8, 1024, "zipf", 0),
+    # combine in 2-chunk slabs with bound checks (5.5 KiB rows, 4000 tokens x 3 slabs)
+    ("combine_slab2_ragged_t4000", 4, 8, 4000, 4000, 6, 2816, "zipf", 1),
     # at the edge of the local scan (8 tiles) and just past it (9 tiles)
     ("local_scan_8_tiles", 8, 8, 512, 512, 8, 2048, "uniform", 1),
     ("scratch_scan_9_tiles", 8, 8, 600, 520, 8, 2048, "zipf", 1),
