@@ -3,11 +3,13 @@
 The compute path is libepdc.so (hand-written HIP for gfx950) behind the C
 ABI in include/epdc.h; this package is its Python binding.
 """
-from .binding import (EPDC_BF16, EXPORTS, EpCfg, EpdcError, epdc_combine, epdc_combine_push,
+from .binding import (EPDC_BF16, EXPORTS, EpCfg, EpdcError, PreparedCall, epdc_combine, epdc_combine_push,
                       epdc_combine_reduce, epdc_dispatch, epdc_dispatch_scratch_bytes, epdc_landing_rows,
-                      epdc_last_error, load_library)
+                      epdc_last_error, load_library, prepare_combine, prepare_combine_push,
+                      prepare_combine_reduce, prepare_dispatch)
 from .buffers import DispatchBuffers, LandingBuffers
 
 __all__ = ["EPDC_BF16", "EXPORTS", "EpCfg", "EpdcError", "epdc_combine", "epdc_combine_push",
            "epdc_combine_reduce", "epdc_dispatch", "epdc_dispatch_scratch_bytes", "epdc_landing_rows",
-           "epdc_last_error", "load_library", "DispatchBuffers", "LandingBuffers"]
+           "epdc_last_error", "load_library", "DispatchBuffers", "LandingBuffers", "PreparedCall",
+           "prepare_dispatch", "prepare_combine", "prepare_combine_push", "prepare_combine_reduce"]

@@ -164,3 +164,58 @@ def epdc_combine_reduce(cfg: EpCfg, numTokens: int, landing, landScale, recvCoun
         ctypes.byref(cfg), int(numTokens), _ptr(landing), _ptr(landScale), _ptr(recvCount), _ptr(sendMap),
         _ptr(out), _stream(stream))
     return _check(rc, check)
+
+
+class PreparedCall:
+    """One entry point with every argument but the stream marshalled once.
+
+    For launch loops that reuse the same buffers (a serving step, a
+    benchmark): the device pointers and sizes are fixed at preparation, so a
+    call costs one ctypes call.  The buffers must stay alive and in place as
+    long as the prepared call is used; `keep` holds references to them."""
+
+    def __init__(self, fn, args, keep):
+        self._fn = fn
+        self._args = tuple(args)
+        self._keep = keep
+
+    def __call__(self, stream=None, check: bool = True) -> int:
+        rc = self._fn(*self._args, _stream(stream))
+        if rc != 0 and check:
+            raise EpdcError(rc, epdc_last_error())
+        return rc
+
+
+def _vp(a):
+    p = _ptr(a)
+    return ctypes.c_void_p(p) if p is not None else None
+
+
+def prepare_dispatch(cfg: EpCfg, numTokens: int, x, expertIds, weights, recvX, recvTokIdx, recvExpertIds,
+                     recvWeights, recvCount, sendMap, scratch, scratchBytes: int | None = None) -> PreparedCall:
+    if scratchBytes is None:
+        scratchBytes = 0 if scratch is None or isinstance(scratch, int) else scratch.numel() * scratch.element_size()
+    bufs = (x, expertIds, weights, recvX, recvTokIdx, recvExpertIds, recvWeights, recvCount, sendMap, scratch)
+    args = [ctypes.byref(cfg), ctypes.c_int32(int(numTokens)), *(_vp(b) for b in bufs),
+            ctypes.c_size_t(int(scratchBytes))]
+    return PreparedCall((_lib or load_library()).epdc_dispatch, args, (cfg, bufs))
+
+
+def prepare_combine(cfg: EpCfg, numTokens: int, y, expertIds, weights, sendMap, out) -> PreparedCall:
+    bufs = (y, expertIds, weights, sendMap, out)
+    args = [ctypes.byref(cfg), ctypes.c_int32(int(numTokens)), *(_vp(b) for b in bufs)]
+    return PreparedCall((_lib or load_library()).epdc_combine, args, (cfg, bufs))
+
+
+def prepare_combine_push(cfg: EpCfg, numTokens: int, y, recvExpertIds, recvWeights, recvCount, landing,
+                         landScale) -> PreparedCall:
+    bufs = (y, recvExpertIds, recvWeights, recvCount, landing, landScale)
+    args = [ctypes.byref(cfg), ctypes.c_int32(int(numTokens)), *(_vp(b) for b in bufs)]
+    return PreparedCall((_lib or load_library()).epdc_combine_push, args, (cfg, bufs))
+
+
+def prepare_combine_reduce(cfg: EpCfg, numTokens: int, landing, landScale, recvCount, sendMap,
+                           out) -> PreparedCall:
+    bufs = (landing, landScale, recvCount, sendMap, out)
+    args = [ctypes.byref(cfg), ctypes.c_int32(int(numTokens)), *(_vp(b) for b in bufs)]
+    return PreparedCall((_lib or load_library()).epdc_combine_reduce, args, (cfg, bufs))

@@ -94,6 +94,27 @@ class DeviceRun:
                                         self.landScale if w.useWeights else None, self.recvCount, self.sendMap,
                                         self.out, stream=stream)
 
+    def prepare(self):
+        """Prepared calls (arguments marshalled once) for the same buffers:
+        self.p_dispatch, p_combine and, once landing rows exist, p_push and
+        p_reduce."""
+        w = self.w
+        wt = self.wts if w.useWeights else None
+        self.p_dispatch = epdc.prepare_dispatch(self.cfg, w.numTokens, self.x, self.ids, wt, self.recvX,
+                                                self.recvTokIdx, self.recvExpertIds,
+                                                self.recvWeights if w.useWeights else None, self.recvCount,
+                                                self.sendMap, self.scratch)
+        self.p_combine = epdc.prepare_combine(self.ccfg, w.numTokens, self.y, self.ids, wt, self.sendMap, self.out)
+        if hasattr(self, "landing"):
+            self.p_push = epdc.prepare_combine_push(self.ccfg, w.numTokens, self.y,
+                                                    self.recvExpertIds if w.useWeights else None,
+                                                    self.recvWeights if w.useWeights else None, self.recvCount,
+                                                    self.landing, self.landScale if w.useWeights else None)
+            self.p_reduce = epdc.prepare_combine_reduce(self.ccfg, w.numTokens, self.landing,
+                                                        self.landScale if w.useWeights else None, self.recvCount,
+                                                        self.sendMap, self.out)
+        return self
+
     def scratch_clean(self) -> bool:
         """After a dispatch the scratch is all zero again (error flag included)."""
         return bool((self.scratch == 0).all().item())

@@ -252,3 +252,25 @@ def test_zero_tokens_needs_only_recvcount_without_gpu():
              recvWeights=None, sendMap=None, scratch=None, scratchBytes=0)
     assert _dispatch(cfg(), 0, **n) == -7  # passes the checks, then no device
     assert _combine(cfg(), 0, y=None, expertIds=None, weights=None, sendMap=None, out=None) == 0
+
+
+def test_prepared_calls_check_like_direct_calls():
+    """A prepared call returns what the direct call returns: the host checks'
+    codes for bad arguments, and (on a host with no GPU) EPDC_ERR_HIP for
+    good ones."""
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("host without a GPU only")
+    ptrs = [P16] * 10
+    bad = epdc.prepare_dispatch(cfg(), 4097, *ptrs, scratchBytes=1 << 20)
+    assert bad(stream=0, check=False) == -3
+    mis = epdc.prepare_dispatch(cfg(), 8, P16 + 8, *ptrs[1:], scratchBytes=1 << 20)
+    assert mis(stream=0, check=False) == -4
+    with pytest.raises(epdc.EpdcError):
+        mis(stream=0)
+    assert epdc.prepare_dispatch(cfg(), 8, *ptrs, scratchBytes=1 << 20)(stream=0, check=False) == -7
+    assert epdc.prepare_combine(cfg(dtype=2), 8, *[P16] * 5)(stream=0, check=False) == -2
+    assert epdc.prepare_combine(cfg(), 8, *[P16] * 5)(stream=0, check=False) == -7
+    assert epdc.prepare_combine_push(cfg(), 8, *[P16] * 6)(stream=0, check=False) == -7
+    assert epdc.prepare_combine_reduce(cfg(), 8, *[P16] * 5)(stream=0, check=False) == -7
+    assert epdc.prepare_combine_reduce(cfg(), 8, P16, None, P16, P16, P16)(stream=0, check=False) == -5

@@ -278,3 +278,42 @@ def test_non_finite_rows(combine_dtype):
         gb = got.view(eb.dtype)
         bad = (gb != eb) & ~nan
         assert not bad.any(), f"{what}: {int(bad.sum())} non-NaN results differ from the oracle"
+
+
+def test_prepared_calls_match_direct_calls():
+    """Prepared calls (arguments marshalled once) write exactly what the
+    direct calls write, for all four entry points."""
+    w = workloads.CONFIGS["pr_scale"]
+    inp = workloads.cached_inputs("pr_scale", 3)
+    g = DeviceRun(w, inp)
+    g.alloc_landing()
+    g.dispatch()
+    g.combine()
+    torch.cuda.synchronize()
+    gather = g.out.clone()
+    g.push()
+    g.reduce()
+    torch.cuda.synchronize()
+    ref = {k: getattr(g, k).clone() for k in ("recvX", "recvTokIdx", "recvExpertIds", "recvWeights", "recvCount",
+                                              "sendMap", "landing", "landScale", "out")}
+    for k in ("recvX", "recvTokIdx", "recvExpertIds", "recvWeights", "sendMap", "landing", "landScale", "out"):
+        getattr(g, k).fill_(0)
+    g.prepare()
+    g.p_dispatch()
+    g.p_combine()
+    torch.cuda.synchronize()
+    assert torch.equal(g.out, gather), "prepared combine differs"
+    g.p_push()
+    g.p_reduce()
+    torch.cuda.synchronize()
+    for k, v in ref.items():
+        if k in ("recvX", "recvTokIdx", "recvExpertIds", "recvWeights"):  # rows past recvCount were zeroed
+            cnt = g.recvCount.cpu().tolist()
+            for p_, c in enumerate(cnt):
+                assert torch.equal(getattr(g, k)[p_, :c], v[p_, :c]), f"prepared dispatch differs: {k}"
+        elif k in ("landing", "landScale"):
+            U = int(g.recvCount.sum().item())
+            assert torch.equal(getattr(g, k)[:U], v[:U]), f"prepared push differs: {k}"
+        else:
+            assert torch.equal(getattr(g, k), v), f"prepared call differs: {k}"
+    assert g.scratch_clean()
