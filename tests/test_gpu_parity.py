@@ -197,7 +197,13 @@ def test_dirty_scratch_is_flagged_and_stays_in_bounds():
     bx, bt = big_x.cpu().numpy(), big_t.cpu().numpy()
     assert (bx[:guard] == 0x5A).all() and (bx[guard + W * M:] == 0x5A).all(), "recvX guard rows written"
     assert (bt[:guard] == -424242).all() and (bt[guard + W * M:] == -424242).all(), "recvTokIdx guard written"
-    assert int(g.scratch[2].item()) != 0, "a dirty scratch was not flagged in the error word"
+    # Whether a block reads garbage before the real value is published is a
+    # race; every garbage base here puts some row outside [0, M) (0x7FFFFFEF
+    # per count, so any sum is huge or negative), so wrong outputs are flagged.
+    o = oracle_dispatch(w, inp)
+    same = (np.array_equal(g.sendMap.cpu().numpy(), o.sendMap)
+            and np.array_equal(g.recvCount.cpu().numpy(), o.recvCount))
+    assert same or int(g.scratch[2].item()) != 0, "wrong outputs from a dirty scratch were not flagged"
 
 
 GRAPH_CASES = [
