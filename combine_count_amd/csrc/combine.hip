@@ -173,7 +173,11 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineParams P, int nSlab
     // and the group is straight-line code, so each wait is for exactly one
     // row.  kGroup bounds the registers held by in-flight rows (and so sets
     // the occupancy).
-    constexpr int kGroup = EPDC_COMBINE_GROUP;
+    // The reduce over landing rows keeps groups of 4 (occupancy 6): on Zipf
+    // routing (~3 PEs per token) it is 5% faster than with 8, though 6%
+    // slower when tokens reach ~5 PEs (uniform routing); the gather is even
+    // on the former and gains on the latter with 8.
+    constexpr int kGroup = LAND ? 4 : EPDC_COMBINE_GROUP;
     uint64_t rem = kept;
     while (rem) {
         int32_t fl[8];
