@@ -51,7 +51,10 @@ extern "C" {
  * and the one-byte fp8 and fp4x2 (for fp4x2 one element is a byte holding
  * two e2m1 values, so hiddenDim counts bytes).  Combine sums rows, so it
  * takes only EPDC_BF16 and EPDC_FP32.  A narrow-wire pair (fp8 or fp4x2
- * dispatch, bf16 combine) is two calls with two cfgs. */
+ * dispatch, bf16 combine) is two calls with two cfgs.  Per-token or per-block
+ * quantisation scales of a narrow-wire row can travel in the row itself:
+ * append their bytes to it (hiddenDim then counts them too; the row only has
+ * to stay a multiple of 16 bytes). */
 typedef enum {
     EPDC_BF16 = 0,
     EPDC_FP32 = 1,

@@ -114,6 +114,8 @@ DTYPES = [
     ("fp4x2_wire_ragged", None, "fp4x2", "bf16"),
     ("fp32_both_ragged", None, "fp32", "fp32"),
     ("fp8_wire_large", "large_weighted", "fp8", "bf16"),
+    # fp8 rows carrying their scales: 7168 e4m3 values + 56 fp32 block scales = 7392 bytes
+    ("fp8_rows_with_block_scales", "gen_zipf_h7168", "fp8", "bf16"),
 ]
 
 
@@ -126,7 +128,26 @@ def test_dtype_parity(case):
         w = workloads.Workload(name, 5, 3, 700, 650, 7, 1056, "uniform", 1, wire=wire, combineDtype=comb)
     else:
         w = workloads.CONFIGS[base].with_(name=name, wire=wire, combineDtype=comb)
-    _check_case(w, workloads.make_inputs(w, 4), name)
+    inp = workloads.make_inputs(w, 4)
+    if name == "fp8_rows_with_block_scales":
+        # the dispatch side only: rows are the fp8 payload with its scales appended
+        rng = np.random.Generator(np.random.PCG64(17))
+        scales = rng.uniform(0.01, 2.0, size=(w.numTokens, 56)).astype(np.float32)
+        x = np.concatenate([inp.x, scales.view(np.uint8)], axis=1)
+        w = w.with_(hiddenDim=x.shape[1])
+        inp = dataclasses.replace(inp, w=w, x=x)
+        g = DeviceRun(w, inp)
+        g.dispatch()
+        torch.cuda.synchronize()
+        o = oracle_dispatch(w, inp)
+        assert_dispatch_equal(g, o, name)
+        got = g.recvX.cpu().numpy()[..., 7168:].copy().view(np.float32)
+        for p_ in range(w.worldSize):
+            c = int(o.recvCount[p_])
+            tok = o.recvTokIdx[p_, :c]
+            assert np.array_equal(got[p_, :c], scales[tok]), "forwarded scales differ"
+        return
+    _check_case(w, inp, name)
 
 
 def test_invalid_expert_ids():
