@@ -159,7 +159,8 @@ __device__ __forceinline__ void store_token(const DispatchParams &P, const u32x4
 //      tile's other blocks wait for that single line (so polling traffic
 //      does not grow with the number of blocks per tile).
 //   3. Loads: the slab-0 waves' metadata rows, then every wave's NTW x
-//      slabs (after the SCAN by default: EPDC_DISPATCH_XLOAD_PHASE).
+//      slabs (with xEarly, the x slabs go out before COUNT instead; see
+//      launch_fused).
 //   4. FINALIZE: one wait for the wave's loads, then every store of its NTW
 //      tokens to every destination, with no further wait (vmcnt is one
 //      in-order counter for loads and stores on this ISA, so waiting on a
@@ -170,7 +171,8 @@ __device__ __forceinline__ void store_token(const DispatchParams &P, const u32x4
 //      counters wrap to zero by themselves, so the scratch is zero again for
 //      the next call (and for every replay of a captured graph).
 template <int CPW, int NTW, bool FULL, bool LOCAL>
-__global__ __launch_bounds__(256) void dispatch_kernel(DispatchParams P, int nSlabs, int nSubs, int nBlocks) {
+__global__ __launch_bounds__(256) void dispatch_kernel(DispatchParams P, int nSlabs, int nSubs, int nBlocks,
+                                                            int xEarly) {
     __shared__ uint64_t sMask[kTile];  // destination-PE set of each token of the tile
     __shared__ uint64_t sBal[64];      // per PE: which tokens of the tile go there
     __shared__ int32_t sPre[64];       // per PE: rows taken by earlier tiles
@@ -236,7 +238,7 @@ __global__ __launch_bounds__(256) void dispatch_kernel(DispatchParams P, int nSl
     if constexpr (localScan) {
         load_x();
         load_meta();
-    } else if (EPDC_DISPATCH_XLOAD_PHASE == 0) {
+    } else if (xEarly) {
         load_x();
     }
 
@@ -257,8 +259,6 @@ __global__ __launch_bounds__(256) void dispatch_kernel(DispatchParams P, int nSl
             __hip_atomic_store(published + (int64_t)tile * P.Wp + lane, (uint32_t)cnt + 1u, __ATOMIC_RELAXED,
                                __HIP_MEMORY_SCOPE_AGENT);
     }
-
-    if constexpr (!localScan && EPDC_DISPATCH_XLOAD_PHASE == 1) load_x();
 
     // 3. SCAN: exclusive base of this tile on each PE.  The leader sums the
     // published counts of all earlier tiles (the row stride Wp is a power of
@@ -305,14 +305,14 @@ __global__ __launch_bounds__(256) void dispatch_kernel(DispatchParams P, int nSl
     }
     __syncthreads();
 
-    // Scanning through the scratch, the metadata rows and then (by default)
-    // the x slabs are requested only now: issued before the SCAN, the x
-    // flood would delay the SCAN's own small reads.  Either way no wait
+    // Scanning through the scratch, the metadata rows and then (without
+    // xEarly) the x slabs are requested only now: issued before the SCAN, the
+    // x flood would delay the SCAN's own small reads.  Either way no wait
     // below follows a store.
     const int32_t E = P.W * P.Epr;
     if constexpr (!localScan) {
         load_meta();
-        if (EPDC_DISPATCH_XLOAD_PHASE == 2) load_x();
+        if (!xEarly) load_x();
     }
 
     // 4. FINALIZE payload: one wait for every load above, then only stores.
@@ -395,19 +395,26 @@ hipError_t launch_fused(const DispatchParams &P, int nTiles, hipStream_t stream)
     const int nBlocks = (int)blocks;
     const bool full = P.rowBytes % kChunkBytes == 0 && P.nChunks % CPW == 0;
     const dim3 grid(nBlocks);
+    // x before COUNT in launches of more blocks than the chip holds at once
+    // (~7 per CU): blocks that start once HBM is saturated would otherwise
+    // idle through the SCAN's round trips, each queued behind streaming
+    // traffic.  While every block fits, the early x flood delays the SCAN
+    // instead.  Measured crossover: between 2048 blocks (after the SCAN 2-5%
+    // faster) and 4096 (before COUNT 8-10% faster).
+    const int xEarly = nBlocks > EPDC_DISPATCH_XEARLY_BLOCKS ? 1 : 0;
     if (nTiles <= EPDC_DISPATCH_LOCAL_SCAN_TILES) {
         if (full)
             hipLaunchKernelGGL((dispatch_kernel<CPW, NTW, true, true>), grid, dim3(256), 0, stream, P, nSlabs, nSubs,
-                               nBlocks);
+                               nBlocks, xEarly);
         else
             hipLaunchKernelGGL((dispatch_kernel<CPW, NTW, false, true>), grid, dim3(256), 0, stream, P, nSlabs,
-                               nSubs, nBlocks);
+                               nSubs, nBlocks, xEarly);
     } else if (full) {
         hipLaunchKernelGGL((dispatch_kernel<CPW, NTW, true, false>), grid, dim3(256), 0, stream, P, nSlabs, nSubs,
-                           nBlocks);
+                           nBlocks, xEarly);
     } else {
         hipLaunchKernelGGL((dispatch_kernel<CPW, NTW, false, false>), grid, dim3(256), 0, stream, P, nSlabs, nSubs,
-                           nBlocks);
+                           nBlocks, xEarly);
     }
     return hipGetLastError();
 }

@@ -62,8 +62,8 @@ __device__ __forceinline__ void wait_vmcnt() {
 #ifndef EPDC_DISPATCH_NTW
 #define EPDC_DISPATCH_NTW 0  // tokens per wave; 0: chosen from the shape
 #endif
-#ifndef EPDC_DISPATCH_XLOAD_PHASE
-#define EPDC_DISPATCH_XLOAD_PHASE 2  // 0: x loads before COUNT, 1: after publishing, 2: after SCAN
+#ifndef EPDC_DISPATCH_XEARLY_BLOCKS
+#define EPDC_DISPATCH_XEARLY_BLOCKS 3072  // launches of more blocks request x before COUNT
 #endif
 #ifndef EPDC_DISPATCH_LOCAL_SCAN_TILES
 #define EPDC_DISPATCH_LOCAL_SCAN_TILES 8  // launches of up to this many 64-token tiles scan in every block

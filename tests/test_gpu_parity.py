@@ -94,6 +94,8 @@ EDGE = [
     ("ragged_rows_1p5k", 4, 8, 300, 257, 5, 768, "uniform", 1),
     ("ragged_rows_5p5k", 8, 16, 300, 300, 8, 2816, "zipf", 1),
     ("ragged_rows_9p5k", 8, 16, 200, 130, 8, 4864, "uniform", 0),
+    # ragged rows in a launch of more than 3072 blocks (x requested before COUNT)
+    ("ragged_rows_x_early_t13000", 8, 16, 13000, 13000, 8, 2816, "uniform", 1),
 ]
 
 
@@ -109,6 +111,7 @@ DTYPES = [
     ("fp8_wire_bf16_combine_h7168", "gen_zipf_h7168", "fp8", "bf16"),
     ("fp4x2_wire_bf16_combine_h7168", "gen_zipf_h7168", "fp4x2", "bf16"),
     ("fp32_both_pr_scale", "pr_scale", "fp32", "fp32"),
+    ("fp32_both_h7168", "gen_zipf_h7168", "fp32", "fp32"),  # 4096 dispatch blocks: x before COUNT
     ("bf16_wire_fp32_combine_defaults", "epcfg_defaults", "bf16", "fp32"),
     ("fp8_wire_fp32_combine_tiny", "tiny", "fp8", "fp32"),
     ("fp4x2_wire_ragged", None, "fp4x2", "bf16"),
