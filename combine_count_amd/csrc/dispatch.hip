@@ -395,12 +395,12 @@ hipError_t launch_fused(const DispatchParams &P, int nTiles, hipStream_t stream)
     const int nBlocks = (int)blocks;
     const bool full = P.rowBytes % kChunkBytes == 0 && P.nChunks % CPW == 0;
     const dim3 grid(nBlocks);
-    // x before COUNT in launches of more blocks than the chip holds at once
-    // (~7 per CU): blocks that start once HBM is saturated would otherwise
-    // idle through the SCAN's round trips, each queued behind streaming
-    // traffic.  While every block fits, the early x flood delays the SCAN
-    // instead.  Measured crossover: between 2048 blocks (after the SCAN 2-5%
-    // faster) and 4096 (before COUNT 8-10% faster).
+    // x before COUNT in launches of well over one round of resident blocks
+    // (about 7 per CU, 1792 on the chip): blocks that start once HBM is
+    // saturated would otherwise idle through the SCAN's round trips, each
+    // queued behind streaming traffic.  In smaller launches the early x flood
+    // delays the SCAN instead.  Measured crossover: between 2048 blocks (after
+    // the SCAN 2-5% faster) and 4096 (before COUNT 8-10% faster).
     const int xEarly = nBlocks > EPDC_DISPATCH_XEARLY_BLOCKS ? 1 : 0;
     if (nTiles <= EPDC_DISPATCH_LOCAL_SCAN_TILES) {
         if (full)

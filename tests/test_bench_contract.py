@@ -29,3 +29,18 @@ def test_algorithmic_bytes_of_the_default_workload():
     p, r = bench.push_bytes(w, U)
     assert p == 2 * U * row + U * K * 8 + U * 4 + W * 4
     assert r == T * K * 4 + W * 4 + U * row + U * 4 + T * row
+
+
+def test_kernel_hash_ignores_comments_but_not_code(tmp_path, monkeypatch):
+    """The counters' validity key: a comment or layout edit keeps it, a code
+    edit changes it."""
+    sys.path.insert(0, ROOT)
+    import bench
+    src = tmp_path / "k.hip"
+    monkeypatch.setattr(bench, "KERNEL_SOURCES", [str(src)])
+    src.write_text("int f(int a) { return a + 1; }  // add one\n")
+    h0 = bench.kernel_source_hash()
+    src.write_text("/* a block\n comment */\nint f(int a) {\n    return a + 1;  // plus one\n}\n")
+    assert bench.kernel_source_hash() == h0
+    src.write_text("int f(int a) { return a + 2; }  // add one\n")
+    assert bench.kernel_source_hash() != h0
