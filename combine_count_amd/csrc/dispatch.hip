@@ -26,18 +26,37 @@ namespace {
 constexpr bool kNtLoad = EPDC_DISPATCH_NT_LOAD;
 constexpr bool kNtStore = EPDC_DISPATCH_NT_STORE;
 
-__device__ __forceinline__ int32_t dest_pe(int32_t e, int32_t E, int32_t Epr, int32_t eprShift) {
-    if (e < 0 || e >= E) return -1;
-    return eprShift >= 0 ? (e >> eprShift) : (e / Epr);
+// PE of expert e (-1 if e is not an expert id): e / Epr by multiply-high
+// (div_magic), a few instructions for any Epr.
+__device__ __forceinline__ int32_t dest_pe(const DispatchParams &P, int32_t e, int32_t E) {
+    if ((uint32_t)e >= (uint32_t)E) return -1;
+    const uint32_t t = __umulhi((uint32_t)e, P.eprMagic);
+    return (int32_t)((t + (((uint32_t)e - t) >> P.eprSh1)) >> P.eprSh2);
 }
 
-// Destination-PE set of token t (bit p set iff some valid slot of t is on p).
-__device__ __forceinline__ uint64_t token_pe_mask(const DispatchParams &P, int32_t t) {
-    const int32_t E = P.W * P.Epr;
+// Expert ids of token t in slots 0..7, requested together (slots past K
+// repeat slot K-1, which leaves the token's PE set unchanged): a tile's ids
+// then cost one memory round trip instead of one per slot.
+__device__ __forceinline__ void load_ids(const DispatchParams &P, int32_t t, int32_t (&v)[8]) {
     const int32_t *ids = P.expertIds + (int64_t)t * P.K;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) v[k] = ids[min(k, P.K - 1)];
+}
+
+// Destination-PE set of token t (bit p set iff some valid slot of t is on p)
+// from its ids as load_ids requested them; slots 8.. (topk above 8) are read
+// here.
+__device__ __forceinline__ uint64_t pe_mask(const DispatchParams &P, const int32_t (&v)[8], int32_t t) {
+    const int32_t E = P.W * P.Epr;
     uint64_t m = 0;
-    for (int k = 0; k < P.K; ++k) {
-        int32_t p = dest_pe(ids[k], E, P.Epr, P.eprShift);
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+        const int32_t p = dest_pe(P, v[k], E);
+        if (p >= 0) m |= 1ull << p;
+    }
+    const int32_t *ids = P.expertIds + (int64_t)t * P.K;
+    for (int k = 8; k < P.K; ++k) {
+        const int32_t p = dest_pe(P, ids[k], E);
         if (p >= 0) m |= 1ull << p;
     }
     return m;
@@ -151,7 +170,8 @@ __device__ __forceinline__ void store_token(const DispatchParams &P, const u32x4
 // [slab*CPW, (slab+1)*CPW).
 //   0. Launches of at most EPDC_DISPATCH_LOCAL_SCAN_TILES tiles request all
 //      their loads first and scan locally (step 2); the others:
-//   1. COUNT (wave 0): the tile's PE masks and per-PE ballots; the tile's
+//   1. COUNT (wave 0): the tile's PE masks (each lane's ids requested
+//      together) and per-PE ballots; the tile's
 //      leader (its first block: sub 0, slab 0) publishes the per-PE counts
 //      as count+1.
 //   2. SCAN: the leader sums the published counts of all earlier tiles into
@@ -235,11 +255,25 @@ __global__ __launch_bounds__(256) void dispatch_kernel(DispatchParams P, int nSl
             }
         }
     };
+    // The ids COUNT reads (wave 0: a token of the tile per lane) and, for a
+    // local scan, those of the earlier tiles this wave counts (tiles wave,
+    // wave + 4, ...; all full) go out before the local scan's x slabs, so
+    // counting waits for them alone (one round trip where a scan is a chain
+    // of them).  With xEarly the x slabs go out first: there the blocks that
+    // count sooner only reach the SCAN's wait sooner and poll it longer
+    // (measured 1% slower at 16384 tokens).
+    constexpr int kScanPerWave = (EPDC_DISPATCH_LOCAL_SCAN_TILES + 2) / 4 > 0
+                                     ? (EPDC_DISPATCH_LOCAL_SCAN_TILES + 2) / 4 : 1;
+    int32_t idOwn[8];
+    int32_t idScan[kScanPerWave][8];
+    if (!localScan && xEarly) load_x();
+    if (wave == 0) load_ids(P, tok0 + min(lane, nTok - 1), idOwn);
     if constexpr (localScan) {
+#pragma unroll
+        for (int i = 0; i < kScanPerWave; ++i)
+            if (wave + 4 * i < tile) load_ids(P, (wave + 4 * i) * kTile + lane, idScan[i]);
         load_x();
         load_meta();
-    } else if (xEarly) {
-        load_x();
     }
 
     // 2. COUNT for this tile (wave 0); the tile's leader block (sub 0,
@@ -247,7 +281,7 @@ __global__ __launch_bounds__(256) void dispatch_kernel(DispatchParams P, int nSl
     const bool leader = (sub == 0 && slab == 0);
     if (wave == 0) {
         const int32_t t = tok0 + lane;
-        const uint64_t m = (lane < nTok) ? token_pe_mask(P, t) : 0ull;
+        const uint64_t m = (lane < nTok) ? pe_mask(P, idOwn, t) : 0ull;
         sMask[lane] = m;
         int cnt = 0;
         for (int p = 0; p < P.W; ++p) {
@@ -268,8 +302,12 @@ __global__ __launch_bounds__(256) void dispatch_kernel(DispatchParams P, int nSl
     // local scan counts the earlier tiles (all full) in this block instead,
     // the 4 waves taking tiles wave, wave + 4, ...
     if constexpr (localScan) {
-        for (int j = wave; j < tile; j += 4) {
-            const uint64_t m = token_pe_mask(P, j * kTile + lane);
+        static_assert(4 * kScanPerWave >= EPDC_DISPATCH_LOCAL_SCAN_TILES - 1, "every earlier tile has a wave");
+#pragma unroll
+        for (int i = 0; i < kScanPerWave; ++i) {
+            const int j = wave + 4 * i;
+            if (j >= tile) break;
+            const uint64_t m = pe_mask(P, idScan[i], j * kTile + lane);
             for (int p = 0; p < P.W; ++p) {
                 const uint64_t bal = __ballot((m >> p) & 1ull);
                 if (lane == p && bal) atomicAdd(&sPre[p], (int32_t)__popcll(bal));
@@ -331,7 +369,7 @@ __global__ __launch_bounds__(256) void dispatch_kernel(DispatchParams P, int nSl
             const int i = iBeg + j;
             if (i < nTok) {
                 const int32_t t = tok0 + i;
-                const int32_t pe = dest_pe(mid[j], E, P.Epr, P.eprShift);
+                const int32_t pe = dest_pe(P, mid[j], E);
                 int32_t flat = -1;
                 uint64_t m = uniform64(sMask[i]);
                 const uint64_t lt = lanemask_lt(i);
@@ -402,14 +440,22 @@ hipError_t launch_fused(const DispatchParams &P, int nTiles, hipStream_t stream)
     // delays the SCAN instead.  Measured crossover: between 2048 blocks (after
     // the SCAN 2-5% faster) and 4096 (before COUNT 8-10% faster).
     const int xEarly = nBlocks > EPDC_DISPATCH_XEARLY_BLOCKS ? 1 : 0;
-    if (nTiles <= EPDC_DISPATCH_LOCAL_SCAN_TILES) {
-        if (full)
-            hipLaunchKernelGGL((dispatch_kernel<CPW, NTW, true, true>), grid, dim3(256), 0, stream, P, nSlabs, nSubs,
-                               nBlocks, xEarly);
-        else
-            hipLaunchKernelGGL((dispatch_kernel<CPW, NTW, false, true>), grid, dim3(256), 0, stream, P, nSlabs,
-                               nSubs, nBlocks, xEarly);
-    } else if (full) {
+    // The local scan is built for one token per wave only: more tokens per
+    // wave within 8 tiles takes over 128 slabs per row (rows of 128 KiB and
+    // up), and its id registers would then cost occupancy; such launches scan
+    // through the scratch.
+    if constexpr (NTW == 1) {
+        if (nTiles <= EPDC_DISPATCH_LOCAL_SCAN_TILES) {
+            if (full)
+                hipLaunchKernelGGL((dispatch_kernel<CPW, NTW, true, true>), grid, dim3(256), 0, stream, P, nSlabs,
+                                   nSubs, nBlocks, xEarly);
+            else
+                hipLaunchKernelGGL((dispatch_kernel<CPW, NTW, false, true>), grid, dim3(256), 0, stream, P, nSlabs,
+                                   nSubs, nBlocks, xEarly);
+            return hipGetLastError();
+        }
+    }
+    if (full) {
         hipLaunchKernelGGL((dispatch_kernel<CPW, NTW, true, false>), grid, dim3(256), 0, stream, P, nSlabs, nSubs,
                            nBlocks, xEarly);
     } else {

@@ -157,7 +157,10 @@ int epdc_dispatch(const epdc_cfg *cfg, int32_t numTokens, const void *x, const i
         P.T = numTokens;
         P.useWeights = cfg->useWeights;
         P.Wp = pow2_ceil(cfg->worldSize);
-        P.eprShift = log2_exact(cfg->numExpertPerRank);
+        const epdc::DivMagic dm = epdc::div_magic((uint32_t)cfg->numExpertPerRank);
+        P.eprMagic = dm.magic;
+        P.eprSh1 = dm.sh1;
+        P.eprSh2 = dm.sh2;
         P.rowBytes = cfg->hiddenDim * elem_bytes(cfg->dtype, false);
         P.nChunks = epdc::ceil_div(P.rowBytes, epdc::kChunkBytes);
         P.x = static_cast<const uint8_t *>(x);

@@ -109,7 +109,9 @@ struct DispatchParams {
     int32_t W, H, M, Epr, K, T, useWeights;
     int32_t rowBytes;  // H * element size of the wire dtype (a multiple of 16)
     int32_t Wp;        // W rounded up to a power of two (tile-count row stride)
-    int32_t eprShift;  // log2(Epr) when Epr is a power of two, else -1
+    // e / Epr for any 32-bit e without a divide (div_magic): magic, shifts
+    uint32_t eprMagic;
+    int32_t eprSh1, eprSh2;
     int32_t nChunks;   // ceil(rowBytes / kChunkBytes)
     const uint8_t *x;
     const int32_t *expertIds;
@@ -165,6 +167,23 @@ struct PushParams {
 };
 
 __host__ __device__ inline int32_t ceil_div(int64_t a, int64_t b) { return (int32_t)((a + b - 1) / b); }
+
+// Unsigned division by an invariant d >= 1 with one multiply-high (Granlund
+// and Montgomery, "Division by invariant integers using multiplication",
+// PLDI 1994, the unsigned case for N = 32): with l = ceil(log2 d),
+// magic = floor(2^32 (2^l - d) / d) + 1 (it fits 32 bits), sh1 = min(l, 1)
+// and sh2 = max(l - 1, 0), every 32-bit n has
+// n / d = (t + ((n - t) >> sh1)) >> sh2 where t = umulhi(n, magic).
+struct DivMagic {
+    uint32_t magic;
+    int32_t sh1, sh2;
+};
+inline DivMagic div_magic(uint32_t d) {
+    int l = 0;
+    while ((1ull << l) < d) ++l;
+    const uint64_t m = (((uint64_t)1 << 32) * (((uint64_t)1 << l) - d)) / d + 1;
+    return DivMagic{(uint32_t)m, l < 1 ? l : 1, l > 1 ? l - 1 : 0};
+}
 
 // Launchers: enqueue on `stream`, return the hipGetLastError() after launch.
 hipError_t launch_dispatch(const DispatchParams &p, hipStream_t stream);

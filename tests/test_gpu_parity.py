@@ -82,6 +82,9 @@ EDGE = [
     ("t40000_h512", 8, 32, 40000, 40000, 8, 512, "uniform", 0),
     ("two_tokens_per_wave_t6000", 2, 4, 6000, 6000, 4, 5632, "uniform", 1),
     ("four_tokens_per_wave_t12000", 2, 4, 12000, 11990, 3, 5632, "zipf", 0),
+    # 8 tiles (local-scan range) but 131 one-chunk slabs per row: two tokens per wave, so the
+    # scan goes through the scratch
+    ("two_tokens_per_wave_8_tiles_h67072", 2, 4, 512, 512, 4, 67072, "uniform", 1),
     ("slab2_h1024", 8, 32, 700, 700, 8, 1024, "zipf", 0),
     # combine in 2-chunk slabs with bound checks (5.5 KiB rows, 4000 tokens x 3 slabs)
     ("combine_slab2_ragged_t4000", 4, 8, 4000, 4000, 6, 2816, "zipf", 1),
