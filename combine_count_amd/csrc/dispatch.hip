@@ -438,7 +438,7 @@ hipError_t launch_fused(const DispatchParams &P, int nTiles, hipStream_t stream)
     // saturated would otherwise idle through the SCAN's round trips, each
     // queued behind streaming traffic.  In smaller launches the early x flood
     // delays the SCAN instead.  Measured crossover: between 2048 blocks (after
-    // the SCAN 2-5% faster) and 4096 (before COUNT 8-10% faster).
+    // the SCAN 1-3% faster) and 3072 (before COUNT 4% faster; 8-10% at 4096).
     const int xEarly = nBlocks > EPDC_DISPATCH_XEARLY_BLOCKS ? 1 : 0;
     // The local scan is built for one token per wave only: more tokens per
     // wave within 8 tiles takes over 128 slabs per row (rows of 128 KiB and

@@ -63,7 +63,7 @@ __device__ __forceinline__ void wait_vmcnt() {
 #define EPDC_DISPATCH_NTW 0  // tokens per wave; 0: chosen from the shape
 #endif
 #ifndef EPDC_DISPATCH_XEARLY_BLOCKS
-#define EPDC_DISPATCH_XEARLY_BLOCKS 3072  // launches of more blocks request x before COUNT
+#define EPDC_DISPATCH_XEARLY_BLOCKS 2560  // launches of more blocks request x before COUNT
 #endif
 #ifndef EPDC_DISPATCH_LOCAL_SCAN_TILES
 #define EPDC_DISPATCH_LOCAL_SCAN_TILES 8  // launches of up to this many 64-token tiles scan in every block
