@@ -156,9 +156,20 @@ def test_dtype_parity(case):
     _check_case(w, inp, name)
 
 
-def test_invalid_expert_ids():
+INVALID = [
+    # name, W, Epr, K: power-of-two and other experts per rank; topk above 8 (the ids past
+    # slot 8 are read one by one)
+    ("pow2_epr", 8, 4, 6),
+    ("epr5_w6", 6, 5, 6),
+    ("epr3_k10", 5, 3, 10),
+]
+
+
+@pytest.mark.parametrize("case", INVALID, ids=[c[0] for c in INVALID])
+def test_invalid_expert_ids(case):
     """Ids outside [0, E) are dropped slots: null entry, no row, no weight."""
-    w = workloads.Workload("invalid_ids", 8, 4, 256, 250, 6, 1024, "uniform", 1)
+    name, W, Epr, K = case
+    w = workloads.Workload(f"invalid_ids_{name}", W, Epr, 256, 250, K, 1024, "uniform", 1)
     inp = workloads.make_inputs(w, 9)
     rng = np.random.Generator(np.random.PCG64(99))
     ids = inp.expertIds.copy()
@@ -168,7 +179,7 @@ def test_invalid_expert_ids():
     ids[mask] = bad[mask].astype(np.int32)
     ids[3, :] = -1  # a token with no valid slot combines to +0
     inp = dataclasses.replace(inp, expertIds=ids)
-    _check_case(w, inp, "invalid_ids")
+    _check_case(w, inp, w.name)
 
 
 DEGENERATE = ["all_to_one_pe", "all_slots_invalid", "all_to_every_pe", "half_tokens_invalid"]
