@@ -19,11 +19,12 @@
 //   * lanes < W load recvCount; a wave scan gives every PE's landing offset
 //     and the number of landed rows U; waves past U exit;
 //   * a ballot over the offsets names the window the row comes from;
-//   * slab-0 waves of a weighted call load the row's K expert ids and weights
-//     (the metadata the dispatch delivered with it) and forward the scale:
-//     the fp32 sum, in slot order from +0, of the weights whose expert lives
-//     on this PE -- the gather combine's scale for that PE;
-//   * the slab is loaded, 16 bytes per lane per chunk, then stored.
+//   * the slab is requested, 16 bytes per lane per chunk, then (slab-0 waves
+//     of a weighted call) the row's K expert ids and weights, the metadata
+//     the dispatch delivered with it; the slab is stored;
+//   * those waves forward the scale: the fp32 sum, in slot order from +0, of
+//     the weights whose expert lives on this PE -- the gather combine's scale
+//     for that PE.
 #include "epdc_internal.h"
 
 namespace epdc {
@@ -52,16 +53,6 @@ __global__ __launch_bounds__(256) void push_kernel(PushParams P, int nSlabs) {
     const int32_t r = L - uniform(__shfl(incl - c, p));
     const int64_t src = (int64_t)p * P.M + r;
 
-    const bool doScale = P.useWeights && slab == 0;
-    int32_t pe = -1;
-    float w = 0.0f;
-    if (doScale && lane < P.K) {
-        const int64_t o = src * P.K + lane;
-        const int32_t e = P.recvExpertIds[o];
-        w = P.recvWeights[o];
-        if (e >= 0 && e < P.W * P.Epr) pe = P.eprShift >= 0 ? (e >> P.eprShift) : (e / P.Epr);
-    }
-
     const uint8_t *srow = P.y + src * P.rowBytes;
     uint8_t *drow = P.landing + (int64_t)L * P.rowBytes;
     // Every lane loads (a lane past the row's end reads the row's first 16
@@ -74,14 +65,26 @@ __global__ __launch_bounds__(256) void push_kernel(PushParams P, int nSlabs) {
         const int e = gc * kChunkBytes + lane * 16;
         v[k] = load16<EPDC_PUSH_NT_LOAD>(srow + ((FULL || (gc < P.nChunks && e < P.rowBytes)) ? e : 0));
     }
+    // The row's metadata goes out behind its slab, so nothing waits for it
+    // before the slab is requested.
+    const bool doScale = P.useWeights && slab == 0;
+    int32_t e = -1;
+    float w = 0.0f;
+    if (doScale && lane < P.K) {
+        const int64_t o = src * P.K + lane;
+        e = P.recvExpertIds[o];
+        w = P.recvWeights[o];
+    }
 #pragma unroll
     for (int k = 0; k < CPW; ++k) {
         const int gc = slab * CPW + k;
-        const int e = gc * kChunkBytes + lane * 16;
-        if (FULL || (gc < P.nChunks && e < P.rowBytes)) store16<EPDC_PUSH_NT_STORE>(drow + e, v[k]);
+        const int eb = gc * kChunkBytes + lane * 16;
+        if (FULL || (gc < P.nChunks && eb < P.rowBytes)) store16<EPDC_PUSH_NT_STORE>(drow + eb, v[k]);
     }
 
     if (doScale) {
+        int32_t pe = -1;
+        if (e >= 0 && e < P.W * P.Epr) pe = P.eprShift >= 0 ? (e >> P.eprShift) : (e / P.Epr);
         float s = 0.0f;
         for (int k = 0; k < P.K; ++k) {
             const int32_t pk = __shfl(pe, k);
