@@ -118,6 +118,29 @@ def read_traffic(kernel, workload):
         return None
 
 
+def stream_reference(torch, nbytes=1 << 30, launches=20):
+    """Plain streaming on the same GPU, for context beside the roofline: torch's
+    device copy (nbytes read + nbytes written) and fill (nbytes written), GB/s
+    over `launches` launches between two HIP events."""
+    src = torch.empty(nbytes, dtype=torch.uint8, device="cuda").random_(0, 255)
+    dst = torch.empty_like(src)
+    out = {}
+    for name, run, moved in (("copy", lambda: dst.copy_(src), 2 * nbytes), ("fill", lambda: dst.fill_(7), nbytes)):
+        for _ in range(3):
+            run()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(launches):
+            run()
+        e1.record()
+        torch.cuda.synchronize()
+        out[name] = round(moved * launches / e0.elapsed_time(e1) / 1e6, 1)
+    del src, dst
+    torch.cuda.empty_cache()
+    return out
+
+
 def cpu_baseline(w, inp, budget_s, step_bytes, push):
     import oracle
     step, _ = oracle.timed_step(w.worldSize, w.maxTokPerRank, w.numExpertPerRank, w.numExpertPerToken,
@@ -287,6 +310,10 @@ def main():
                 "traffic": read_traffic(dom, w.name),
                 "us_per_launch": round(dom_ms * 1e3, 2), "algorithmic_bytes_per_launch": dom_b}
 
+    ref = stream_reference(torch)
+    print(f"[bench] stream reference: copy {ref['copy']:.0f} GB/s, fill {ref['fill']:.0f} GB/s",
+          file=sys.stderr, flush=True)
+
     cpu = None
     if args.cpu_seconds > 0:
         print("[bench] timing the CPU oracle", file=sys.stderr, flush=True)
@@ -310,7 +337,9 @@ def main():
                    "step_us_hot": round(hot_ms * 1e3, 2),
                    "graph_replay_step_us": round(graph_ms * 1e3, 2),
                    "buffer_sets_rotated": len(sets), "scratch_clean": scratch_ok,
-                   "frac_of_hbm_peak": round(value / HBM_PEAK_GBPS, 4)})
+                   "frac_of_hbm_peak": round(value / HBM_PEAK_GBPS, 4),
+                   "stream_reference_GBps": dict(ref, what="torch copy_ (1 GiB read + 1 GiB written) and fill_ "
+                                                           "(1 GiB written) on the same GPU, 20 launches each")})
     line = {
         "metric": METRIC, "value": round(value, 1), "unit": "GB/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 5),
