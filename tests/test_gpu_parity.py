@@ -99,6 +99,23 @@ EDGE = [
     ("ragged_rows_9p5k", 8, 16, 200, 130, 8, 4864, "uniform", 0),
     # ragged rows in a launch of more than 2560 blocks (x requested before COUNT)
     ("ragged_rows_x_early_t13000", 8, 16, 13000, 13000, 8, 2816, "uniform", 1),
+    # further compiled dispatch variants (slab chunks, tokens per wave, bound checks, scan):
+    ("ragged_ntw2_t66000_h264", 2, 4, 66000, 66000, 2, 264, "uniform", 1),       # 1, 2, checked
+    ("ragged_ntw4_t132000_h264", 2, 4, 132000, 132000, 2, 264, "zipf", 0),       # 1, 4, checked
+    ("ntw2_cpw2_t13200_h5120", 2, 4, 13200, 13200, 3, 5120, "uniform", 1),       # 2, 2
+    ("ntw2_cpw4_t22000_h6144", 2, 4, 22000, 22000, 3, 6144, "uniform", 1),       # 4, 2
+    ("ntw2_cpw7_t11000_h21504", 2, 4, 11000, 11000, 2, 21504, "uniform", 1),     # 7, 2
+    ("ntw2_cpw8_t8300_h32768", 2, 4, 8300, 8300, 2, 32768, "zipf", 1),           # 8, 2
+    ("local_ragged_cpw4_t300_h1792", 4, 8, 300, 300, 5, 1792, "uniform", 1),     # 4, 1, checked, local
+    ("ragged_scan_t1000_h264", 4, 8, 1000, 1000, 5, 264, "uniform", 1),          # 1, 1, checked, scratch
+    ("ragged_ntw2_cpw2_t66000_h768", 2, 4, 66000, 66000, 2, 768, "uniform", 1),  # 2, 2, checked
+    ("ragged_ntw4_cpw2_t132000_h768", 2, 4, 132000, 132000, 2, 768, "zipf", 1),  # 2, 4, checked
+    ("ragged_ntw2_cpw4_t66000_h1792", 2, 4, 66000, 66000, 2, 1792, "uniform", 0),  # 4, 2, checked
+    ("ragged_ntw4_cpw4_t132000_h1792", 2, 4, 132000, 132000, 2, 1792, "uniform", 1),  # 4, 4, checked
+    ("ragged_ntw2_cpw7_t66000_h2816", 2, 4, 66000, 66000, 2, 2816, "zipf", 1),   # 7, 2, checked
+    ("ragged_ntw2_cpw8_t33000_h4864", 2, 4, 33000, 33000, 2, 4864, "uniform", 1),  # 8, 2, checked
+    ("ntw4_cpw2_t26300_h5120", 2, 4, 26300, 26300, 2, 5120, "uniform", 1),       # 2, 4
+    ("ntw4_cpw4_t43700_h6144", 2, 4, 43700, 43700, 2, 6144, "uniform", 1),       # 4, 4
 ]
 
 
