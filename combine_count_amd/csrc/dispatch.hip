@@ -487,11 +487,19 @@ hipError_t launch_dispatch(const DispatchParams &P, hipStream_t stream) {
 #if EPDC_DISPATCH_CPW != 0 && EPDC_DISPATCH_NTW != 0
     return launch_fused<EPDC_DISPATCH_CPW, EPDC_DISPATCH_NTW>(P, nTiles, stream);
 #else
-    // Slab width: the widest of 8/7/4/2 chunks that divides the row (a wave
-    // then moves up to 8 KiB of a token with no bound checks).  Other rows
-    // (not a whole number of 1 KiB chunks, e.g. 3.5 KiB fp4x2 rows at
-    // hidden 7168) take the narrowest of 1/2/4/7/8 chunks that covers the row
-    // (8 beyond that) with bound checks on the tail.
+    // Slab width.  Launches of at most EPDC_DISPATCH_NARROW_TILES tiles are
+    // bound by round trips, not bytes: 2-chunk slabs (1 for an odd chunk
+    // count) spread a token's stores over more waves (64 tokens x h7168:
+    // 4.9 -> 4.2 us).  Otherwise the widest of 8/7/4/2 chunks that divides
+    // the row (a wave then moves up to 8 KiB of a token with no bound
+    // checks); other rows (not a whole number of 1 KiB chunks, e.g. 3.5 KiB
+    // fp4x2 rows at hidden 7168) take the narrowest of 1/2/4/7/8 chunks that
+    // covers the row (8 beyond that) with bound checks on the tail.
+    if (nTiles <= EPDC_DISPATCH_NARROW_TILES) {
+        if (P.nChunks <= 1) return launch_cpw<1>(P, nTiles, stream);
+        if (P.rowBytes % kChunkBytes != 0 || P.nChunks % 2 == 0) return launch_cpw<2>(P, nTiles, stream);
+        return launch_cpw<1>(P, nTiles, stream);
+    }
     if (P.rowBytes % kChunkBytes == 0) {
         if (P.nChunks % 8 == 0) return launch_cpw<8>(P, nTiles, stream);
         if (P.nChunks % 7 == 0) return launch_cpw<7>(P, nTiles, stream);

@@ -65,6 +65,9 @@ __device__ __forceinline__ void wait_vmcnt() {
 #ifndef EPDC_DISPATCH_XEARLY_BLOCKS
 #define EPDC_DISPATCH_XEARLY_BLOCKS 2560  // launches of more blocks request x before COUNT
 #endif
+#ifndef EPDC_DISPATCH_NARROW_TILES
+#define EPDC_DISPATCH_NARROW_TILES 4  // launches of up to this many tiles use 1- or 2-chunk slabs
+#endif
 #ifndef EPDC_DISPATCH_LOCAL_SCAN_TILES
 #define EPDC_DISPATCH_LOCAL_SCAN_TILES 8  // launches of up to this many 64-token tiles scan in every block
 #endif

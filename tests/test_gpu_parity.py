@@ -97,6 +97,7 @@ EDGE = [
     ("ragged_rows_1p5k", 4, 8, 300, 257, 5, 768, "uniform", 1),
     ("ragged_rows_5p5k", 8, 16, 300, 300, 8, 2816, "zipf", 1),
     ("ragged_rows_9p5k", 8, 16, 200, 130, 8, 4864, "uniform", 0),
+    ("ragged_rows_9p5k_5_tiles", 8, 16, 320, 300, 8, 4864, "uniform", 1),  # 8-chunk slabs, local scan
     # ragged rows in a launch of more than 2560 blocks (x requested before COUNT)
     ("ragged_rows_x_early_t13000", 8, 16, 13000, 13000, 8, 2816, "uniform", 1),
     # further compiled dispatch variants (slab chunks, tokens per wave, bound checks, scan):
