@@ -310,9 +310,12 @@ def main():
                 "traffic": read_traffic(dom, w.name),
                 "us_per_launch": round(dom_ms * 1e3, 2), "algorithmic_bytes_per_launch": dom_b}
 
-    ref = stream_reference(torch)
-    print(f"[bench] stream reference: copy {ref['copy']:.0f} GB/s, fill {ref['fill']:.0f} GB/s",
-          file=sys.stderr, flush=True)
+    # (not in counter runs: their copies would mix with the calibration copy's)
+    ref = None
+    if not args.copy_calibration:
+        ref = stream_reference(torch)
+        print(f"[bench] stream reference: copy {ref['copy']:.0f} GB/s, fill {ref['fill']:.0f} GB/s",
+              file=sys.stderr, flush=True)
 
     cpu = None
     if args.cpu_seconds > 0:
@@ -339,7 +342,8 @@ def main():
                    "buffer_sets_rotated": len(sets), "scratch_clean": scratch_ok,
                    "frac_of_hbm_peak": round(value / HBM_PEAK_GBPS, 4),
                    "stream_reference_GBps": dict(ref, what="torch copy_ (1 GiB read + 1 GiB written) and fill_ "
-                                                           "(1 GiB written) on the same GPU, 20 launches each")})
+                                                           "(1 GiB written) on the same GPU, 20 launches each")
+                   if ref else None})
     line = {
         "metric": METRIC, "value": round(value, 1), "unit": "GB/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 5),
