@@ -82,10 +82,17 @@ def load_library() -> ctypes.CDLL:
 
 
 def _ptr(a):
+    """Device address of a buffer argument: None, a raw address (int), or a
+    contiguous device tensor (anything else is refused before any launch: a
+    host pointer would fault the GPU, a strided view would be read densely)."""
     if a is None:
         return None
     if isinstance(a, int):
         return a
+    if not a.is_cuda:
+        raise ValueError(f"expected a device tensor, got one on {a.device}")
+    if not a.is_contiguous():
+        raise ValueError(f"expected a contiguous tensor, got strides {tuple(a.stride())} for shape {tuple(a.shape)}")
     return a.data_ptr()
 
 

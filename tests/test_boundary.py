@@ -274,3 +274,36 @@ def test_prepared_calls_check_like_direct_calls():
     assert epdc.prepare_combine_push(cfg(), 8, *[P16] * 6)(stream=0, check=False) == -7
     assert epdc.prepare_combine_reduce(cfg(), 8, *[P16] * 5)(stream=0, check=False) == -7
     assert epdc.prepare_combine_reduce(cfg(), 8, P16, None, P16, P16, P16)(stream=0, check=False) == -5
+
+
+class _FakeDeviceTensor:
+    """Reports a device placement and a layout like a torch tensor would."""
+
+    def __init__(self, contiguous):
+        self.is_cuda = True
+        self._c = contiguous
+        self.shape, self.device = (4, 4), "cuda:0"
+
+    def is_contiguous(self):
+        return self._c
+
+    def stride(self):
+        return (1, 4)
+
+    def data_ptr(self):
+        return P16
+
+
+def test_binding_refuses_host_and_strided_tensors_before_any_call():
+    import torch
+    host = torch.zeros(64, dtype=torch.int32)
+    ptrs = [P16] * 10
+    with pytest.raises(ValueError, match="device tensor"):
+        epdc.epdc_dispatch(cfg(), 8, host, *ptrs[1:], scratchBytes=1 << 20, stream=0)
+    with pytest.raises(ValueError, match="contiguous"):
+        epdc.epdc_combine(cfg(), 8, _FakeDeviceTensor(False), P16, P16, P16, P16, stream=0)
+    with pytest.raises(ValueError, match="device tensor"):
+        epdc.prepare_combine_reduce(cfg(), 8, P16, None, P16, host, P16)
+    # a contiguous device tensor passes the binding (the library then runs its own checks)
+    assert epdc.epdc_combine(cfg(dtype=2), 8, _FakeDeviceTensor(True), P16, P16, P16, P16, stream=0,
+                             check=False) == -2

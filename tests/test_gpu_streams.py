@@ -68,3 +68,16 @@ def test_current_stream_is_used():
     assert_bits_equal(dev_to_bits(out_reduce.view(torch.bfloat16)), oracle_reduce(w, land_o, scale_o, o),
                       "reduce on the current stream")
     assert np.array_equal(dev_to_bits(out_gather.view(torch.bfloat16)), dev_to_bits(out_reduce.view(torch.bfloat16)))
+
+
+def test_strided_device_tensor_is_refused():
+    """A strided view would be read densely from its base address: the
+    binding refuses it before anything is launched."""
+    import combine_count_amd as epdc
+    w = workloads.CONFIGS["tiny"]
+    inp = workloads.make_inputs(w, 2)
+    g = DeviceRun(w, inp)
+    wide = torch.zeros((w.numTokens, 2 * w.hiddenDim), dtype=torch.bfloat16, device="cuda")
+    strided = wide[:, ::2]
+    with pytest.raises(ValueError, match="contiguous"):
+        epdc.epdc_combine(g.ccfg, w.numTokens, g.y, g.ids, g.wts, g.sendMap, strided)
