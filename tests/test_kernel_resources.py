@@ -58,6 +58,9 @@ def test_default_variants_keep_their_occupancy(compiled):
     # scan through the scratch; and the same for launches of at most 8 tiles (local scan)
     assert _kernel(d, r"dispatch_kernelILi7ELi1ELb1ELb0EE")["Occupancy"] >= 7
     assert _kernel(d, r"dispatch_kernelILi7ELi1ELb1ELb1EE")["Occupancy"] >= 7
+    # launches of at most 4 tiles: 2- (or 1-) chunk slabs under the local scan
+    assert _kernel(d, r"dispatch_kernelILi2ELi1ELb1ELb1EE")["Occupancy"] == 8
+    assert _kernel(d, r"dispatch_kernelILi1ELi1ELb1ELb1EE")["Occupancy"] == 8
     # gather combine, 2-chunk slabs, bf16 (up to 8 rows in flight), and its landing-row twin
     assert _kernel(c, r"combine_kernelILi2ELb1ELb0ELb0EE")["Occupancy"] >= 4
     assert _kernel(c, r"combine_kernelILi2ELb1ELb0ELb1EE")["Occupancy"] >= 4
