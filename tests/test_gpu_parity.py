@@ -263,8 +263,10 @@ def test_dirty_scratch_is_flagged_and_stays_in_bounds():
 
 
 GRAPH_CASES = [
+    ("epcfg_defaults", None),  # 2 tiles: 2-chunk slabs, local scan
     ("pr_scale", None),  # 8 tiles: local scan, scratch untouched
     ("gen_zipf_h2048", dict(numTokens=1024, maxTokPerRank=1024)),  # 16 tiles: scan through the scratch
+    ("gen_zipf_h7168", dict(wire="fp32", combineDtype="fp32")),  # 4096 blocks: x before COUNT
 ]
 
 
