@@ -181,6 +181,19 @@ def _load_worked_example():
     return d
 
 
+def _per_pe(field, conv):
+    """'p0 a b , c d ; p1 ...' -> {pe: [[a, b], [c, d]]} (rows split by ',')."""
+    res = {}
+    for part in field.split(";"):
+        toks = part.split(None, 1)
+        res[int(toks[0][1:])] = [[conv(v) for v in row.split()] for row in toks[1].split(",")]
+    return res
+
+
+def _f32_bits(a):
+    return np.ascontiguousarray(a, dtype=np.float32).view(np.uint32)
+
+
 def check_worked_example(lib):
     fails = []
     d = _load_worked_example()
@@ -189,37 +202,82 @@ def check_worked_example(lib):
     ids = np.array([[int(v) for v in r.split()] for r in d["expertIds"].split(";")], dtype=np.int32)
     wts = np.array([[float(v) for v in r.split()] for r in d["weights"].split(";")], dtype=np.float32)
     T = ids.shape[0]
-    x = (np.arange(T * H, dtype=np.uint16).reshape(T, H) + 0x3F00).astype(np.uint16)
-    for useW in (1, 0):
-        out = oracle.dispatch(W, H, M, Epr, K, useW, x, ids, wts if useW else None, fill=SENTINEL, lib=lib)
-        exp_cnt = [int(v) for v in d["expect_recvCount"].split()]
-        exp_map = np.array([[int(v) for v in r.split()] for r in d["expect_sendMap"].split(";")])
-        if list(out.recvCount) != exp_cnt:
-            fails.append(f"worked example: recvCount {list(out.recvCount)} != {exp_cnt}")
-        if not np.array_equal(out.sendMap, exp_map):
-            fails.append(f"worked example: sendMap {out.sendMap.tolist()} != {exp_map.tolist()}")
-        for part in d["expect_recvTokIdx"].split(";"):
-            toks = part.split()
-            p = int(toks[0][1:])
-            exp = [int(v) for v in toks[1:]]
-            if list(out.recvTokIdx[p, :len(exp)]) != exp:
-                fails.append(f"worked example: recvTokIdx[{p}] {list(out.recvTokIdx[p])} != {exp}")
-        # combine over constant-valued returned rows
-        y = np.zeros((W, M, H), dtype=np.uint16)
-        for part in d["y_row_values"].split(";"):
-            toks = part.split()
-            p = int(toks[0][1:])
-            vals = torch.tensor([float(v) for v in toks[1:]], dtype=torch.float32).to(torch.bfloat16)
-            bits = vals.view(torch.int16).numpy().view(np.uint16)
-            for r, b in enumerate(bits):
-                y[p, r, :] = b
-        got = oracle.combine(W, H, M, Epr, K, useW, y, ids, wts if useW else None, out.sendMap, lib=lib)
-        key = "expect_out_weighted_bf16" if useW else "expect_out_unweighted_bf16"
-        exp_out = [int(v, 16) for v in d[key].split()]
-        for t in range(T):
-            if not (got[t] == exp_out[t]).all():
-                fails.append(f"worked example useWeights={useW}: out[{t}] = {hex(int(got[t][0]))} "
-                             f"!= {hex(exp_out[t])}")
+    exp_cnt = [int(v) for v in d["expect_recvCount"].split()]
+    exp_map = np.array([[int(v) for v in r.split()] for r in d["expect_sendMap"].split(";")])
+    exp_tok = {int(part.split()[0][1:]): [int(v) for v in part.split()[1:]]
+               for part in d["expect_recvTokIdx"].split(";")}
+    exp_ids = _per_pe(d["expect_recvExpertIds"], int)
+    exp_wts = _per_pe(d["expect_recvWeights"], float)
+    # returned rows: constant per (PE, window row), as bf16 bits and as fp32
+    y32 = np.zeros((W, M, H), dtype=np.float32)
+    for part in d["y_row_values"].split(";"):
+        toks = part.split()
+        for r, v in enumerate(toks[1:]):
+            y32[int(toks[0][1:]), r, :] = float(v)
+    y16 = torch.from_numpy(y32).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    # distinct token rows, so that a row copied from the wrong token shows
+    x16 = (np.arange(T * H, dtype=np.uint16).reshape(T, H) + 0x3F00).astype(np.uint16)
+    x32 = (np.arange(T * H, dtype=np.float32).reshape(T, H) * 0.5 - 3.0).astype(np.float32)
+    for fp32 in (0, 1):
+        x, y = (x32, y32) if fp32 else (x16, y16)
+        tag = "fp32" if fp32 else "bf16"
+        for useW in (1, 0):
+            out = oracle.dispatch(W, H, M, Epr, K, useW, x, ids, wts if useW else None, fill=SENTINEL, lib=lib)
+            if list(out.recvCount) != exp_cnt:
+                fails.append(f"worked example: recvCount {list(out.recvCount)} != {exp_cnt}")
+            if not np.array_equal(out.sendMap, exp_map):
+                fails.append(f"worked example: sendMap {out.sendMap.tolist()} != {exp_map.tolist()}")
+            for p, exp in exp_tok.items():
+                if list(out.recvTokIdx[p, :len(exp)]) != exp:
+                    fails.append(f"worked example: recvTokIdx[{p}] {list(out.recvTokIdx[p])} != {exp}")
+                for r, t in enumerate(exp):
+                    if out.recvX[p, r].tobytes() != x[t].tobytes():
+                        fails.append(f"worked example {tag}: recvX[{p}][{r}] is not token {t}'s row")
+                    if list(out.recvExpertIds[p, r]) != exp_ids[p][r]:
+                        fails.append(f"worked example: recvExpertIds[{p}][{r}] "
+                                     f"{list(out.recvExpertIds[p, r])} != {exp_ids[p][r]}")
+                    got_w = list(out.recvWeights[p, r])
+                    want_w = [float(np.float32(v)) for v in exp_wts[p][r]] if useW else [SENTINEL["recvWeights"]] * K
+                    if got_w != want_w:
+                        fails.append(f"worked example useWeights={useW}: recvWeights[{p}][{r}] {got_w} != {want_w}")
+                # rows past the count stay untouched
+                if out.recvX[p, len(exp):].size and (out.recvX[p, len(exp):].view(np.uint8) != 0xAD).any():
+                    fails.append(f"worked example {tag}: recvX[{p}] written past its count")
+            key = f"expect_out_{'weighted' if useW else 'unweighted'}_{tag}"
+            exp_out = [int(v, 16) for v in d[key].split()]
+            got = oracle.combine(W, H, M, Epr, K, useW, y, ids, wts if useW else None, out.sendMap, lib=lib)
+            bits = _f32_bits(got) if fp32 else got
+            for t in range(T):
+                if not (bits[t] == exp_out[t]).all():
+                    fails.append(f"worked example {tag} useWeights={useW}: out[{t}] = {hex(int(bits[t][0]))} "
+                                 f"!= {hex(exp_out[t])}")
+            # scatter combine: push lands the returned rows, reduce gives the same bits
+            cap = oracle.landing_rows(W, K, T)
+            if cap != int(d["landing_capacity"]):
+                fails.append(f"worked example: landing capacity {cap} != {d['landing_capacity']}")
+            land, scale = oracle.combine_push(W, H, M, Epr, K, useW, T, y, out.recvExpertIds, out.recvWeights,
+                                              out.recvCount, fill_byte=0xA5, scale_fill=-3.25, lib=lib)
+            land_vals = [float(v) for v in d["expect_landing_values"].split()]
+            U = len(land_vals)
+            land32 = land if fp32 else (land.astype(np.uint32) << 16).view(np.float32)
+            for L, v in enumerate(land_vals):
+                if not (land32[L] == np.float32(v)).all():
+                    fails.append(f"worked example {tag}: landing row {L} = {land32[L][0]} != {v}")
+            if (land[U:].view(np.uint8) != 0xA5).any():
+                fails.append(f"worked example {tag}: landing rows past {U} were written")
+            want_scale = ([int(v, 16) for v in d["expect_landScale_bits"].split()] if useW
+                          else [int(np.float32(-3.25).view(np.uint32))] * U)
+            if list(_f32_bits(scale[:U])) != want_scale:
+                fails.append(f"worked example useWeights={useW}: landScale {[hex(v) for v in _f32_bits(scale[:U])]} "
+                             f"!= {[hex(v) for v in want_scale]}")
+            if (scale[U:] != np.float32(-3.25)).any():
+                fails.append("worked example: landScale past the landed rows was written")
+            red = oracle.combine_reduce(W, H, M, Epr, K, useW, land, scale, out.recvCount, out.sendMap, lib=lib)
+            rbits = _f32_bits(red) if fp32 else red
+            for t in range(T):
+                if not (rbits[t] == exp_out[t]).all():
+                    fails.append(f"worked example scatter {tag} useWeights={useW}: out[{t}] = "
+                                 f"{hex(int(rbits[t][0]))} != {hex(exp_out[t])}")
     return fails
 
 

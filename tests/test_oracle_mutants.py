@@ -36,6 +36,9 @@ MUTANTS = [
     ("metadata: slot stored as token index",
      "recvTokIdx[row] = t;",
      "recvTokIdx[row] = k;"),
+    ("expert ids copied from the mirrored token",
+     "memcpy(recvExpertIds + row * K, expertIds + (int64_t)t * K,",
+     "memcpy(recvExpertIds + row * K, expertIds + (int64_t)(T - 1 - t) * K,"),
     ("weights copied from the mirrored token",
      "memcpy(recvWeights + row * K, weights + (int64_t)t * K,",
      "memcpy(recvWeights + row * K, weights + (int64_t)(T - 1 - t) * K,"),
