@@ -158,7 +158,27 @@ def cpu_baseline(w, inp, budget_s, step_bytes, push):
             "kind": "oracle",
             "sample": f"{n} full {what} steps of {w.name} (seed {inp.seed}), single-threaded C "
                       f"oracle, {el:.1f} s wall",
-            "ms_per_step": round(el / n * 1e3, 2)}
+            "ms_per_step": round(el / n * 1e3, 2),
+            "host": host_cpu()}
+
+
+def host_cpu():
+    """The host the CPU figure was taken on: its CPU model, the cores the
+    OS reports and the cores this process may run on."""
+    model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    try:
+        usable = len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        usable = None
+    return {"cpu_model": model, "nproc": os.cpu_count(), "usable_cores": usable}
 
 
 def main():

@@ -44,3 +44,13 @@ def test_kernel_hash_ignores_comments_but_not_code(tmp_path, monkeypatch):
     assert bench.kernel_source_hash() == h0
     src.write_text("int f(int a) { return a + 2; }  // add one\n")
     assert bench.kernel_source_hash() != h0
+
+
+def test_cpu_baseline_names_its_host():
+    """The CPU figure carries the host it ran on: CPU model and core counts."""
+    sys.path.insert(0, ROOT)
+    import bench
+    h = bench.host_cpu()
+    assert set(h) == {"cpu_model", "nproc", "usable_cores"}
+    assert h["nproc"] >= 1 and 1 <= h["usable_cores"] <= h["nproc"]
+    assert h["cpu_model"] is None or isinstance(h["cpu_model"], str)
