@@ -177,7 +177,10 @@ __device__ __forceinline__ void store_token(const DispatchParams &P, const u32x4
 //   2. SCAN: the leader sums the published counts of all earlier tiles into
 //      the tile's base row on each PE and publishes it as base+1; the
 //      tile's other blocks wait for that single line (so polling traffic
-//      does not grow with the number of blocks per tile).
+//      does not grow with the number of blocks per tile).  In launches of
+//      at most EPDC_DISPATCH_SELF_SCAN_BLOCKS blocks every block sums the
+//      counts itself (selfScan), which takes the publish-and-poll round
+//      trip off the path.
 //   3. Loads: the slab-0 waves' metadata rows, then every wave's NTW x
 //      slabs (with xEarly, the x slabs go out before COUNT instead; see
 //      launch_fused).
@@ -192,7 +195,7 @@ __device__ __forceinline__ void store_token(const DispatchParams &P, const u32x4
 //      the next call (and for every replay of a captured graph).
 template <int CPW, int NTW, bool FULL, bool LOCAL>
 __global__ __launch_bounds__(256) void dispatch_kernel(DispatchParams P, int nSlabs, int nSubs, int nBlocks,
-                                                            int xEarly) {
+                                                            int xEarly, int selfScan) {
     __shared__ uint64_t sMask[kTile];  // destination-PE set of each token of the tile
     __shared__ uint64_t sBal[64];      // per PE: which tokens of the tile go there
     __shared__ int32_t sPre[64];       // per PE: rows taken by earlier tiles
@@ -298,6 +301,9 @@ __global__ __launch_bounds__(256) void dispatch_kernel(DispatchParams P, int nSl
     // published counts of all earlier tiles (the row stride Wp is a power of
     // two dividing 256, so thread tid only ever sums PE tid % Wp) and
     // publishes the result; the tile's other blocks wait for that one line.
+    // With selfScan every block sums for itself and nothing is published:
+    // a block still waits only for the counts of earlier tiles, whose
+    // leaders were dispatched before it.
     // Tile 0's base rows are 0: nothing to sum, publish or wait for.  A
     // local scan counts the earlier tiles (all full) in this block instead,
     // the 4 waves taking tiles wave, wave + 4, ...
@@ -313,7 +319,7 @@ __global__ __launch_bounds__(256) void dispatch_kernel(DispatchParams P, int nSl
                 if (lane == p && bal) atomicAdd(&sPre[p], (int32_t)__popcll(bal));
             }
         }
-    } else if (tile > 0 && leader) {
+    } else if (tile > 0 && (leader || selfScan)) {
         const int n = tile * P.Wp;
         uint32_t acc = 0;
         int idx = tid;
@@ -332,10 +338,12 @@ __global__ __launch_bounds__(256) void dispatch_kernel(DispatchParams P, int nSl
             acc += v - 1u;
         }
         if (acc) atomicAdd(&sPre[tid & (P.Wp - 1)], (int32_t)acc);
-        __syncthreads();
-        if (tid < P.Wp)
-            __hip_atomic_store(prefixes + (int64_t)tile * P.Wp + tid, (uint32_t)sPre[tid] + 1u, __ATOMIC_RELAXED,
-                               __HIP_MEMORY_SCOPE_AGENT);
+        if (!selfScan) {
+            __syncthreads();
+            if (tid < P.Wp)
+                __hip_atomic_store(prefixes + (int64_t)tile * P.Wp + tid, (uint32_t)sPre[tid] + 1u,
+                                   __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
     } else if (tile > 0 && tid < P.Wp) {
         uint32_t v = load_published(prefixes + (int64_t)tile * P.Wp + tid);
         if (v == 0) v = wait_published(prefixes + (int64_t)tile * P.Wp + tid, hdr + kScratchError);
@@ -440,6 +448,12 @@ hipError_t launch_fused(const DispatchParams &P, int nTiles, hipStream_t stream)
     // delays the SCAN instead.  Measured crossover: between 2048 blocks (after
     // the SCAN 1-3% faster) and 3072 (before COUNT 4% faster; 8-10% at 4096).
     const int xEarly = nBlocks > EPDC_DISPATCH_XEARLY_BLOCKS ? 1 : 0;
+    // Every block sums the earlier tiles' counts itself in launches of up to
+    // 4 blocks per CU, where it saves a round trip (measured at 4096 tokens:
+    // fp4x2 rows 2.6%, h2048 2.3%; 640 / 1024 tokens at h7168 5.3% / 3.6%).
+    // In larger launches the tile leader's one published line is faster
+    // (1.5% at 2048 blocks, 1.6% for fp8 rows at 1536).
+    const int selfScan = nBlocks <= EPDC_DISPATCH_SELF_SCAN_BLOCKS ? 1 : 0;
     // The local scan is built for one token per wave only: more tokens per
     // wave within 8 tiles takes over 128 slabs per row (rows of 128 KiB and
     // up), and its id registers would then cost occupancy; such launches scan
@@ -448,19 +462,19 @@ hipError_t launch_fused(const DispatchParams &P, int nTiles, hipStream_t stream)
         if (nTiles <= EPDC_DISPATCH_LOCAL_SCAN_TILES) {
             if (full)
                 hipLaunchKernelGGL((dispatch_kernel<CPW, NTW, true, true>), grid, dim3(256), 0, stream, P, nSlabs,
-                                   nSubs, nBlocks, xEarly);
+                                   nSubs, nBlocks, xEarly, selfScan);
             else
                 hipLaunchKernelGGL((dispatch_kernel<CPW, NTW, false, true>), grid, dim3(256), 0, stream, P, nSlabs,
-                                   nSubs, nBlocks, xEarly);
+                                   nSubs, nBlocks, xEarly, selfScan);
             return hipGetLastError();
         }
     }
     if (full) {
         hipLaunchKernelGGL((dispatch_kernel<CPW, NTW, true, false>), grid, dim3(256), 0, stream, P, nSlabs, nSubs,
-                           nBlocks, xEarly);
+                           nBlocks, xEarly, selfScan);
     } else {
         hipLaunchKernelGGL((dispatch_kernel<CPW, NTW, false, false>), grid, dim3(256), 0, stream, P, nSlabs, nSubs,
-                           nBlocks, xEarly);
+                           nBlocks, xEarly, selfScan);
     }
     return hipGetLastError();
 }

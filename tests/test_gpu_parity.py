@@ -91,6 +91,12 @@ EDGE = [
     # at the edge of the local scan (8 tiles) and just past it (9 tiles)
     ("local_scan_8_tiles", 8, 8, 512, 512, 8, 2048, "uniform", 1),
     ("scratch_scan_9_tiles", 8, 8, 600, 520, 8, 2048, "zipf", 1),
+    # the two SCAN forms around their switch at 1024 blocks (h7168: 32 blocks per tile):
+    # 32 tiles, every block sums the counts itself; 33 tiles, the tile leader publishes
+    # base rows (both with a ragged last tile); and 63 self-summing tiles of 256-byte rows
+    ("self_scan_1024_blocks_t2047", 8, 32, 2048, 2047, 8, 7168, "zipf", 1),
+    ("leader_scan_1056_blocks_t2049", 8, 32, 2049, 2049, 8, 7168, "zipf", 1),
+    ("self_scan_63_tiles_h128", 4, 8, 4100, 4000, 4, 128, "uniform", 1),
     # 32 KiB rows (four 8-chunk slabs per row)
     ("h16384_rows", 8, 16, 600, 600, 8, 16384, "zipf", 1),
     # rows that are not a whole number of 1 KiB chunks, one per tail-checked slab width
