@@ -441,19 +441,24 @@ hipError_t launch_fused(const DispatchParams &P, int nTiles, hipStream_t stream)
     const int nBlocks = (int)blocks;
     const bool full = P.rowBytes % kChunkBytes == 0 && P.nChunks % CPW == 0;
     const dim3 grid(nBlocks);
-    // x before COUNT in launches of well over one round of resident blocks
-    // (about 7 per CU, 1792 on the chip): blocks that start once HBM is
-    // saturated would otherwise idle through the SCAN's round trips, each
-    // queued behind streaming traffic.  In smaller launches the early x flood
-    // delays the SCAN instead.  Measured crossover: between 2048 blocks (after
-    // the SCAN 1-3% faster) and 3072 (before COUNT 4% faster; 8-10% at 4096).
-    const int xEarly = nBlocks > EPDC_DISPATCH_XEARLY_BLOCKS ? 1 : 0;
     // Every block sums the earlier tiles' counts itself in launches of up to
     // 4 blocks per CU, where it saves a round trip (measured at 4096 tokens:
     // fp4x2 rows 2.6%, h2048 2.3%; 640 / 1024 tokens at h7168 5.3% / 3.6%).
     // In larger launches the tile leader's one published line is faster
     // (1.5% at 2048 blocks, 1.6% for fp8 rows at 1536).
     const int selfScan = nBlocks <= EPDC_DISPATCH_SELF_SCAN_BLOCKS ? 1 : 0;
+    // x before COUNT in launches of well over one round of resident blocks
+    // (about 7 per CU, 1792 on the chip): blocks that start once HBM is
+    // saturated would otherwise idle through the SCAN's round trips, each
+    // queued behind streaming traffic.  In smaller launches the early x flood
+    // delays the SCAN instead.  Measured crossover: between 2048 blocks (after
+    // the SCAN 1-3% faster) and 3072 (before COUNT 4% faster; 8-10% at 4096).
+    // Self-summing launches whose slabs are at most 4 chunks also request x
+    // before COUNT (4096 tokens: fp4x2 rows 2.6%, h1024 2%, h2048 1%, fp8 rows
+    // at h4096 1% faster); with wider slabs there the early x delays the SCAN
+    // (2-3.5% slower with 7-chunk slabs).
+    const int xEarly =
+        (nBlocks > EPDC_DISPATCH_XEARLY_BLOCKS || (selfScan && CPW <= EPDC_DISPATCH_XEARLY_SELF_CPW)) ? 1 : 0;
     // The local scan is built for one token per wave only: more tokens per
     // wave within 8 tiles takes over 128 slabs per row (rows of 128 KiB and
     // up), and its id registers would then cost occupancy; such launches scan

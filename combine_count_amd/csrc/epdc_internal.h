@@ -68,6 +68,9 @@ __device__ __forceinline__ void wait_vmcnt() {
 #ifndef EPDC_DISPATCH_SELF_SCAN_BLOCKS
 #define EPDC_DISPATCH_SELF_SCAN_BLOCKS 1024  // launches of up to this many blocks sum the tile counts in every block
 #endif
+#ifndef EPDC_DISPATCH_XEARLY_SELF_CPW
+#define EPDC_DISPATCH_XEARLY_SELF_CPW 4  // ... and self-summing launches with slabs of at most this many chunks
+#endif
 #ifndef EPDC_DISPATCH_NARROW_TILES
 #define EPDC_DISPATCH_NARROW_TILES 4  // launches of up to this many tiles use 1- or 2-chunk slabs
 #endif

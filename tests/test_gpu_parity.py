@@ -97,6 +97,8 @@ EDGE = [
     ("self_scan_1024_blocks_t2047", 8, 32, 2048, 2047, 8, 7168, "zipf", 1),
     ("leader_scan_1056_blocks_t2049", 8, 32, 2049, 2049, 8, 7168, "zipf", 1),
     ("self_scan_63_tiles_h128", 4, 8, 4100, 4000, 4, 128, "uniform", 1),
+    # self-summing with x requested before COUNT (slabs of at most 4 chunks), ragged 3.5 KiB rows
+    ("self_scan_x_early_ragged_h1792", 4, 8, 1000, 1000, 5, 1792, "uniform", 1),
     # 32 KiB rows (four 8-chunk slabs per row)
     ("h16384_rows", 8, 16, 600, 600, 8, 16384, "zipf", 1),
     # rows that are not a whole number of 1 KiB chunks, one per tail-checked slab width
