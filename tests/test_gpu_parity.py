@@ -271,15 +271,19 @@ def test_dirty_scratch_is_flagged_and_stays_in_bounds():
 
 
 GRAPH_CASES = [
-    ("epcfg_defaults", None),  # 2 tiles: 2-chunk slabs, local scan
-    ("pr_scale", None),  # 8 tiles: local scan, scratch untouched
-    ("gen_zipf_h2048", dict(numTokens=1024, maxTokPerRank=1024)),  # 16 tiles: scan through the scratch
-    ("gen_zipf_h7168", dict(wire="fp32", combineDtype="fp32")),  # 4096 blocks: x before COUNT
+    # id, workload, overrides
+    ("epcfg_defaults", "epcfg_defaults", None),  # 2 tiles: 2-chunk slabs, local scan
+    ("pr_scale", "pr_scale", None),  # 8 tiles: local scan, scratch untouched
+    # 16 tiles, 256 blocks: every block sums the published counts, x before COUNT (4-chunk slabs)
+    ("h2048_t1024_self_scan", "gen_zipf_h2048", dict(numTokens=1024, maxTokPerRank=1024)),
+    # 2048 blocks: the tile leaders publish base rows, x after the SCAN
+    ("h7168_t4096_leader_scan", "gen_zipf_h7168", None),
+    ("h7168_fp32_x_early", "gen_zipf_h7168", dict(wire="fp32", combineDtype="fp32")),  # 4096 blocks
 ]
 
 
-@pytest.mark.parametrize("name,over", GRAPH_CASES, ids=[c[0] for c in GRAPH_CASES])
-def test_deterministic_and_graph_replay(name, over):
+@pytest.mark.parametrize("case_id,name,over", GRAPH_CASES, ids=[c[0] for c in GRAPH_CASES])
+def test_deterministic_and_graph_replay(case_id, name, over):
     """Two eager runs are bitwise equal; a captured dispatch+combine graph
     replayed several times (eager work and syncs in between) equals eager,
     and the scratch is zero after every replay."""
