@@ -99,6 +99,16 @@ EDGE = [
     ("self_scan_63_tiles_h128", 4, 8, 4100, 4000, 4, 128, "uniform", 1),
     # self-summing with x requested before COUNT (slabs of at most 4 chunks), ragged 3.5 KiB rows
     ("self_scan_x_early_ragged_h1792", 4, 8, 1000, 1000, 5, 1792, "uniform", 1),
+    # the token-count x topk grid of mori PR #599's checks, at 8 PEs / 256 experts / h7168
+    # (uniform routing; the Zipf workloads cover the skewed case)
+    ("pr_grid_ct512_topk6", 8, 32, 512, 512, 6, 7168, "uniform", 1),
+    ("pr_grid_ct512_topk8", 8, 32, 512, 512, 8, 7168, "uniform", 1),
+    ("pr_grid_ct1024_topk6", 8, 32, 1024, 1024, 6, 7168, "uniform", 1),
+    ("pr_grid_ct1024_topk8", 8, 32, 1024, 1024, 8, 7168, "uniform", 1),
+    ("pr_grid_ct2048_topk6", 8, 32, 2048, 2048, 6, 7168, "uniform", 1),
+    ("pr_grid_ct2048_topk8", 8, 32, 2048, 2048, 8, 7168, "uniform", 1),
+    ("pr_grid_ct4096_topk6", 8, 32, 4096, 4096, 6, 7168, "uniform", 1),
+    ("pr_grid_ct4096_topk8", 8, 32, 4096, 4096, 8, 7168, "uniform", 1),
     # 32 KiB rows (four 8-chunk slabs per row)
     ("h16384_rows", 8, 16, 600, 600, 8, 16384, "zipf", 1),
     # rows that are not a whole number of 1 KiB chunks, one per tail-checked slab width
