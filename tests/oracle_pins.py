@@ -376,7 +376,7 @@ def check_page_staging_bytes(lib, n_seeds=12):
 # --------------------------------------------------------------------------
 # structural invariants on the real configurations
 # --------------------------------------------------------------------------
-def check_invariants(lib, names=None, seeds=(1, 2), h_cap=None):
+def check_invariants(lib, names=None, seeds=(1, 2, 3), h_cap=None):
     """I1-I4: counts sum to kept slots; U_t <= min(W, K); windows hold their
     tokens in strictly ascending order, each a bitwise copy; sendMap decodes
     to a row holding the same token on the slot's PE."""
