@@ -54,3 +54,14 @@ def test_cpu_baseline_names_its_host():
     assert set(h) == {"cpu_model", "nproc", "usable_cores"}
     assert h["nproc"] >= 1 and 1 <= h["usable_cores"] <= h["nproc"]
     assert h["cpu_model"] is None or isinstance(h["cpu_model"], str)
+
+
+def test_timed_path_does_not_import_the_oracle():
+    """bench.py's timed path (the package, the input generator and the device
+    harness) leaves the oracle unloaded; only its cpu_baseline leg imports it."""
+    code = ("import sys; sys.path[:0] = [{root!r}, {tests!r}]\n"
+            "import bench, combine_count_amd, workloads, gpu_harness\n"
+            "assert 'oracle' not in sys.modules, sorted(m for m in sys.modules if 'oracle' in m)\n"
+            "print('ok')\n").format(root=ROOT, tests=os.path.join(ROOT, "tests"))
+    r = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, timeout=300)
+    assert r.returncode == 0 and r.stdout.strip() == "ok", r.stderr[-2000:]
