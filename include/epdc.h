@@ -100,10 +100,13 @@ typedef struct epdc_cfg {
  * The scratch must be zero-filled once before its first use (e.g. one
  * hipMemset at allocation).  Every dispatch leaves it zeroed again, so it
  * needs no reset between calls or graph replays.  Word 2 (byte offset 8) is
- * an error flag that a dispatch sets nonzero -- and never clears -- if one of
- * its bounded in-kernel waits timed out, which means that call's outputs are
- * invalid; it stays zero in correct operation.  One scratch buffer serves one
- * dispatch at a time: calls that may run concurrently need separate buffers. */
+ * an error flag that a dispatch sets nonzero -- and never clears -- when that
+ * call's outputs are invalid: 1 if one of its bounded in-kernel waits timed
+ * out, 2 if a computed row fell outside its window (only possible when the
+ * scratch was not zero at launch; such rows are skipped, nothing is written
+ * outside the windows).  It stays zero in correct operation.  One scratch
+ * buffer serves one dispatch at a time: calls that may run concurrently need
+ * separate buffers. */
 size_t epdc_dispatch_scratch_bytes(const epdc_cfg *cfg);
 
 /*
