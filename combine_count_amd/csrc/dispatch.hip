@@ -183,7 +183,7 @@ __device__ __forceinline__ void store_token(const DispatchParams &P, const u32x4
 //      trip off the path.
 //   3. Loads: the slab-0 waves' metadata rows, then every wave's NTW x
 //      slabs (with xEarly, the x slabs go out before COUNT instead; see
-//      launch_fused).
+//      plan_dispatch in epdc_internal.h).
 //   4. FINALIZE: one wait for the wave's loads, then every store of its NTW
 //      tokens to every destination, with no further wait (vmcnt is one
 //      in-order counter for loads and stores on this ISA, so waiting on a
@@ -431,68 +431,43 @@ __global__ __launch_bounds__(256) void dispatch_kernel(DispatchParams P, int nSl
     }
 }
 
+// Runs a plan (plan_dispatch in epdc_internal.h) with its compiled variant.
 template <int CPW, int NTW>
-hipError_t launch_fused(const DispatchParams &P, int nTiles, hipStream_t stream) {
+hipError_t launch_fused(const DispatchParams &P, const DispatchPlan &pl, hipStream_t stream) {
     static_assert(kTile % (4 * NTW) == 0, "a block's tokens must tile the 64-token tile");
-    const int nSubs = kTile / (4 * NTW);
-    const int nSlabs = ceil_div(P.nChunks, CPW);
-    const int64_t blocks = (int64_t)nTiles * nSubs * nSlabs;
-    if (blocks > INT32_MAX) return hipErrorInvalidConfiguration;
-    const int nBlocks = (int)blocks;
-    const bool full = P.rowBytes % kChunkBytes == 0 && P.nChunks % CPW == 0;
+    if (pl.nBlocks > INT32_MAX) return hipErrorInvalidConfiguration;
+    const int nBlocks = (int)pl.nBlocks;
     const dim3 grid(nBlocks);
-    // Every block sums the earlier tiles' counts itself in launches of up to
-    // 4 blocks per CU, where it saves a round trip (measured at 4096 tokens:
-    // fp4x2 rows 2.6%, h2048 2.3%; 640 / 1024 tokens at h7168 5.3% / 3.6%).
-    // In larger launches the tile leader's one published line is faster
-    // (1.5% at 2048 blocks, 1.6% for fp8 rows at 1536).
-    const int selfScan = nBlocks <= EPDC_DISPATCH_SELF_SCAN_BLOCKS ? 1 : 0;
-    // x before COUNT in launches of well over one round of resident blocks
-    // (about 7 per CU, 1792 on the chip): blocks that start once HBM is
-    // saturated would otherwise idle through the SCAN's round trips, each
-    // queued behind streaming traffic.  In smaller launches the early x flood
-    // delays the SCAN instead.  Measured crossover: between 2048 blocks (after
-    // the SCAN 1-3% faster) and 3072 (before COUNT 4% faster; 8-10% at 4096).
-    // Self-summing launches whose slabs are at most 4 chunks also request x
-    // before COUNT (4096 tokens: fp4x2 rows 2.6%, h1024 2%, h2048 1%, fp8 rows
-    // at h4096 1% faster); with wider slabs there the early x delays the SCAN
-    // (2-3.5% slower with 7-chunk slabs).
-    const int xEarly =
-        (nBlocks > EPDC_DISPATCH_XEARLY_BLOCKS || (selfScan && CPW <= EPDC_DISPATCH_XEARLY_SELF_CPW)) ? 1 : 0;
-    // The local scan is built for one token per wave only: more tokens per
-    // wave within 8 tiles takes over 128 slabs per row (rows of 128 KiB and
-    // up), and its id registers would then cost occupancy; such launches scan
-    // through the scratch.
+    const int xEarly = pl.xEarly ? 1 : 0;
+    const int selfScan = pl.selfScan ? 1 : 0;
     if constexpr (NTW == 1) {
-        if (nTiles <= EPDC_DISPATCH_LOCAL_SCAN_TILES) {
-            if (full)
-                hipLaunchKernelGGL((dispatch_kernel<CPW, NTW, true, true>), grid, dim3(256), 0, stream, P, nSlabs,
-                                   nSubs, nBlocks, xEarly, selfScan);
+        if (pl.local) {
+            if (pl.full)
+                hipLaunchKernelGGL((dispatch_kernel<CPW, NTW, true, true>), grid, dim3(256), 0, stream, P, pl.nSlabs,
+                                   pl.nSubs, nBlocks, xEarly, selfScan);
             else
-                hipLaunchKernelGGL((dispatch_kernel<CPW, NTW, false, true>), grid, dim3(256), 0, stream, P, nSlabs,
-                                   nSubs, nBlocks, xEarly, selfScan);
+                hipLaunchKernelGGL((dispatch_kernel<CPW, NTW, false, true>), grid, dim3(256), 0, stream, P, pl.nSlabs,
+                                   pl.nSubs, nBlocks, xEarly, selfScan);
             return hipGetLastError();
         }
     }
-    if (full) {
-        hipLaunchKernelGGL((dispatch_kernel<CPW, NTW, true, false>), grid, dim3(256), 0, stream, P, nSlabs, nSubs,
-                           nBlocks, xEarly, selfScan);
-    } else {
-        hipLaunchKernelGGL((dispatch_kernel<CPW, NTW, false, false>), grid, dim3(256), 0, stream, P, nSlabs, nSubs,
-                           nBlocks, xEarly, selfScan);
-    }
+    if (pl.full)
+        hipLaunchKernelGGL((dispatch_kernel<CPW, NTW, true, false>), grid, dim3(256), 0, stream, P, pl.nSlabs,
+                           pl.nSubs, nBlocks, xEarly, selfScan);
+    else
+        hipLaunchKernelGGL((dispatch_kernel<CPW, NTW, false, false>), grid, dim3(256), 0, stream, P, pl.nSlabs,
+                           pl.nSubs, nBlocks, xEarly, selfScan);
     return hipGetLastError();
 }
 
-// Tokens per wave: one (most blocks, measured fastest at 4096 and 16384
-// tokens) unless that would exceed kMaxBlocks blocks.
 template <int CPW>
-hipError_t launch_cpw(const DispatchParams &P, int nTiles, hipStream_t stream) {
-    constexpr int64_t kMaxBlocks = 16384;
-    const int64_t perTokenWave = (int64_t)nTiles * (kTile / 4) * ceil_div(P.nChunks, CPW);
-    if (perTokenWave <= kMaxBlocks) return launch_fused<CPW, 1>(P, nTiles, stream);
-    if (perTokenWave <= 2 * kMaxBlocks) return launch_fused<CPW, 2>(P, nTiles, stream);
-    return launch_fused<CPW, 4>(P, nTiles, stream);
+hipError_t launch_cpw(const DispatchParams &P, const DispatchPlan &pl, hipStream_t stream) {
+    switch (pl.ntw) {
+        case 1: return launch_fused<CPW, 1>(P, pl, stream);
+        case 2: return launch_fused<CPW, 2>(P, pl, stream);
+        case 4: return launch_fused<CPW, 4>(P, pl, stream);
+        default: return hipErrorInvalidConfiguration;
+    }
 }
 
 }  // namespace
@@ -502,35 +477,18 @@ hipError_t launch_dispatch(const DispatchParams &P, hipStream_t stream) {
         hipLaunchKernelGGL(zero_count_kernel, dim3(1), dim3(64), 0, stream, P.recvCount, P.W);
         return hipGetLastError();
     }
-    const int nTiles = ceil_div(P.T, kTile);
+    const DispatchPlan pl = plan_dispatch(P.T, P.rowBytes);
 #if EPDC_DISPATCH_CPW != 0 && EPDC_DISPATCH_NTW != 0
-    return launch_fused<EPDC_DISPATCH_CPW, EPDC_DISPATCH_NTW>(P, nTiles, stream);
+    return launch_fused<EPDC_DISPATCH_CPW, EPDC_DISPATCH_NTW>(P, pl, stream);
 #else
-    // Slab width.  Launches of at most EPDC_DISPATCH_NARROW_TILES tiles are
-    // bound by round trips, not bytes: 2-chunk slabs (1 for an odd chunk
-    // count) spread a token's stores over more waves (64 tokens x h7168:
-    // 4.9 -> 4.2 us).  Otherwise the widest of 8/7/4/2 chunks that divides
-    // the row (a wave then moves up to 8 KiB of a token with no bound
-    // checks); other rows (not a whole number of 1 KiB chunks, e.g. 3.5 KiB
-    // fp4x2 rows at hidden 7168) take the narrowest of 1/2/4/7/8 chunks that
-    // covers the row (8 beyond that) with bound checks on the tail.
-    if (nTiles <= EPDC_DISPATCH_NARROW_TILES) {
-        if (P.nChunks <= 1) return launch_cpw<1>(P, nTiles, stream);
-        if (P.rowBytes % kChunkBytes != 0 || P.nChunks % 2 == 0) return launch_cpw<2>(P, nTiles, stream);
-        return launch_cpw<1>(P, nTiles, stream);
+    switch (pl.cpw) {
+        case 1: return launch_cpw<1>(P, pl, stream);
+        case 2: return launch_cpw<2>(P, pl, stream);
+        case 4: return launch_cpw<4>(P, pl, stream);
+        case 7: return launch_cpw<7>(P, pl, stream);
+        case 8: return launch_cpw<8>(P, pl, stream);
+        default: return hipErrorInvalidConfiguration;
     }
-    if (P.rowBytes % kChunkBytes == 0) {
-        if (P.nChunks % 8 == 0) return launch_cpw<8>(P, nTiles, stream);
-        if (P.nChunks % 7 == 0) return launch_cpw<7>(P, nTiles, stream);
-        if (P.nChunks % 4 == 0) return launch_cpw<4>(P, nTiles, stream);
-        if (P.nChunks % 2 == 0) return launch_cpw<2>(P, nTiles, stream);
-        return launch_cpw<1>(P, nTiles, stream);
-    }
-    if (P.nChunks <= 1) return launch_cpw<1>(P, nTiles, stream);
-    if (P.nChunks <= 2) return launch_cpw<2>(P, nTiles, stream);
-    if (P.nChunks <= 4) return launch_cpw<4>(P, nTiles, stream);
-    if (P.nChunks <= 7) return launch_cpw<7>(P, nTiles, stream);
-    return launch_cpw<8>(P, nTiles, stream);
 #endif
 }
 

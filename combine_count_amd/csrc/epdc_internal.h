@@ -194,6 +194,81 @@ inline DivMagic div_magic(uint32_t d) {
     return DivMagic{(uint32_t)m, l < 1 ? l : 1, l > 1 ? l - 1 : 0};
 }
 
+// Launch geometry of one dispatch, chosen from the token count and the row
+// size alone (host code; the launcher runs exactly this plan, and a host test
+// pins it for the documented shapes).
+struct DispatchPlan {
+    int32_t cpw;      // 1 KiB chunks per slab: 1, 2, 4, 7 or 8
+    int32_t ntw;      // tokens per wave: 1, 2 or 4
+    int32_t nSlabs;   // slabs per row
+    int32_t nSubs;    // blocks per tile and slab (64 / (4 * ntw))
+    int64_t nBlocks;  // grid size (0: no tokens, only recvCount is written)
+    bool full;        // every slab lies inside the row: no per-lane bound checks
+    bool local;       // local scan: every block counts the earlier tiles' ids
+    bool selfScan;    // every block sums the published tile counts
+    bool xEarly;      // x slabs requested before COUNT
+};
+
+inline DispatchPlan plan_dispatch(int32_t T, int32_t rowBytes) {
+    DispatchPlan pl{};
+    if (T <= 0) return pl;
+    const int32_t nTiles = ceil_div(T, kTile);
+    const int32_t nChunks = ceil_div(rowBytes, kChunkBytes);
+    const bool whole = rowBytes % kChunkBytes == 0;
+#if EPDC_DISPATCH_CPW != 0 && EPDC_DISPATCH_NTW != 0
+    pl.cpw = EPDC_DISPATCH_CPW;
+    pl.ntw = EPDC_DISPATCH_NTW;
+#else
+    // Slab width.  Launches of at most EPDC_DISPATCH_NARROW_TILES tiles are
+    // bound by round trips, not bytes: 2-chunk slabs (1 for an odd chunk
+    // count) spread a token's stores over more waves (64 tokens x h7168:
+    // 4.9 -> 4.2 us).  Otherwise the widest of 8/7/4/2 chunks that divides
+    // the row (a wave then moves up to 8 KiB of a token with no bound
+    // checks); other rows (not a whole number of 1 KiB chunks, e.g. 3.5 KiB
+    // fp4x2 rows at hidden 7168) take the narrowest of 1/2/4/7/8 chunks that
+    // covers the row (8 beyond that) with bound checks on the tail.
+    if (nTiles <= EPDC_DISPATCH_NARROW_TILES)
+        pl.cpw = nChunks <= 1 ? 1 : (!whole || nChunks % 2 == 0) ? 2 : 1;
+    else if (whole)
+        pl.cpw = nChunks % 8 == 0 ? 8 : nChunks % 7 == 0 ? 7 : nChunks % 4 == 0 ? 4 : nChunks % 2 == 0 ? 2 : 1;
+    else
+        pl.cpw = nChunks <= 1 ? 1 : nChunks <= 2 ? 2 : nChunks <= 4 ? 4 : nChunks <= 7 ? 7 : 8;
+    // Tokens per wave: one (most blocks, measured fastest at 4096 and 16384
+    // tokens) unless that would exceed 16384 blocks.
+    const int64_t perTokenWave = (int64_t)nTiles * (kTile / 4) * ceil_div(nChunks, pl.cpw);
+    pl.ntw = perTokenWave <= 16384 ? 1 : perTokenWave <= 2 * 16384 ? 2 : 4;
+#endif
+    pl.nSubs = kTile / (4 * pl.ntw);
+    pl.nSlabs = ceil_div(nChunks, pl.cpw);
+    pl.nBlocks = (int64_t)nTiles * pl.nSubs * pl.nSlabs;
+    pl.full = whole && nChunks % pl.cpw == 0;
+    // The local scan is built for one token per wave only: more tokens per
+    // wave within 8 tiles takes over 128 slabs per row (rows of 128 KiB and
+    // up), and its id registers would then cost occupancy; such launches scan
+    // through the scratch.
+    pl.local = pl.ntw == 1 && nTiles <= EPDC_DISPATCH_LOCAL_SCAN_TILES;
+    // Every block sums the earlier tiles' counts itself in launches of up to
+    // 4 blocks per CU, where it saves a round trip (measured at 4096 tokens:
+    // fp4x2 rows 2.6%, h2048 2.3%; 640 / 1024 tokens at h7168 5.3% / 3.6%).
+    // In larger launches the tile leader's one published line is faster
+    // (1.5% at 2048 blocks, 1.6% for fp8 rows at 1536).
+    pl.selfScan = !pl.local && pl.nBlocks <= EPDC_DISPATCH_SELF_SCAN_BLOCKS;
+    // x before COUNT in launches of well over one round of resident blocks
+    // (about 7 per CU, 1792 on the chip): blocks that start once HBM is
+    // saturated would otherwise idle through the SCAN's round trips, each
+    // queued behind streaming traffic.  In smaller launches the early x flood
+    // delays the SCAN instead.  Measured crossover: between 2048 blocks (after
+    // the SCAN 1-3% faster) and 3072 (before COUNT 4% faster; 8-10% at 4096).
+    // Self-summing launches whose slabs are at most 4 chunks also request x
+    // before COUNT (4096 tokens: fp4x2 rows 2.6%, h1024 2%, h2048 1%, fp8 rows
+    // at h4096 1% faster); with wider slabs there the early x delays the SCAN
+    // (2-3.5% slower with 7-chunk slabs).  (A local scan requests every load
+    // up front anyway.)
+    pl.xEarly = !pl.local && (pl.nBlocks > EPDC_DISPATCH_XEARLY_BLOCKS ||
+                              (pl.selfScan && pl.cpw <= EPDC_DISPATCH_XEARLY_SELF_CPW));
+    return pl;
+}
+
 // Launchers: enqueue on `stream`, return the hipGetLastError() after launch.
 hipError_t launch_dispatch(const DispatchParams &p, hipStream_t stream);
 hipError_t launch_combine(const CombineParams &p, bool fp32, bool landing, hipStream_t stream);

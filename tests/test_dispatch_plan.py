@@ -1,0 +1,68 @@
+"""The dispatch's launch geometry (epdc::plan_dispatch, host code the
+launcher runs) for the shapes its rules were measured on.  Every plan gives
+the same results (the GPU parity tests cover them all); this pins which one
+each shape gets, so that a rule cannot change by accident."""
+import os
+import subprocess
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+FIELDS = ("cpw", "ntw", "nSlabs", "nSubs", "nBlocks", "full", "local", "selfScan", "xEarly")
+EXPECT = {
+    # (numTokens, rowBytes): (cpw, ntw, nSlabs, nSubs, nBlocks, full, local, selfScan, xEarly)
+    # 4096 tokens x h7168 bf16: two 7-chunk slabs, 2048 blocks, tile leaders publish, x after the SCAN
+    (4096, 14336): (7, 1, 2, 16, 2048, 1, 0, 0, 0),
+    # fp8 rows: one 7-chunk slab, 1024 blocks: every block sums the counts, x after the SCAN
+    (4096, 7168): (7, 1, 1, 16, 1024, 1, 0, 1, 0),
+    # fp4x2 rows (3.5 KiB): one bound-checked 4-chunk slab, self-summing, x before COUNT
+    (4096, 3584): (4, 1, 1, 16, 1024, 0, 0, 1, 1),
+    # h2048 bf16: one 4-chunk slab, self-summing, x before COUNT
+    (4096, 4096): (4, 1, 1, 16, 1024, 1, 0, 1, 1),
+    # fp32 rows: four 7-chunk slabs, 4096 blocks: x before COUNT
+    (4096, 28672): (7, 1, 4, 16, 4096, 1, 0, 0, 1),
+    # 16384 tokens: 8192 blocks, x before COUNT
+    (16384, 14336): (7, 1, 2, 16, 8192, 1, 0, 0, 1),
+    # one tile: 2-chunk slabs (at most 4 tiles), local scan
+    (1, 14336): (2, 1, 7, 16, 112, 1, 1, 0, 0),
+    (8, 14336): (2, 1, 7, 16, 112, 1, 1, 0, 0),
+    # two tiles of odd-chunk fp8 rows: 1-chunk slabs, local scan
+    (128, 7168): (1, 1, 7, 16, 224, 1, 1, 0, 0),
+    # 8 tiles: 7-chunk slabs, still the local scan; 9 tiles: self-summing
+    (512, 14336): (7, 1, 2, 16, 256, 1, 1, 0, 0),
+    (576, 14336): (7, 1, 2, 16, 288, 1, 0, 1, 0),
+    # around the self-summing limit (1024 blocks)
+    (2047, 14336): (7, 1, 2, 16, 1024, 1, 0, 1, 0),
+    (2049, 14336): (7, 1, 2, 16, 1056, 1, 0, 0, 0),
+    # around the x-early limit (2560 blocks): 80 and 81 tiles
+    (5120, 14336): (7, 1, 2, 16, 2560, 1, 0, 0, 0),
+    (5121, 14336): (7, 1, 2, 16, 2592, 1, 0, 0, 1),
+    # 528-byte rows: more than 16384 / 32768 one-token waves take 2 / 4 tokens per wave
+    (66000, 528): (1, 2, 1, 8, 8256, 0, 0, 0, 1),
+    (132000, 528): (1, 4, 1, 4, 8252, 0, 0, 0, 1),
+    # 8-chunk slabs; rows past 8 chunks that are not whole: 8-chunk slabs with bound checks
+    (1000, 8192): (8, 1, 1, 16, 256, 1, 0, 1, 0),
+    (1000, 9728): (8, 1, 2, 16, 512, 0, 0, 1, 0),
+    # no tokens: nothing but recvCount
+    (0, 14336): (0, 0, 0, 0, 0, 0, 0, 0, 0),
+}
+
+
+def test_dispatch_plans(tmp_path):
+    import sys
+    sys.path.insert(0, ROOT)
+    from combine_count_amd import _build as B
+    exe = str(tmp_path / "dispatch_plan_check")
+    src = os.path.join(ROOT, "tests", "host", "dispatch_plan_check.cpp")
+    r = subprocess.run([B.HIPCC, *B.COMMON, src, "-o", exe], capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr
+    args = [str(v) for shape in EXPECT for v in shape]
+    r = subprocess.run([exe, *args], capture_output=True, text=True, timeout=60)
+    assert r.returncode == 0, r.stderr
+    got = {}
+    for line in r.stdout.split("\n"):
+        if line.strip():
+            v = [int(x) for x in line.split()]
+            got[(v[0], v[1])] = tuple(v[2:])
+    for shape, exp in EXPECT.items():
+        assert got.get(shape) == exp, (f"T={shape[0]} rowBytes={shape[1]}: "
+                                       f"{dict(zip(FIELDS, got.get(shape, ())))} != {dict(zip(FIELDS, exp))}")
