@@ -226,27 +226,25 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineParams P, int nSlab
     }
 }
 
+// Runs a plan (plan_combine in epdc_internal.h) with its compiled variant.
 template <int CPW, bool FP32, bool LAND>
-hipError_t launch(const CombineParams &P, hipStream_t stream) {
-    const int nSlabs = ceil_div(P.nChunks, CPW);
-    const int64_t waves = (int64_t)P.T * nSlabs;
-    if (waves > INT32_MAX - 3) return hipErrorInvalidConfiguration;
-    const dim3 grid((uint32_t)ceil_div(waves, 4));
-    const bool full = (P.rowBytes % kChunkBytes == 0) && (P.nChunks % CPW == 0);
-    if (full)
-        hipLaunchKernelGGL((combine_kernel<CPW, true, FP32, LAND>), grid, dim3(256), 0, stream, P, nSlabs);
+hipError_t launch(const CombineParams &P, const RowPlan &pl, hipStream_t stream) {
+    if (pl.waves > INT32_MAX - 3) return hipErrorInvalidConfiguration;
+    const dim3 grid((uint32_t)pl.nBlocks);
+    if (pl.full)
+        hipLaunchKernelGGL((combine_kernel<CPW, true, FP32, LAND>), grid, dim3(256), 0, stream, P, pl.nSlabs);
     else
-        hipLaunchKernelGGL((combine_kernel<CPW, false, FP32, LAND>), grid, dim3(256), 0, stream, P, nSlabs);
+        hipLaunchKernelGGL((combine_kernel<CPW, false, FP32, LAND>), grid, dim3(256), 0, stream, P, pl.nSlabs);
     return hipGetLastError();
 }
 
 template <bool FP32, bool LAND>
 hipError_t launch_dtype(const CombineParams &P, hipStream_t stream) {
+    const RowPlan pl = plan_combine(P.T, P.rowBytes);
 #if EPDC_COMBINE_CPW == 0
-    if (P.nChunks % 2 == 0 && (int64_t)P.T * (P.nChunks / 2) >= 8192) return launch<2, FP32, LAND>(P, stream);
-    return launch<1, FP32, LAND>(P, stream);
+    return pl.cpw == 2 ? launch<2, FP32, LAND>(P, pl, stream) : launch<1, FP32, LAND>(P, pl, stream);
 #else
-    return launch<EPDC_COMBINE_CPW, FP32, LAND>(P, stream);
+    return launch<EPDC_COMBINE_CPW, FP32, LAND>(P, pl, stream);
 #endif
 }
 

@@ -95,16 +95,15 @@ __global__ __launch_bounds__(256) void push_kernel(PushParams P, int nSlabs) {
     }
 }
 
+// Runs a plan (plan_push in epdc_internal.h) with its compiled variant.
 template <int CPW>
-hipError_t launch_cpw(const PushParams &P, hipStream_t stream) {
-    const int nSlabs = ceil_div(P.nChunks, CPW);
-    const int64_t waves = (int64_t)P.landRows * nSlabs;
-    if (waves > INT32_MAX - 3) return hipErrorInvalidConfiguration;
-    const dim3 grid((uint32_t)ceil_div(waves, 4));
-    if (P.rowBytes % kChunkBytes == 0 && P.nChunks % CPW == 0)
-        hipLaunchKernelGGL((push_kernel<CPW, true>), grid, dim3(256), 0, stream, P, nSlabs);
+hipError_t launch_cpw(const PushParams &P, const RowPlan &pl, hipStream_t stream) {
+    if (pl.waves > INT32_MAX - 3) return hipErrorInvalidConfiguration;
+    const dim3 grid((uint32_t)pl.nBlocks);
+    if (pl.full)
+        hipLaunchKernelGGL((push_kernel<CPW, true>), grid, dim3(256), 0, stream, P, pl.nSlabs);
     else
-        hipLaunchKernelGGL((push_kernel<CPW, false>), grid, dim3(256), 0, stream, P, nSlabs);
+        hipLaunchKernelGGL((push_kernel<CPW, false>), grid, dim3(256), 0, stream, P, pl.nSlabs);
     return hipGetLastError();
 }
 
@@ -112,23 +111,18 @@ hipError_t launch_cpw(const PushParams &P, hipStream_t stream) {
 
 hipError_t launch_combine_push(const PushParams &P, hipStream_t stream) {
     if (P.landRows == 0) return hipSuccess;
+    const RowPlan pl = plan_push(P.landRows, P.rowBytes);
 #if EPDC_PUSH_CPW == 0
-    // Slab width as in the dispatch: the widest of 8/7/4/2 chunks dividing a
-    // whole-chunk row, else the narrowest width covering the row (8 beyond).
-    if (P.rowBytes % kChunkBytes == 0) {
-        if (P.nChunks % 8 == 0) return launch_cpw<8>(P, stream);
-        if (P.nChunks % 7 == 0) return launch_cpw<7>(P, stream);
-        if (P.nChunks % 4 == 0) return launch_cpw<4>(P, stream);
-        if (P.nChunks % 2 == 0) return launch_cpw<2>(P, stream);
-        return launch_cpw<1>(P, stream);
+    switch (pl.cpw) {
+        case 1: return launch_cpw<1>(P, pl, stream);
+        case 2: return launch_cpw<2>(P, pl, stream);
+        case 4: return launch_cpw<4>(P, pl, stream);
+        case 7: return launch_cpw<7>(P, pl, stream);
+        case 8: return launch_cpw<8>(P, pl, stream);
+        default: return hipErrorInvalidConfiguration;
     }
-    if (P.nChunks <= 1) return launch_cpw<1>(P, stream);
-    if (P.nChunks <= 2) return launch_cpw<2>(P, stream);
-    if (P.nChunks <= 4) return launch_cpw<4>(P, stream);
-    if (P.nChunks <= 7) return launch_cpw<7>(P, stream);
-    return launch_cpw<8>(P, stream);
 #else
-    return launch_cpw<EPDC_PUSH_CPW>(P, stream);
+    return launch_cpw<EPDC_PUSH_CPW>(P, pl, stream);
 #endif
 }
 

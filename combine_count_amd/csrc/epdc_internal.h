@@ -269,6 +269,56 @@ inline DispatchPlan plan_dispatch(int32_t T, int32_t rowBytes) {
     return pl;
 }
 
+// Launch geometry of a combine (gather or reduce, one row per token) or a
+// push (one row per landing row): one wave per (row, slab of cpw 1 KiB
+// chunks), 4 waves per block.
+struct RowPlan {
+    int32_t cpw;      // 1 KiB chunks per slab
+    int32_t nSlabs;   // slabs per row
+    int64_t waves;    // rows * nSlabs
+    int64_t nBlocks;  // ceil(waves / 4)
+    bool full;        // every slab lies inside the row: no per-lane bound checks
+};
+
+inline RowPlan row_plan(int64_t rows, int32_t rowBytes, int32_t cpw) {
+    RowPlan pl{};
+    const int32_t nChunks = ceil_div(rowBytes, kChunkBytes);
+    pl.cpw = cpw;
+    pl.nSlabs = ceil_div(nChunks, cpw);
+    pl.waves = rows * pl.nSlabs;
+    pl.nBlocks = (pl.waves + 3) / 4;
+    pl.full = rowBytes % kChunkBytes == 0 && nChunks % cpw == 0;
+    return pl;
+}
+
+inline RowPlan plan_combine(int32_t T, int32_t rowBytes) {
+#if EPDC_COMBINE_CPW == 0
+    // 2-chunk slabs when the row splits into them evenly and that still
+    // leaves at least 8192 waves; 1-chunk slabs otherwise.
+    const int32_t nChunks = ceil_div(rowBytes, kChunkBytes);
+    const int32_t cpw = nChunks % 2 == 0 && (int64_t)T * (nChunks / 2) >= 8192 ? 2 : 1;
+#else
+    const int32_t cpw = EPDC_COMBINE_CPW;
+#endif
+    return row_plan(T, rowBytes, cpw);
+}
+
+inline RowPlan plan_push(int32_t landRows, int32_t rowBytes) {
+#if EPDC_PUSH_CPW == 0
+    // Slab width as in the dispatch: the widest of 8/7/4/2 chunks dividing a
+    // whole-chunk row, else the narrowest width covering the row (8 beyond).
+    const int32_t nChunks = ceil_div(rowBytes, kChunkBytes);
+    int32_t cpw;
+    if (rowBytes % kChunkBytes == 0)
+        cpw = nChunks % 8 == 0 ? 8 : nChunks % 7 == 0 ? 7 : nChunks % 4 == 0 ? 4 : nChunks % 2 == 0 ? 2 : 1;
+    else
+        cpw = nChunks <= 1 ? 1 : nChunks <= 2 ? 2 : nChunks <= 4 ? 4 : nChunks <= 7 ? 7 : 8;
+#else
+    const int32_t cpw = EPDC_PUSH_CPW;
+#endif
+    return row_plan(landRows, rowBytes, cpw);
+}
+
 // Launchers: enqueue on `stream`, return the hipGetLastError() after launch.
 hipError_t launch_dispatch(const DispatchParams &p, hipStream_t stream);
 hipError_t launch_combine(const CombineParams &p, bool fp32, bool landing, hipStream_t stream);

@@ -1,0 +1,29 @@
+// Prints the launch plans of csrc/epdc_internal.h (host code the launchers
+// run) for shapes given on the command line:
+//   dispatch T rowBytes ...  -> T rowBytes cpw ntw nSlabs nSubs nBlocks full local selfScan xEarly
+//   combine  T rowBytes ...  -> T rowBytes cpw nSlabs waves nBlocks full
+//   push     L rowBytes ...  -> L rowBytes cpw nSlabs waves nBlocks full   (L = landing rows)
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+
+#include "../../combine_count_amd/csrc/epdc_internal.h"
+
+int main(int argc, char **argv) {
+    if (argc < 2) return 2;
+    const char *kind = argv[1];
+    for (int i = 2; i + 1 < argc; i += 2) {
+        const int n = std::atoi(argv[i]), rowBytes = std::atoi(argv[i + 1]);
+        if (!std::strcmp(kind, "dispatch")) {
+            const epdc::DispatchPlan p = epdc::plan_dispatch(n, rowBytes);
+            std::printf("%d %d %d %d %d %d %lld %d %d %d %d\n", n, rowBytes, p.cpw, p.ntw, p.nSlabs, p.nSubs,
+                        (long long)p.nBlocks, (int)p.full, (int)p.local, (int)p.selfScan, (int)p.xEarly);
+        } else {
+            const epdc::RowPlan p =
+                !std::strcmp(kind, "combine") ? epdc::plan_combine(n, rowBytes) : epdc::plan_push(n, rowBytes);
+            std::printf("%d %d %d %d %lld %lld %d\n", n, rowBytes, p.cpw, p.nSlabs, (long long)p.waves,
+                        (long long)p.nBlocks, (int)p.full);
+        }
+    }
+    return 0;
+}

@@ -1,13 +1,15 @@
-"""The dispatch's launch geometry (epdc::plan_dispatch, host code the
-launcher runs) for the shapes its rules were measured on.  Every plan gives
-the same results (the GPU parity tests cover them all); this pins which one
-each shape gets, so that a rule cannot change by accident."""
+"""The launch geometry of the three kernels (epdc::plan_dispatch,
+plan_combine and plan_push: host code the launchers run) for the shapes
+their rules were measured on.  Every plan gives the same results (the GPU
+parity tests cover them all); this pins which one each shape gets, so that a
+rule cannot change by accident."""
 import os
 import subprocess
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
 FIELDS = ("cpw", "ntw", "nSlabs", "nSubs", "nBlocks", "full", "local", "selfScan", "xEarly")
+ROW_FIELDS = ("cpw", "nSlabs", "waves", "nBlocks", "full")
 EXPECT = {
     # (numTokens, rowBytes): (cpw, ntw, nSlabs, nSubs, nBlocks, full, local, selfScan, xEarly)
     # 4096 tokens x h7168 bf16: two 7-chunk slabs, 2048 blocks, tile leaders publish, x after the SCAN
@@ -47,22 +49,50 @@ EXPECT = {
 }
 
 
-def test_dispatch_plans(tmp_path):
-    import sys
-    sys.path.insert(0, ROOT)
-    from combine_count_amd import _build as B
-    exe = str(tmp_path / "dispatch_plan_check")
-    src = os.path.join(ROOT, "tests", "host", "dispatch_plan_check.cpp")
-    r = subprocess.run([B.HIPCC, *B.COMMON, src, "-o", exe], capture_output=True, text=True)
-    assert r.returncode == 0, r.stderr
-    args = [str(v) for shape in EXPECT for v in shape]
-    r = subprocess.run([exe, *args], capture_output=True, text=True, timeout=60)
+COMBINE = {
+    # (numTokens, rowBytes): (cpw, nSlabs, waves, nBlocks, full)
+    # 2-chunk slabs when the row splits evenly and that leaves >= 8192 waves
+    (4096, 14336): (2, 7, 28672, 7168, 1),      # bf16 out, h7168
+    (4096, 28672): (2, 14, 57344, 14336, 1),    # fp32 out
+    (4096, 4096): (2, 2, 8192, 2048, 1),        # h2048: exactly 8192 waves
+    (1024, 14336): (1, 14, 14336, 3584, 1),     # 7168 two-chunk waves: too few
+    (4000, 5632): (2, 3, 12000, 3000, 0),       # 5.5 KiB rows: 6 chunks, the last one checked
+    (8, 256): (1, 1, 8, 2, 0),                  # h128: a quarter chunk
+    (1, 14336): (1, 14, 14, 4, 1),
+}
+PUSH = {
+    # (landing rows, rowBytes): (cpw, nSlabs, waves, nBlocks, full); slab width as in the dispatch
+    (32768, 14336): (7, 2, 65536, 16384, 1),    # 4096 tokens x min(8, 8) landing rows, bf16
+    (32768, 28672): (7, 4, 131072, 32768, 1),   # fp32
+    (3072, 4096): (4, 1, 3072, 768, 1),
+    (1000, 5632): (7, 1, 1000, 250, 0),         # ragged 5.5 KiB rows
+    (8, 16384): (8, 2, 16, 4, 1),
+}
+
+
+def _run(exe, kind, table):
+    args = [str(v) for shape in table for v in shape]
+    r = subprocess.run([exe, kind, *args], capture_output=True, text=True, timeout=60)
     assert r.returncode == 0, r.stderr
     got = {}
     for line in r.stdout.split("\n"):
         if line.strip():
             v = [int(x) for x in line.split()]
             got[(v[0], v[1])] = tuple(v[2:])
-    for shape, exp in EXPECT.items():
-        assert got.get(shape) == exp, (f"T={shape[0]} rowBytes={shape[1]}: "
-                                       f"{dict(zip(FIELDS, got.get(shape, ())))} != {dict(zip(FIELDS, exp))}")
+    return got
+
+
+def test_launch_plans(tmp_path):
+    import sys
+    sys.path.insert(0, ROOT)
+    from combine_count_amd import _build as B
+    exe = str(tmp_path / "launch_plan_check")
+    src = os.path.join(ROOT, "tests", "host", "launch_plan_check.cpp")
+    r = subprocess.run([B.HIPCC, *B.COMMON, src, "-o", exe], capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr
+    for kind, table, fields in (("dispatch", EXPECT, FIELDS), ("combine", COMBINE, ROW_FIELDS),
+                                ("push", PUSH, ROW_FIELDS)):
+        got = _run(exe, kind, table)
+        for shape, exp in table.items():
+            assert got.get(shape) == exp, (f"{kind} {shape}: {dict(zip(fields, got.get(shape, ())))} "
+                                           f"!= {dict(zip(fields, exp))}")
