@@ -97,6 +97,10 @@ EDGE = [
     ("self_scan_1024_blocks_t2047", 8, 32, 2048, 2047, 8, 7168, "zipf", 1),
     ("leader_scan_1056_blocks_t2049", 8, 32, 2049, 2049, 8, 7168, "zipf", 1),
     ("self_scan_63_tiles_h128", 4, 8, 4100, 4000, 4, 128, "uniform", 1),
+    # around the x-early switch at 2560 blocks: 80 tiles (x after the SCAN), 81 tiles (x
+    # before COUNT, a last tile of one token)
+    ("x_late_2560_blocks_t5120", 8, 32, 5120, 5120, 8, 7168, "zipf", 1),
+    ("x_early_2592_blocks_t5121", 8, 32, 5121, 5121, 8, 7168, "zipf", 1),
     # self-summing with x requested before COUNT (slabs of at most 4 chunks), ragged 3.5 KiB rows
     ("self_scan_x_early_ragged_h1792", 4, 8, 1000, 1000, 5, 1792, "uniform", 1),
     # the token-count x topk grid of mori PR #599's checks, at 8 PEs / 256 experts / h7168
