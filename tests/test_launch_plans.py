@@ -96,3 +96,58 @@ def test_launch_plans(tmp_path):
         for shape, exp in table.items():
             assert got.get(shape) == exp, (f"{kind} {shape}: {dict(zip(fields, got.get(shape, ())))} "
                                            f"!= {dict(zip(fields, exp))}")
+
+
+def _gpu_parity_shapes():
+    """(numTokens, dispatch row bytes) of the dispatches the GPU parity tests run."""
+    import workloads
+    import test_gpu_parity as P
+    import test_gpu_random_shapes as R
+    wb = workloads.WIRE_BYTES
+    shapes = set()
+    for name, _ in P.CONFIG_SEEDS:
+        w = workloads.CONFIGS[name]
+        shapes.add((w.numTokens, w.dispatchHidden * wb[w.wire]))
+    for _name, _W, _Epr, _M, T, _K, H, _routing, _useW in P.EDGE:
+        shapes.add((T, H * 2))
+    for name, base, wire, comb in P.DTYPES:
+        if base is None:
+            w = workloads.Workload(name, 5, 3, 700, 650, 7, 1056, "uniform", 1, wire=wire, combineDtype=comb)
+        else:
+            w = workloads.CONFIGS[base].with_(wire=wire, combineDtype=comb)
+        rb = w.dispatchHidden * wb[wire] + (56 * 4 if name == "fp8_rows_with_block_scales" else 0)
+        shapes.add((w.numTokens, rb))
+    for _id, name, over in P.GRAPH_CASES:
+        w = workloads.CONFIGS[name].with_(**(over or {}))
+        shapes.add((w.numTokens, w.dispatchHidden * wb[w.wire]))
+    for _i, _W, _Epr, _M, T, _K, H, dt, _useW, _routing in R.CASES:
+        shapes.add((T, H * wb[dt]))
+    return sorted(shapes)
+
+
+def test_gpu_parity_reaches_the_dispatch_variants(tmp_path):
+    """The GPU parity cases run 36 of the 40 compiled dispatch variants (slab
+    width x tokens per wave x bound checks, and the local scan's) -- all but
+    7- and 8-chunk slabs at four tokens per wave (rows of 5.5 KiB and more at
+    over 132,000 tokens, the same code as the reached ones) -- and every
+    combination of SCAN form (tile leader / every block) and x order."""
+    import sys
+    sys.path.insert(0, ROOT)
+    sys.path.insert(0, os.path.join(ROOT, "tests"))
+    from combine_count_amd import _build as B
+    exe = str(tmp_path / "launch_plan_check")
+    r = subprocess.run([B.HIPCC, *B.COMMON, os.path.join(ROOT, "tests", "host", "launch_plan_check.cpp"), "-o", exe],
+                       capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr
+    shapes = [s for s in _gpu_parity_shapes() if s[0] > 0]
+    got = _run(exe, "dispatch", shapes)
+    variants, modes = set(), set()
+    for cpw, ntw, _nSlabs, _nSubs, _nBlocks, full, local, self_scan, x_early in got.values():
+        variants.add((cpw, ntw, full, local))
+        if not local:
+            modes.add((self_scan, x_early))
+    compiled = {(c, n, f, 0) for c in (1, 2, 4, 7, 8) for n in (1, 2, 4) for f in (0, 1)}
+    compiled |= {(c, 1, f, 1) for c in (1, 2, 4, 7, 8) for f in (0, 1)}
+    missing = compiled - variants
+    assert missing <= {(7, 4, 0, 0), (7, 4, 1, 0), (8, 4, 0, 0), (8, 4, 1, 0)}, sorted(missing)
+    assert modes == {(0, 0), (0, 1), (1, 0), (1, 1)}, sorted(modes)
