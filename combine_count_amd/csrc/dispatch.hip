@@ -193,9 +193,13 @@ __device__ __forceinline__ void store_token(const DispatchParams &P, const u32x4
 //   5. The last block to finish clears the published counts; the done
 //      counters wrap to zero by themselves, so the scratch is zero again for
 //      the next call (and for every replay of a captured graph).
-template <int CPW, int NTW, bool FULL, bool LOCAL>
+// XE (x before COUNT) is a compile-time choice: with it a runtime flag, the
+// compiler's waits had to cover both load orders at once (measured: the
+// 4096-token h7168 launch, which never takes the early order, 1.4% slower).
+template <int CPW, int NTW, bool FULL, bool LOCAL, bool XE>
 __global__ __launch_bounds__(256) void dispatch_kernel(DispatchParams P, int nSlabs, int nSubs, int nBlocks,
-                                                            int xEarly, int selfScan) {
+                                                            int selfScan) {
+    constexpr bool xEarly = XE;
     __shared__ uint64_t sMask[kTile];  // destination-PE set of each token of the tile
     __shared__ uint64_t sBal[64];      // per PE: which tokens of the tile go there
     __shared__ int32_t sPre[64];       // per PE: rows taken by earlier tiles
@@ -432,32 +436,27 @@ __global__ __launch_bounds__(256) void dispatch_kernel(DispatchParams P, int nSl
 }
 
 // Runs a plan (plan_dispatch in epdc_internal.h) with its compiled variant.
+template <int CPW, int NTW, bool FULL, bool LOCAL, bool XE>
+hipError_t launch_variant(const DispatchParams &P, const DispatchPlan &pl, hipStream_t stream) {
+    hipLaunchKernelGGL((dispatch_kernel<CPW, NTW, FULL, LOCAL, XE>), dim3((uint32_t)pl.nBlocks), dim3(256), 0, stream,
+                       P, pl.nSlabs, pl.nSubs, (int)pl.nBlocks, pl.selfScan ? 1 : 0);
+    return hipGetLastError();
+}
+
 template <int CPW, int NTW>
 hipError_t launch_fused(const DispatchParams &P, const DispatchPlan &pl, hipStream_t stream) {
     static_assert(kTile % (4 * NTW) == 0, "a block's tokens must tile the 64-token tile");
     if (pl.nBlocks > INT32_MAX) return hipErrorInvalidConfiguration;
-    const int nBlocks = (int)pl.nBlocks;
-    const dim3 grid(nBlocks);
-    const int xEarly = pl.xEarly ? 1 : 0;
-    const int selfScan = pl.selfScan ? 1 : 0;
     if constexpr (NTW == 1) {
-        if (pl.local) {
-            if (pl.full)
-                hipLaunchKernelGGL((dispatch_kernel<CPW, NTW, true, true>), grid, dim3(256), 0, stream, P, pl.nSlabs,
-                                   pl.nSubs, nBlocks, xEarly, selfScan);
-            else
-                hipLaunchKernelGGL((dispatch_kernel<CPW, NTW, false, true>), grid, dim3(256), 0, stream, P, pl.nSlabs,
-                                   pl.nSubs, nBlocks, xEarly, selfScan);
-            return hipGetLastError();
-        }
+        if (pl.local)  // every load is requested up front: no x-early variant
+            return pl.full ? launch_variant<CPW, NTW, true, true, false>(P, pl, stream)
+                           : launch_variant<CPW, NTW, false, true, false>(P, pl, stream);
     }
     if (pl.full)
-        hipLaunchKernelGGL((dispatch_kernel<CPW, NTW, true, false>), grid, dim3(256), 0, stream, P, pl.nSlabs,
-                           pl.nSubs, nBlocks, xEarly, selfScan);
-    else
-        hipLaunchKernelGGL((dispatch_kernel<CPW, NTW, false, false>), grid, dim3(256), 0, stream, P, pl.nSlabs,
-                           pl.nSubs, nBlocks, xEarly, selfScan);
-    return hipGetLastError();
+        return pl.xEarly ? launch_variant<CPW, NTW, true, false, true>(P, pl, stream)
+                         : launch_variant<CPW, NTW, true, false, false>(P, pl, stream);
+    return pl.xEarly ? launch_variant<CPW, NTW, false, false, true>(P, pl, stream)
+                     : launch_variant<CPW, NTW, false, false, false>(P, pl, stream);
 }
 
 template <int CPW>

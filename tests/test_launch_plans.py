@@ -126,11 +126,12 @@ def _gpu_parity_shapes():
 
 
 def test_gpu_parity_reaches_the_dispatch_variants(tmp_path):
-    """The GPU parity cases run 36 of the 40 compiled dispatch variants (slab
-    width x tokens per wave x bound checks, and the local scan's) -- all but
-    7- and 8-chunk slabs at four tokens per wave (rows of 5.5 KiB and more at
-    over 132,000 tokens, the same code as the reached ones) -- and every
-    combination of SCAN form (tile leader / every block) and x order."""
+    """The GPU parity cases reach 36 of the 40 dispatch geometries (slab width x
+    tokens per wave x bound checks, and the local scan's) -- all but 7- and
+    8-chunk slabs at four tokens per wave (rows of 5.5 KiB and more at over
+    132,000 tokens, the same code as the reached ones) -- and every combination
+    of SCAN form (tile leader / every block) and x order (each non-local
+    geometry is compiled once per x order)."""
     import sys
     sys.path.insert(0, ROOT)
     sys.path.insert(0, os.path.join(ROOT, "tests"))
