@@ -1,8 +1,9 @@
 """ctypes binding of libepdc.so (include/epdc.h), same entry-point names.
 
-Argument marshalling only: tensors become their device pointers, the stream
-defaults to torch's current stream, and a negative return code becomes an
-``EpdcError``.  Every step of dispatch and combine runs in the HIP kernels of
+Argument marshalling only: tensors become their device pointers (after a
+check that each is on the device, contiguous and at least as large as the
+call needs), the stream defaults to torch's current stream, and a negative
+return code becomes an ``EpdcError``.  Every step of dispatch and combine runs in the HIP kernels of
 libepdc.so; there is no other code path.  If the library is not built this
 module raises on first use.
 """
@@ -26,6 +27,11 @@ ERRORS = {
 }
 EXPORTS = ("epdc_dispatch_scratch_bytes", "epdc_dispatch", "epdc_combine", "epdc_landing_rows",
            "epdc_combine_push", "epdc_combine_reduce", "epdc_last_error")
+# include/epdc.h: the dispatch scratch's status word (index in 32-bit words) and its values
+EPDC_STATUS_WORD = 2
+EPDC_STATUS_WAIT_TIMEOUT = 1
+EPDC_STATUS_ROW_OUTSIDE = 2
+EPDC_MAX_SCALE_DIM = 1024
 
 
 class EpdcError(RuntimeError):
@@ -44,6 +50,7 @@ class EpCfg(ctypes.Structure):
         ("numExpertPerToken", ctypes.c_int32),
         ("dtype", ctypes.c_int32),
         ("useWeights", ctypes.c_int32),
+        ("scaleDim", ctypes.c_int32),
     ]
 
     def __repr__(self):
@@ -66,15 +73,15 @@ def load_library() -> ctypes.CDLL:
     lib.epdc_dispatch_scratch_bytes.restype = sz
     lib.epdc_dispatch_scratch_bytes.argtypes = [cfgp]
     lib.epdc_dispatch.restype = ctypes.c_int
-    lib.epdc_dispatch.argtypes = [cfgp, i32] + [p] * 10 + [sz, p]
+    lib.epdc_dispatch.argtypes = [cfgp, i32] + [p] * 12 + [sz, p]
     lib.epdc_combine.restype = ctypes.c_int
-    lib.epdc_combine.argtypes = [cfgp, i32] + [p] * 5 + [p]
+    lib.epdc_combine.argtypes = [cfgp, i32] + [p] * 5 + [i32, p]
     lib.epdc_landing_rows.restype = i32
     lib.epdc_landing_rows.argtypes = [cfgp, i32]
     lib.epdc_combine_push.restype = ctypes.c_int
     lib.epdc_combine_push.argtypes = [cfgp, i32] + [p] * 6 + [p]
     lib.epdc_combine_reduce.restype = ctypes.c_int
-    lib.epdc_combine_reduce.argtypes = [cfgp, i32] + [p] * 5 + [p]
+    lib.epdc_combine_reduce.argtypes = [cfgp, i32] + [p] * 5 + [i32, p]
     lib.epdc_last_error.restype = ctypes.c_char_p
     lib.epdc_last_error.argtypes = []
     _lib = lib
@@ -94,6 +101,69 @@ def _ptr(a):
     if not a.is_contiguous():
         raise ValueError(f"expected a contiguous tensor, got strides {tuple(a.stride())} for shape {tuple(a.shape)}")
     return a.data_ptr()
+
+
+_ELEM = {EPDC_BF16: 2, EPDC_FP32: 4, EPDC_FP8: 1, EPDC_FP4X2: 1}
+
+
+def _need(a, nbytes: int, name: str):
+    """A tensor argument must hold at least the bytes include/epdc.h states
+    for it (a short buffer would be read or written past its end on the
+    device).  Raw addresses and None pass through unchecked."""
+    if a is None or isinstance(a, int):
+        return
+    _ptr(a)  # device and layout first
+    if not hasattr(a, "element_size"):
+        return
+    have = a.numel() * a.element_size()
+    if have < nbytes:
+        raise ValueError(f"{name} holds {have} bytes, the call needs {nbytes}")
+
+
+def _sizes_dispatch(cfg, T, x, expertIds, weights, scales, recvX, recvTokIdx, recvExpertIds, recvWeights,
+                    recvScales, recvCount, sendMap):
+    W, M, H, K, S = cfg.worldSize, cfg.maxTokPerRank, cfg.hiddenDim, cfg.numExpertPerToken, cfg.scaleDim
+    eb = _ELEM.get(cfg.dtype)
+    if eb is None or T <= 0 or min(W, M, H, K) < 1 or S < 0:
+        return  # the library rejects it, or nothing token-sized is touched
+    rb = H * eb
+    for a, n, name in ((x, T * rb, "x"), (expertIds, T * K * 4, "expertIds"), (recvX, W * M * rb, "recvX"),
+                       (recvTokIdx, W * M * 4, "recvTokIdx"), (recvExpertIds, W * M * K * 4, "recvExpertIds"),
+                       (recvCount, W * 4, "recvCount"), (sendMap, T * K * 4, "sendMap"),
+                       (weights, T * K * 4 if cfg.useWeights else 0, "weights"),
+                       (recvWeights, W * M * K * 4 if cfg.useWeights else 0, "recvWeights"),
+                       (scales, T * S * 4, "scales"), (recvScales, W * M * S * 4, "recvScales")):
+        _need(a, n, name)
+
+
+def _sizes_combine(cfg, T, outDtype, y, expertIds, weights, sendMap, out, landing=False):
+    W, M, H, K = cfg.worldSize, cfg.maxTokPerRank, cfg.hiddenDim, cfg.numExpertPerToken
+    eb, ob = {EPDC_BF16: 2, EPDC_FP32: 4}.get(cfg.dtype), {EPDC_BF16: 2, EPDC_FP32: 4}.get(outDtype)
+    if eb is None or ob is None or T <= 0 or min(W, M, H, K) < 1:
+        return
+    rows = T * min(W, K) if landing else W * M
+    _need(y, rows * H * eb, "landing" if landing else "y")
+    _need(sendMap, T * K * 4, "sendMap")
+    _need(out, T * H * ob, "out")
+    if cfg.useWeights:
+        _need(weights, (rows if landing else T * K) * 4, "landScale" if landing else "weights")
+        if not landing:
+            _need(expertIds, T * K * 4, "expertIds")
+
+
+def _sizes_push(cfg, T, y, recvExpertIds, recvWeights, recvCount, landing, landScale):
+    W, M, H, K = cfg.worldSize, cfg.maxTokPerRank, cfg.hiddenDim, cfg.numExpertPerToken
+    eb = {EPDC_BF16: 2, EPDC_FP32: 4}.get(cfg.dtype)
+    if eb is None or T <= 0 or min(W, M, H, K) < 1:
+        return
+    R = T * min(W, K)
+    _need(y, W * M * H * eb, "y")
+    _need(recvCount, W * 4, "recvCount")
+    _need(landing, R * H * eb, "landing")
+    if cfg.useWeights:
+        _need(recvExpertIds, W * M * K * 4, "recvExpertIds")
+        _need(recvWeights, W * M * K * 4, "recvWeights")
+        _need(landScale, R * 4, "landScale")
 
 
 _current_stream = None
@@ -133,23 +203,31 @@ def epdc_dispatch_scratch_bytes(cfg: EpCfg) -> int:
     return load_library().epdc_dispatch_scratch_bytes(ctypes.byref(cfg))
 
 
-def epdc_dispatch(cfg: EpCfg, numTokens: int, x, expertIds, weights, recvX, recvTokIdx, recvExpertIds,
-                  recvWeights, recvCount, sendMap, scratch, scratchBytes: int | None = None,
+def epdc_dispatch(cfg: EpCfg, numTokens: int, x, expertIds, weights, scales, recvX, recvTokIdx, recvExpertIds,
+                  recvWeights, recvScales, recvCount, sendMap, scratch, scratchBytes: int | None = None,
                   stream=None, check: bool = True) -> int:
     if scratchBytes is None:
         scratchBytes = 0 if scratch is None or isinstance(scratch, int) else scratch.numel() * scratch.element_size()
+    _sizes_dispatch(cfg, numTokens, x, expertIds, weights, scales, recvX, recvTokIdx, recvExpertIds, recvWeights,
+                    recvScales, recvCount, sendMap)
     rc = (_lib or load_library()).epdc_dispatch(
-        ctypes.byref(cfg), int(numTokens), _ptr(x), _ptr(expertIds), _ptr(weights), _ptr(recvX),
-        _ptr(recvTokIdx), _ptr(recvExpertIds), _ptr(recvWeights), _ptr(recvCount), _ptr(sendMap),
-        _ptr(scratch), int(scratchBytes), _stream(stream))
+        ctypes.byref(cfg), int(numTokens), _ptr(x), _ptr(expertIds), _ptr(weights), _ptr(scales), _ptr(recvX),
+        _ptr(recvTokIdx), _ptr(recvExpertIds), _ptr(recvWeights), _ptr(recvScales), _ptr(recvCount),
+        _ptr(sendMap), _ptr(scratch), int(scratchBytes), _stream(stream))
     return _check(rc, check)
 
 
-def epdc_combine(cfg: EpCfg, numTokens: int, y, expertIds, weights, sendMap, out, stream=None,
+def _out_dtype(cfg: EpCfg, outDtype) -> int:
+    """outDtype of a combine or reduce; None means the rows' own type."""
+    return cfg.dtype if outDtype is None else int(outDtype)
+
+
+def epdc_combine(cfg: EpCfg, numTokens: int, y, expertIds, weights, sendMap, out, outDtype=None, stream=None,
                  check: bool = True) -> int:
+    _sizes_combine(cfg, numTokens, _out_dtype(cfg, outDtype), y, expertIds, weights, sendMap, out)
     rc = (_lib or load_library()).epdc_combine(
         ctypes.byref(cfg), int(numTokens), _ptr(y), _ptr(expertIds), _ptr(weights), _ptr(sendMap),
-        _ptr(out), _stream(stream))
+        _ptr(out), _out_dtype(cfg, outDtype), _stream(stream))
     return _check(rc, check)
 
 
@@ -159,18 +237,30 @@ def epdc_landing_rows(cfg: EpCfg, numTokens: int) -> int:
 
 def epdc_combine_push(cfg: EpCfg, numTokens: int, y, recvExpertIds, recvWeights, recvCount, landing, landScale,
                       stream=None, check: bool = True) -> int:
+    _sizes_push(cfg, numTokens, y, recvExpertIds, recvWeights, recvCount, landing, landScale)
     rc = (_lib or load_library()).epdc_combine_push(
         ctypes.byref(cfg), int(numTokens), _ptr(y), _ptr(recvExpertIds), _ptr(recvWeights), _ptr(recvCount),
         _ptr(landing), _ptr(landScale), _stream(stream))
     return _check(rc, check)
 
 
-def epdc_combine_reduce(cfg: EpCfg, numTokens: int, landing, landScale, recvCount, sendMap, out, stream=None,
-                        check: bool = True) -> int:
+def epdc_combine_reduce(cfg: EpCfg, numTokens: int, landing, landScale, recvCount, sendMap, out, outDtype=None,
+                        stream=None, check: bool = True) -> int:
+    _sizes_combine(cfg, numTokens, _out_dtype(cfg, outDtype), landing, None, landScale, sendMap, out, landing=True)
+    _need(recvCount, cfg.worldSize * 4, "recvCount")
     rc = (_lib or load_library()).epdc_combine_reduce(
         ctypes.byref(cfg), int(numTokens), _ptr(landing), _ptr(landScale), _ptr(recvCount), _ptr(sendMap),
-        _ptr(out), _stream(stream))
+        _ptr(out), _out_dtype(cfg, outDtype), _stream(stream))
     return _check(rc, check)
+
+
+def dispatch_status(scratch) -> int:
+    """The status word of a dispatch scratch buffer (a device tensor), read
+    after the caller's own synchronisation: 0, EPDC_STATUS_WAIT_TIMEOUT or
+    EPDC_STATUS_ROW_OUTSIDE (include/epdc.h).  One 4-byte copy to the host."""
+    import torch
+    words = scratch.view(torch.int32) if scratch.element_size() != 4 or scratch.dtype != torch.int32 else scratch
+    return int(words.reshape(-1)[EPDC_STATUS_WORD].item())
 
 
 class PreparedCall:
@@ -198,31 +288,41 @@ def _vp(a):
     return ctypes.c_void_p(p) if p is not None else None
 
 
-def prepare_dispatch(cfg: EpCfg, numTokens: int, x, expertIds, weights, recvX, recvTokIdx, recvExpertIds,
-                     recvWeights, recvCount, sendMap, scratch, scratchBytes: int | None = None) -> PreparedCall:
+def prepare_dispatch(cfg: EpCfg, numTokens: int, x, expertIds, weights, scales, recvX, recvTokIdx, recvExpertIds,
+                     recvWeights, recvScales, recvCount, sendMap, scratch,
+                     scratchBytes: int | None = None) -> PreparedCall:
     if scratchBytes is None:
         scratchBytes = 0 if scratch is None or isinstance(scratch, int) else scratch.numel() * scratch.element_size()
-    bufs = (x, expertIds, weights, recvX, recvTokIdx, recvExpertIds, recvWeights, recvCount, sendMap, scratch)
+    _sizes_dispatch(cfg, numTokens, x, expertIds, weights, scales, recvX, recvTokIdx, recvExpertIds, recvWeights,
+                    recvScales, recvCount, sendMap)
+    bufs = (x, expertIds, weights, scales, recvX, recvTokIdx, recvExpertIds, recvWeights, recvScales, recvCount,
+            sendMap, scratch)
     args = [ctypes.byref(cfg), ctypes.c_int32(int(numTokens)), *(_vp(b) for b in bufs),
             ctypes.c_size_t(int(scratchBytes))]
     return PreparedCall((_lib or load_library()).epdc_dispatch, args, (cfg, bufs))
 
 
-def prepare_combine(cfg: EpCfg, numTokens: int, y, expertIds, weights, sendMap, out) -> PreparedCall:
+def prepare_combine(cfg: EpCfg, numTokens: int, y, expertIds, weights, sendMap, out, outDtype=None) -> PreparedCall:
+    _sizes_combine(cfg, numTokens, _out_dtype(cfg, outDtype), y, expertIds, weights, sendMap, out)
     bufs = (y, expertIds, weights, sendMap, out)
-    args = [ctypes.byref(cfg), ctypes.c_int32(int(numTokens)), *(_vp(b) for b in bufs)]
+    args = [ctypes.byref(cfg), ctypes.c_int32(int(numTokens)), *(_vp(b) for b in bufs),
+            ctypes.c_int32(_out_dtype(cfg, outDtype))]
     return PreparedCall((_lib or load_library()).epdc_combine, args, (cfg, bufs))
 
 
 def prepare_combine_push(cfg: EpCfg, numTokens: int, y, recvExpertIds, recvWeights, recvCount, landing,
                          landScale) -> PreparedCall:
+    _sizes_push(cfg, numTokens, y, recvExpertIds, recvWeights, recvCount, landing, landScale)
     bufs = (y, recvExpertIds, recvWeights, recvCount, landing, landScale)
     args = [ctypes.byref(cfg), ctypes.c_int32(int(numTokens)), *(_vp(b) for b in bufs)]
     return PreparedCall((_lib or load_library()).epdc_combine_push, args, (cfg, bufs))
 
 
-def prepare_combine_reduce(cfg: EpCfg, numTokens: int, landing, landScale, recvCount, sendMap,
-                           out) -> PreparedCall:
+def prepare_combine_reduce(cfg: EpCfg, numTokens: int, landing, landScale, recvCount, sendMap, out,
+                           outDtype=None) -> PreparedCall:
+    _sizes_combine(cfg, numTokens, _out_dtype(cfg, outDtype), landing, None, landScale, sendMap, out, landing=True)
+    _need(recvCount, cfg.worldSize * 4, "recvCount")
     bufs = (landing, landScale, recvCount, sendMap, out)
-    args = [ctypes.byref(cfg), ctypes.c_int32(int(numTokens)), *(_vp(b) for b in bufs)]
+    args = [ctypes.byref(cfg), ctypes.c_int32(int(numTokens)), *(_vp(b) for b in bufs),
+            ctypes.c_int32(_out_dtype(cfg, outDtype))]
     return PreparedCall((_lib or load_library()).epdc_combine_reduce, args, (cfg, bufs))

@@ -38,6 +38,8 @@ class DispatchBuffers:
         self.recvExpertIds = torch.empty((W, M, K), dtype=torch.int32, device=device)
         self.recvWeights = (torch.empty((W, M, K), dtype=torch.float32, device=device)
                             if cfg.useWeights else None)
+        self.recvScales = (torch.empty((W, M, cfg.scaleDim), dtype=torch.float32, device=device)
+                           if cfg.scaleDim > 0 else None)
         self.recvCount = torch.empty((W,), dtype=torch.int32, device=device)
         self.sendMap = torch.empty((M, K), dtype=torch.int32, device=device)
         self.scratch = torch.zeros((nbytes + 3) // 4, dtype=torch.int32, device=device)

@@ -1,23 +1,26 @@
-// EP combine for gfx950: gather + weighted reduction, fp32 accumulate; bf16
-// rows out rounded to nearest even, or fp32 rows out unrounded.
+// EP combine for gfx950: gather + weighted reduction, fp32 accumulate; a
+// bf16 output rounded to nearest even, or the fp32 accumulator itself.
 //
 // MORI JIT v2 design doc, §5 and §9: the HIP backend's combine is a gather
 // (each token pulls the rows its PEs returned); §3.7: combine sums, so it
-// needs an arithmetic dtype (bf16 or fp32 here; §5: the HIP backend's combine
-// outputs bf16 or fp32).  mori PR #599 "Perf/ep disp 1250
-// ship", item "meta prefetch": the gather's per-token metadata (token
-// indices, weights) is loaded once, up front.
+// needs an arithmetic dtype (bf16 or fp32 rows here; §5: the HIP backend's
+// combine outputs bf16 or fp32 -- chosen apart from the rows' type).  mori PR
+// #599 "Perf/ep disp 1250 ship", item "meta prefetch": the gather's per-token
+// metadata (token indices, weights) is loaded once, up front.
 //
 // One wave64 per (token, column slab of CPW 1 KiB chunks):
-//   * lanes k < K load the token's K sendMap entries, expert ids and weights
-//     once; a ballot over "sendMap >= 0" gives the kept slots, i.e. the
-//     token's PEs in first-appearance order;
+//   * lanes k < K load the token's K sendMap entries (and, weighted, its
+//     expert ids and weights) once; a ballot over "sendMap >= 0" gives the
+//     kept slots, i.e. the token's PEs in first-appearance order;
 //   * lane k0 of a kept slot sums, in slot order from +0, the weights of the
 //     slots on its PE (read from the other lanes by shuffles);
 //   * the PE loop walks the kept slots in ascending order, a group of up to
-//     EPDC_COMBINE_GROUP rows at a time: all of a group's row loads are issued
+//     kCombineGroup rows at a time: all of a group's row loads are issued
 //     before its first FMA; every lane owns 16 contiguous bytes per chunk
-//     (8 bf16 or 4 fp32 elements), one 16-byte access.
+//     (8 bf16 or 4 fp32 elements), one 16-byte access;
+//   * the lane's elements go out as 16 bytes (bf16 rows to bf16 output, fp32
+//     to fp32), 32 bytes (bf16 rows to fp32 output) or 8 bytes (fp32 rows to
+//     bf16 output).
 // The same kernel (LAND = true) is the reduce half of the scatter combine:
 // the rows come from the packed landing rows the push wrote and each row's
 // scale from the push's forwarded scales (combine_push.hip).
@@ -60,7 +63,7 @@ __device__ __forceinline__ void load_slab(u32x4 (&v)[CPW], const uint8_t *row, i
         const int e = gc * kChunkBytes + lane * 16;
         // A lane past the row's end loads the row's first 16 bytes (in
         // bounds; its sums are never stored): no branch or wait per load.
-        v[c] = load16<EPDC_COMBINE_NT_LOAD>(row + ((FULL || (gc < nChunks && e < rowBytes)) ? e : 0));
+        v[c] = load16<kCombineNtLoad>(row + ((FULL || (gc < nChunks && e < rowBytes)) ? e : 0));
     }
 }
 
@@ -102,7 +105,8 @@ __device__ __forceinline__ void gather_reduce(float (&acc)[CPW][8], const Combin
 // LAND = true: the reduce half of the scatter combine over the landing rows
 // (combine_push.hip), with the scale each landed row carries; same order,
 // same arithmetic, so the same bits.
-template <int CPW, bool FULL, bool FP32, bool LAND>
+// FP32: fp32 returned rows (else bf16); OUT32: fp32 output (else bf16).
+template <int CPW, bool FULL, bool FP32, bool OUT32, bool LAND>
 __global__ __launch_bounds__(256) void combine_kernel(CombineParams P, int nSlabs) {
     const int lane = threadIdx.x & 63;
     const int item = blockIdx.x * 4 + (threadIdx.x >> 6);
@@ -142,9 +146,11 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineParams P, int nSlab
         if (lane < P.K) {
             const int64_t o = (int64_t)t * P.K + lane;
             flat = P.sendMap[o];
-            const int32_t e = P.expertIds[o];
-            if (e >= 0 && e < E) pe = P.eprShift >= 0 ? (e >> P.eprShift) : (e / P.Epr);
-            if (P.useWeights) w = P.weights[o];
+            if (P.useWeights) {
+                const int32_t e = P.expertIds[o];
+                if (e >= 0 && e < E) pe = P.eprShift >= 0 ? (e >> P.eprShift) : (e / P.Epr);
+                w = P.weights[o];
+            }
         }
         // Kept slots; an entry outside [0, W*M) (not written by a dispatch
         // of this cfg) counts as dropped rather than being read out of bounds.
@@ -177,7 +183,7 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineParams P, int nSlab
     // routing (~3 PEs per token) it is 5% faster than with 8, though 6%
     // slower when tokens reach ~5 PEs (uniform routing); the gather is even
     // on the former and gains on the latter with 8.
-    constexpr int kGroup = LAND ? 4 : EPDC_COMBINE_GROUP;
+    constexpr int kGroup = LAND ? 4 : kCombineGroup;
     uint64_t rem = kept;
     while (rem) {
         int32_t fl[8];
@@ -203,57 +209,67 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineParams P, int nSlab
         }
     }
 
-    uint8_t *orow = P.out + (int64_t)t * P.rowBytes;
+    // The lane's elements start at element e / (bytes per row element) of
+    // the row, so at byte e * (output element size / row element size) of
+    // the output row.
+    uint8_t *orow = P.out + (int64_t)t * P.outRowBytes;
 #pragma unroll
     for (int c = 0; c < CPW; ++c) {
         const int gc = slab * CPW + c;
         const int e = gc * kChunkBytes + lane * 16;
         if (FULL || (gc < P.nChunks && e < P.rowBytes)) {
-            u32x4 o;
-            if (FP32) {
-                o.x = __float_as_uint(acc[c][0]);
-                o.y = __float_as_uint(acc[c][1]);
-                o.z = __float_as_uint(acc[c][2]);
-                o.w = __float_as_uint(acc[c][3]);
+            if (FP32 && OUT32) {
+                store16<kCombineNtStore>(orow + e, u32x4{__float_as_uint(acc[c][0]), __float_as_uint(acc[c][1]),
+                                                         __float_as_uint(acc[c][2]), __float_as_uint(acc[c][3])});
+            } else if (FP32) {  // 4 fp32 elements -> 8 bytes of bf16
+                store8<kCombineNtStore>(orow + e / 2, u32x2{f32_to_bf16(acc[c][0]) | (f32_to_bf16(acc[c][1]) << 16),
+                                                            f32_to_bf16(acc[c][2]) | (f32_to_bf16(acc[c][3]) << 16)});
+            } else if (OUT32) {  // 8 bf16 elements -> 32 bytes of fp32
+                store16<kCombineNtStore>(orow + 2 * e, u32x4{__float_as_uint(acc[c][0]), __float_as_uint(acc[c][1]),
+                                                             __float_as_uint(acc[c][2]), __float_as_uint(acc[c][3])});
+                store16<kCombineNtStore>(orow + 2 * e + 16,
+                                         u32x4{__float_as_uint(acc[c][4]), __float_as_uint(acc[c][5]),
+                                               __float_as_uint(acc[c][6]), __float_as_uint(acc[c][7])});
             } else {
-                o.x = f32_to_bf16(acc[c][0]) | (f32_to_bf16(acc[c][1]) << 16);
-                o.y = f32_to_bf16(acc[c][2]) | (f32_to_bf16(acc[c][3]) << 16);
-                o.z = f32_to_bf16(acc[c][4]) | (f32_to_bf16(acc[c][5]) << 16);
-                o.w = f32_to_bf16(acc[c][6]) | (f32_to_bf16(acc[c][7]) << 16);
+                store16<kCombineNtStore>(orow + e, u32x4{f32_to_bf16(acc[c][0]) | (f32_to_bf16(acc[c][1]) << 16),
+                                                         f32_to_bf16(acc[c][2]) | (f32_to_bf16(acc[c][3]) << 16),
+                                                         f32_to_bf16(acc[c][4]) | (f32_to_bf16(acc[c][5]) << 16),
+                                                         f32_to_bf16(acc[c][6]) | (f32_to_bf16(acc[c][7]) << 16)});
             }
-            store16<EPDC_COMBINE_NT_STORE>(orow + e, o);
         }
     }
 }
 
 // Runs a plan (plan_combine in epdc_internal.h) with its compiled variant.
-template <int CPW, bool FP32, bool LAND>
+template <int CPW, bool FP32, bool OUT32, bool LAND>
 hipError_t launch(const CombineParams &P, const RowPlan &pl, hipStream_t stream) {
     if (pl.waves > INT32_MAX - 3) return hipErrorInvalidConfiguration;
     const dim3 grid((uint32_t)pl.nBlocks);
     if (pl.full)
-        hipLaunchKernelGGL((combine_kernel<CPW, true, FP32, LAND>), grid, dim3(256), 0, stream, P, pl.nSlabs);
+        hipLaunchKernelGGL((combine_kernel<CPW, true, FP32, OUT32, LAND>), grid, dim3(256), 0, stream, P, pl.nSlabs);
     else
-        hipLaunchKernelGGL((combine_kernel<CPW, false, FP32, LAND>), grid, dim3(256), 0, stream, P, pl.nSlabs);
+        hipLaunchKernelGGL((combine_kernel<CPW, false, FP32, OUT32, LAND>), grid, dim3(256), 0, stream, P, pl.nSlabs);
     return hipGetLastError();
 }
 
-template <bool FP32, bool LAND>
+template <bool FP32, bool OUT32, bool LAND>
 hipError_t launch_dtype(const CombineParams &P, hipStream_t stream) {
     const RowPlan pl = plan_combine(P.T, P.rowBytes);
-#if EPDC_COMBINE_CPW == 0
-    return pl.cpw == 2 ? launch<2, FP32, LAND>(P, pl, stream) : launch<1, FP32, LAND>(P, pl, stream);
-#else
-    return launch<EPDC_COMBINE_CPW, FP32, LAND>(P, pl, stream);
-#endif
+    return pl.cpw == 2 ? launch<2, FP32, OUT32, LAND>(P, pl, stream) : launch<1, FP32, OUT32, LAND>(P, pl, stream);
+}
+
+template <bool LAND>
+hipError_t launch_types(const CombineParams &P, bool fp32, bool out32, hipStream_t stream) {
+    if (fp32)
+        return out32 ? launch_dtype<true, true, LAND>(P, stream) : launch_dtype<true, false, LAND>(P, stream);
+    return out32 ? launch_dtype<false, true, LAND>(P, stream) : launch_dtype<false, false, LAND>(P, stream);
 }
 
 }  // namespace
 
-hipError_t launch_combine(const CombineParams &P, bool fp32, bool landing, hipStream_t stream) {
+hipError_t launch_combine(const CombineParams &P, bool fp32, bool out32, bool landing, hipStream_t stream) {
     if (P.T == 0) return hipSuccess;
-    if (landing) return fp32 ? launch_dtype<true, true>(P, stream) : launch_dtype<false, true>(P, stream);
-    return fp32 ? launch_dtype<true, false>(P, stream) : launch_dtype<false, false>(P, stream);
+    return landing ? launch_types<true>(P, fp32, out32, stream) : launch_types<false>(P, fp32, out32, stream);
 }
 
 }  // namespace epdc

@@ -63,7 +63,7 @@ __global__ __launch_bounds__(256) void push_kernel(PushParams P, int nSlabs) {
     for (int k = 0; k < CPW; ++k) {
         const int gc = slab * CPW + k;
         const int e = gc * kChunkBytes + lane * 16;
-        v[k] = load16<EPDC_PUSH_NT_LOAD>(srow + ((FULL || (gc < P.nChunks && e < P.rowBytes)) ? e : 0));
+        v[k] = load16<kPushNtLoad>(srow + ((FULL || (gc < P.nChunks && e < P.rowBytes)) ? e : 0));
     }
     // The row's metadata goes out behind its slab, so nothing waits for it
     // before the slab is requested.
@@ -79,7 +79,7 @@ __global__ __launch_bounds__(256) void push_kernel(PushParams P, int nSlabs) {
     for (int k = 0; k < CPW; ++k) {
         const int gc = slab * CPW + k;
         const int eb = gc * kChunkBytes + lane * 16;
-        if (FULL || (gc < P.nChunks && eb < P.rowBytes)) store16<EPDC_PUSH_NT_STORE>(drow + eb, v[k]);
+        if (FULL || (gc < P.nChunks && eb < P.rowBytes)) store16<kPushNtStore>(drow + eb, v[k]);
     }
 
     if (doScale) {
@@ -112,7 +112,6 @@ hipError_t launch_cpw(const PushParams &P, const RowPlan &pl, hipStream_t stream
 hipError_t launch_combine_push(const PushParams &P, hipStream_t stream) {
     if (P.landRows == 0) return hipSuccess;
     const RowPlan pl = plan_push(P.landRows, P.rowBytes);
-#if EPDC_PUSH_CPW == 0
     switch (pl.cpw) {
         case 1: return launch_cpw<1>(P, pl, stream);
         case 2: return launch_cpw<2>(P, pl, stream);
@@ -121,9 +120,6 @@ hipError_t launch_combine_push(const PushParams &P, hipStream_t stream) {
         case 8: return launch_cpw<8>(P, pl, stream);
         default: return hipErrorInvalidConfiguration;
     }
-#else
-    return launch_cpw<EPDC_PUSH_CPW>(P, pl, stream);
-#endif
 }
 
 }  // namespace epdc

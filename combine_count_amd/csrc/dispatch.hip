@@ -23,8 +23,8 @@
 namespace epdc {
 namespace {
 
-constexpr bool kNtLoad = EPDC_DISPATCH_NT_LOAD;
-constexpr bool kNtStore = EPDC_DISPATCH_NT_STORE;
+constexpr bool kNtLoad = kDispatchNtLoad;
+constexpr bool kNtStore = kDispatchNtStore;
 
 // PE of expert e (-1 if e is not an expert id): e / Epr by multiply-high
 // (div_magic), a few instructions for any Epr.
@@ -81,7 +81,7 @@ __device__ __noinline__ uint32_t wait_published(uint32_t *slot, uint32_t *errWor
     uint32_t v = load_published(slot);
     for (int spins = 0; v == 0; ++spins) {
         if (spins >= kMaxSpins) {
-            __hip_atomic_store(errWord, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            __hip_atomic_store(errWord, kStatusWaitTimeout, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             return 1u;
         }
         __builtin_amdgcn_s_sleep(2);
@@ -129,7 +129,7 @@ __device__ __forceinline__ void store_slab(const u32x4 (&v)[CPW], uint8_t *row, 
 // flagged and skipped rather than written.
 __device__ __forceinline__ bool row_ok(const DispatchParams &P, int32_t r) {
     if ((uint32_t)r < (uint32_t)P.M) return true;
-    __hip_atomic_store(P.scratch + kScratchError, 2u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(P.scratch + kScratchError, kStatusRowOutside, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     return false;
 }
 
@@ -163,12 +163,38 @@ __device__ __forceinline__ void store_token(const DispatchParams &P, const u32x4
     }
 }
 
+// Scales 64.. of token t to each of its destination rows (its PE mask m):
+// scale rows longer than a wave, loaded here 64 at a time (the first 64
+// travel in registers from the metadata loads).  Runs after the wave's other
+// stores, so the loads' wait also covers those stores; such rows are rare.
+__device__ __forceinline__ void copy_scale_tail(const DispatchParams &P, int32_t t, uint64_t m, uint64_t lt,
+                                             const uint64_t *sBal, const int32_t *sPre, int lane) {
+    for (int s0 = 64; s0 < P.S; s0 += 64) {
+        const bool in = s0 + lane < P.S;
+        const float v = in ? P.scales[(int64_t)t * P.S + s0 + lane] : 0.0f;
+        uint64_t rest = m;
+        while (rest) {
+            const int p = __builtin_ctzll(rest);
+            rest &= rest - 1;
+            const int32_t r = uniform((int32_t)((uint32_t)sPre[p] + (uint32_t)__popcll(sBal[p] & lt)));
+            if ((uint32_t)r >= (uint32_t)P.M) continue;  // flagged by the metadata loop
+            if (in) P.recvScales[((int64_t)p * P.M + r) * P.S + s0 + lane] = v;
+        }
+    }
+}
+
 // ------------------------------------------- COUNT + SCAN + FINALIZE
-// One kernel.  Block b = blockIdx.x = (tile * nSubs + sub) * nSlabs + slab
-// has 4 waves and copies the 4*NTW tokens [sub*4*NTW, (sub+1)*4*NTW) of a
-// 64-token tile -- NTW consecutive tokens per wave -- over chunks
-// [slab*CPW, (slab+1)*CPW).
-//   0. Launches of at most EPDC_DISPATCH_LOCAL_SCAN_TILES tiles request all
+// One kernel.  A block has 4 waves and copies the 4*NTW tokens
+// [sub*4*NTW, (sub+1)*4*NTW) of a 64-token tile -- NTW consecutive tokens per
+// wave -- over chunks [slab*CPW, (slab+1)*CPW).  Block b = blockIdx.x is
+// (tile * nSubs + sub) * nSlabs + slab, except in self-summing launches
+// (selfScan), where the tile leaders (sub 0, slab 0) come first: blocks
+// 0..nTiles-1, then every tile's other blocks in the same order.  The
+// leaders' COUNT then starts in the first blocks of the grid, before the
+// rest of it floods the memory with row loads (4096 tokens: fp4x2 rows 16.1
+// -> 15.4 us, h2048 17.2 -> 16.6; larger launches, whose blocks wait on
+// their leader, lose 2-5% with it).
+//   0. Launches of at most kLocalScanTiles tiles request all
 //      their loads first and scan locally (step 2); the others:
 //   1. COUNT (wave 0): the tile's PE masks (each lane's ids requested
 //      together) and per-PE ballots; the tile's
@@ -178,10 +204,11 @@ __device__ __forceinline__ void store_token(const DispatchParams &P, const u32x4
 //      the tile's base row on each PE and publishes it as base+1; the
 //      tile's other blocks wait for that single line (so polling traffic
 //      does not grow with the number of blocks per tile).  In launches of
-//      at most EPDC_DISPATCH_SELF_SCAN_BLOCKS blocks every block sums the
+//      at most kSelfScanBlocks blocks every block sums the
 //      counts itself (selfScan), which takes the publish-and-poll round
 //      trip off the path.
-//   3. Loads: the slab-0 waves' metadata rows, then every wave's NTW x
+//   3. Loads: the slab-0 waves' metadata rows (ids, weights and scales),
+//      then every wave's NTW x
 //      slabs (with xEarly, the x slabs go out before COUNT instead; see
 //      plan_dispatch in epdc_internal.h).
 //   4. FINALIZE: one wait for the wave's loads, then every store of its NTW
@@ -216,15 +243,31 @@ __global__ __launch_bounds__(256) void dispatch_kernel(DispatchParams P, int nSl
     if (tid < 64) sPre[tid] = 0;
     __syncthreads();
     const int b = blockIdx.x;
-    const int slab = b % nSlabs;
-    const int ts = b / nSlabs;
-    const int sub = ts % nSubs;
-    const int tile = ts / nSubs;
+    int slab, sub, tile;
+    if (selfScan) {  // leaders first
+        if (b < nTilesAll) {
+            tile = b;
+            sub = 0;
+            slab = 0;
+        } else {
+            const int per = nSubs * nSlabs - 1;  // >= 3: nSubs >= 4
+            const int bb = b - nTilesAll;
+            tile = bb / per;
+            const int r = bb - tile * per + 1;
+            sub = r / nSlabs;
+            slab = r - sub * nSlabs;
+        }
+    } else {
+        slab = b % nSlabs;
+        const int ts = b / nSlabs;
+        sub = ts % nSubs;
+        tile = ts / nSubs;
+    }
     const int32_t tok0 = tile * kTile;
     const int nTok = min(kTile, P.T - tok0);
     const int iBeg = (sub * 4 + wave) * NTW;  // this wave's tokens: [iBeg, iBeg + NTW) of the tile
     const uint8_t *xTile = P.x + (int64_t)tok0 * P.rowBytes;
-    // LOCAL (launches of at most EPDC_DISPATCH_LOCAL_SCAN_TILES tiles): every
+    // LOCAL (launches of at most kLocalScanTiles tiles): every
     // block counts the earlier tiles' tokens itself (their ids are a few KB,
     // read from L2), so there is no publishing, no cross-block wait and no
     // scratch, and every load can be issued up front -- small launches are
@@ -238,7 +281,7 @@ __global__ __launch_bounds__(256) void dispatch_kernel(DispatchParams P, int nSl
 
     // Every x slab of this wave (a token past the end of the tile re-reads
     // the last one; it is not stored), and the slab-0 waves' metadata rows
-    // (lanes are slots).
+    // (lanes are slots; with scales, lanes are also the first 64 scales).
     u32x4 buf[NTW][CPW];
     auto load_x = [&]() {
 #pragma unroll
@@ -248,18 +291,20 @@ __global__ __launch_bounds__(256) void dispatch_kernel(DispatchParams P, int nSl
         }
     };
     int32_t mid[NTW];
-    float mwt[NTW];
+    float mwt[NTW], msc[NTW];
     auto load_meta = [&]() {
 #pragma unroll
         for (int j = 0; j < NTW; ++j) {
             mid[j] = -1;
             mwt[j] = 0.0f;
+            msc[j] = 0.0f;
             const int i = iBeg + j;
             if (slab == 0 && i < nTok && lane < P.K) {
                 const int64_t o = (int64_t)(tok0 + i) * P.K + lane;
                 mid[j] = P.expertIds[o];
                 if (P.useWeights) mwt[j] = P.weights[o];
             }
+            if (slab == 0 && i < nTok && lane < P.S) msc[j] = P.scales[(int64_t)(tok0 + i) * P.S + lane];
         }
     };
     // The ids COUNT reads (wave 0: a token of the tile per lane) and, for a
@@ -269,8 +314,7 @@ __global__ __launch_bounds__(256) void dispatch_kernel(DispatchParams P, int nSl
     // of them).  With xEarly the x slabs go out first: there the blocks that
     // count sooner only reach the SCAN's wait sooner and poll it longer
     // (measured 1% slower at 16384 tokens).
-    constexpr int kScanPerWave = (EPDC_DISPATCH_LOCAL_SCAN_TILES + 2) / 4 > 0
-                                     ? (EPDC_DISPATCH_LOCAL_SCAN_TILES + 2) / 4 : 1;
+    constexpr int kScanPerWave = (kLocalScanTiles + 2) / 4 > 0 ? (kLocalScanTiles + 2) / 4 : 1;
     int32_t idOwn[8];
     int32_t idScan[kScanPerWave][8];
     if (!localScan && xEarly) load_x();
@@ -312,7 +356,7 @@ __global__ __launch_bounds__(256) void dispatch_kernel(DispatchParams P, int nSl
     // local scan counts the earlier tiles (all full) in this block instead,
     // the 4 waves taking tiles wave, wave + 4, ...
     if constexpr (localScan) {
-        static_assert(4 * kScanPerWave >= EPDC_DISPATCH_LOCAL_SCAN_TILES - 1, "every earlier tile has a wave");
+        static_assert(4 * kScanPerWave >= kLocalScanTiles - 1, "every earlier tile has a wave");
 #pragma unroll
         for (int i = 0; i < kScanPerWave; ++i) {
             const int j = wave + 4 * i;
@@ -397,9 +441,11 @@ __global__ __launch_bounds__(256) void dispatch_kernel(DispatchParams P, int nSl
                         P.recvExpertIds[(int64_t)f * P.K + lane] = mid[j];
                         if (P.useWeights) P.recvWeights[(int64_t)f * P.K + lane] = mwt[j];
                     }
+                    if (lane < P.S) P.recvScales[(int64_t)f * P.S + lane] = msc[j];
                     if (lane == 0) P.recvTokIdx[f] = t;
                 }
                 if (lane < P.K) P.sendMap[(int64_t)t * P.K + lane] = flat;
+                if (P.S > 64) copy_scale_tail(P, t, uniform64(sMask[i]), lt, sBal, sPre, lane);
             }
         }
         if (sub == 0 && wave == 0 && tok0 + kTile >= P.T && lane < P.W)
@@ -451,12 +497,15 @@ hipError_t launch_fused(const DispatchParams &P, const DispatchPlan &pl, hipStre
         if (pl.local)  // every load is requested up front: no x-early variant
             return pl.full ? launch_variant<CPW, NTW, true, true, false>(P, pl, stream)
                            : launch_variant<CPW, NTW, false, true, false>(P, pl, stream);
+        if (!pl.xEarly)
+            return pl.full ? launch_variant<CPW, NTW, true, false, false>(P, pl, stream)
+                           : launch_variant<CPW, NTW, false, false, false>(P, pl, stream);
     }
-    if (pl.full)
-        return pl.xEarly ? launch_variant<CPW, NTW, true, false, true>(P, pl, stream)
-                         : launch_variant<CPW, NTW, true, false, false>(P, pl, stream);
-    return pl.xEarly ? launch_variant<CPW, NTW, false, false, true>(P, pl, stream)
-                     : launch_variant<CPW, NTW, false, false, false>(P, pl, stream);
+    // Several tokens per wave only come with launches of over 8192 blocks,
+    // which always request x before COUNT (plan_dispatch).
+    if (!pl.xEarly) return hipErrorInvalidConfiguration;
+    return pl.full ? launch_variant<CPW, NTW, true, false, true>(P, pl, stream)
+                   : launch_variant<CPW, NTW, false, false, true>(P, pl, stream);
 }
 
 template <int CPW>
@@ -477,9 +526,6 @@ hipError_t launch_dispatch(const DispatchParams &P, hipStream_t stream) {
         return hipGetLastError();
     }
     const DispatchPlan pl = plan_dispatch(P.T, P.rowBytes);
-#if EPDC_DISPATCH_CPW != 0 && EPDC_DISPATCH_NTW != 0
-    return launch_fused<EPDC_DISPATCH_CPW, EPDC_DISPATCH_NTW>(P, pl, stream);
-#else
     switch (pl.cpw) {
         case 1: return launch_cpw<1>(P, pl, stream);
         case 2: return launch_cpw<2>(P, pl, stream);
@@ -488,7 +534,6 @@ hipError_t launch_dispatch(const DispatchParams &P, hipStream_t stream) {
         case 8: return launch_cpw<8>(P, pl, stream);
         default: return hipErrorInvalidConfiguration;
     }
-#endif
 }
 
 }  // namespace epdc

@@ -12,6 +12,10 @@
 
 #include "epdc_internal.h"
 
+static_assert(EPDC_STATUS_WORD == epdc::kScratchError, "status word offset");
+static_assert(EPDC_STATUS_WAIT_TIMEOUT == epdc::kStatusWaitTimeout, "status value");
+static_assert(EPDC_STATUS_ROW_OUTSIDE == epdc::kStatusRowOutside, "status value");
+
 namespace {
 
 thread_local std::string g_lastError;
@@ -82,6 +86,8 @@ int check_cfg(const epdc_cfg *c, int32_t numTokens, bool combine) {
                        : fail(EPDC_ERR_UNSUPPORTED, "dtype %d is not an EPDC dtype (0..3)", c->dtype);
     if (c->useWeights != 0 && c->useWeights != 1)
         return fail(EPDC_ERR_UNSUPPORTED, "useWeights must be 0 or 1, got %d", c->useWeights);
+    if (c->scaleDim < 0 || c->scaleDim > EPDC_MAX_SCALE_DIM)
+        return fail(EPDC_ERR_INVALID_ARG, "scaleDim %d outside [0, %d]", c->scaleDim, EPDC_MAX_SCALE_DIM);
     if (((int64_t)c->hiddenDim * eb) % 16 != 0)
         return fail(EPDC_ERR_ALIGN, "row of hiddenDim*%d = %lld bytes is not a multiple of 16", eb,
                     (long long)c->hiddenDim * eb);
@@ -105,6 +111,12 @@ int32_t landing_rows(const epdc_cfg *c, int32_t numTokens) {
     return numTokens * perToken;
 }
 
+// Output type of a combine or reduce: bf16 or fp32 (MORI JIT v2 design doc,
+// §5), independent of the rows' type.  -1 if it is neither.
+int32_t out_elem_bytes(int32_t outDtype) {
+    return outDtype == EPDC_BF16 ? 2 : outDtype == EPDC_FP32 ? 4 : -1;
+}
+
 int hip_status(hipError_t e, const char *what) {
     if (e == hipSuccess) return EPDC_OK;
     return fail(EPDC_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
@@ -124,9 +136,9 @@ size_t epdc_dispatch_scratch_bytes(const epdc_cfg *cfg) {
 }
 
 int epdc_dispatch(const epdc_cfg *cfg, int32_t numTokens, const void *x, const int32_t *expertIds,
-                  const float *weights, void *recvX, int32_t *recvTokIdx, int32_t *recvExpertIds,
-                  float *recvWeights, int32_t *recvCount, int32_t *sendMap, void *scratch,
-                  size_t scratchBytes, void *stream) {
+                  const float *weights, const float *scales, void *recvX, int32_t *recvTokIdx,
+                  int32_t *recvExpertIds, float *recvWeights, float *recvScales, int32_t *recvCount,
+                  int32_t *sendMap, void *scratch, size_t scratchBytes, void *stream) {
     try {
         g_lastError.clear();
         int rc = check_cfg(cfg, numTokens, false);
@@ -138,6 +150,10 @@ int epdc_dispatch(const epdc_cfg *cfg, int32_t numTokens, const void *x, const i
                 return fail(EPDC_ERR_NULLPTR, "a required dispatch pointer is NULL");
             if (cfg->useWeights && (!weights || !recvWeights))
                 return fail(EPDC_ERR_NULLPTR, "useWeights=1 needs weights and recvWeights");
+            if (cfg->scaleDim > 0 && (!scales || !recvScales))
+                return fail(EPDC_ERR_NULLPTR, "scaleDim > 0 needs scales and recvScales");
+            if (cfg->scaleDim > 0 && (!aligned(scales, 4) || !aligned(recvScales, 4)))
+                return fail(EPDC_ERR_ALIGN, "scales and recvScales must be 4-byte aligned");
             if (!aligned(x, 16) || !aligned(recvX, 16))
                 return fail(EPDC_ERR_ALIGN, "x and recvX must be 16-byte aligned");
             if (!aligned(expertIds, 4) || !aligned(recvTokIdx, 4) || !aligned(recvExpertIds, 4) ||
@@ -156,6 +172,7 @@ int epdc_dispatch(const epdc_cfg *cfg, int32_t numTokens, const void *x, const i
         P.K = cfg->numExpertPerToken;
         P.T = numTokens;
         P.useWeights = cfg->useWeights;
+        P.S = cfg->scaleDim;
         P.Wp = pow2_ceil(cfg->worldSize);
         const epdc::DivMagic dm = epdc::div_magic((uint32_t)cfg->numExpertPerRank);
         P.eprMagic = dm.magic;
@@ -166,10 +183,12 @@ int epdc_dispatch(const epdc_cfg *cfg, int32_t numTokens, const void *x, const i
         P.x = static_cast<const uint8_t *>(x);
         P.expertIds = expertIds;
         P.weights = cfg->useWeights ? weights : nullptr;
+        P.scales = cfg->scaleDim > 0 ? scales : nullptr;
         P.recvX = static_cast<uint8_t *>(recvX);
         P.recvTokIdx = recvTokIdx;
         P.recvExpertIds = recvExpertIds;
         P.recvWeights = cfg->useWeights ? recvWeights : nullptr;
+        P.recvScales = cfg->scaleDim > 0 ? recvScales : nullptr;
         P.recvCount = recvCount;
         P.sendMap = sendMap;
         P.scratch = static_cast<uint32_t *>(scratch);
@@ -180,18 +199,20 @@ int epdc_dispatch(const epdc_cfg *cfg, int32_t numTokens, const void *x, const i
 }
 
 int epdc_combine(const epdc_cfg *cfg, int32_t numTokens, const void *y, const int32_t *expertIds,
-                 const float *weights, const int32_t *sendMap, void *out, void *stream) {
+                 const float *weights, const int32_t *sendMap, void *out, int32_t outDtype, void *stream) {
     try {
         g_lastError.clear();
         int rc = check_cfg(cfg, numTokens, true);
         if (rc != EPDC_OK) return rc;
+        if (out_elem_bytes(outDtype) < 0)
+            return fail(EPDC_ERR_UNSUPPORTED, "outDtype %d is not EPDC_BF16 or EPDC_FP32", outDtype);
         if (numTokens == 0) return EPDC_OK;
-        if (!y || !expertIds || !sendMap || !out)
-            return fail(EPDC_ERR_NULLPTR, "a required combine pointer is NULL");
-        if (cfg->useWeights && !weights) return fail(EPDC_ERR_NULLPTR, "useWeights=1 needs weights");
+        if (!y || !sendMap || !out) return fail(EPDC_ERR_NULLPTR, "a required combine pointer is NULL");
+        if (cfg->useWeights && (!weights || !expertIds))
+            return fail(EPDC_ERR_NULLPTR, "useWeights=1 needs expertIds and weights");
         if (!aligned(y, 16) || !aligned(out, 16))
             return fail(EPDC_ERR_ALIGN, "y and out must be 16-byte aligned");
-        if (!aligned(expertIds, 4) || !aligned(sendMap, 4) || (cfg->useWeights && !aligned(weights, 4)))
+        if (!aligned(sendMap, 4) || (cfg->useWeights && (!aligned(weights, 4) || !aligned(expertIds, 4))))
             return fail(EPDC_ERR_ALIGN, "int32/fp32 arrays must be 4-byte aligned");
         epdc::CombineParams P{};
         P.W = cfg->worldSize;
@@ -203,13 +224,15 @@ int epdc_combine(const epdc_cfg *cfg, int32_t numTokens, const void *y, const in
         P.useWeights = cfg->useWeights;
         P.eprShift = log2_exact(cfg->numExpertPerRank);
         P.rowBytes = cfg->hiddenDim * elem_bytes(cfg->dtype, true);
+        P.outRowBytes = cfg->hiddenDim * out_elem_bytes(outDtype);
         P.nChunks = epdc::ceil_div(P.rowBytes, epdc::kChunkBytes);
         P.y = static_cast<const uint8_t *>(y);
-        P.expertIds = expertIds;
+        P.expertIds = cfg->useWeights ? expertIds : nullptr;
         P.weights = cfg->useWeights ? weights : nullptr;
         P.sendMap = sendMap;
         P.out = static_cast<uint8_t *>(out);
-        return hip_status(epdc::launch_combine(P, cfg->dtype == EPDC_FP32, false, static_cast<hipStream_t>(stream)),
+        return hip_status(epdc::launch_combine(P, cfg->dtype == EPDC_FP32, outDtype == EPDC_FP32, false,
+                                               static_cast<hipStream_t>(stream)),
                           "combine launch");
     } catch (...) {
         return fail(EPDC_ERR_HIP, "unexpected C++ exception in epdc_combine");
@@ -264,11 +287,14 @@ int epdc_combine_push(const epdc_cfg *cfg, int32_t numTokens, const void *y, con
 }
 
 int epdc_combine_reduce(const epdc_cfg *cfg, int32_t numTokens, const void *landing, const float *landScale,
-                        const int32_t *recvCount, const int32_t *sendMap, void *out, void *stream) {
+                        const int32_t *recvCount, const int32_t *sendMap, void *out, int32_t outDtype,
+                        void *stream) {
     try {
         g_lastError.clear();
         int rc = check_cfg(cfg, numTokens, true);
         if (rc != EPDC_OK) return rc;
+        if (out_elem_bytes(outDtype) < 0)
+            return fail(EPDC_ERR_UNSUPPORTED, "outDtype %d is not EPDC_BF16 or EPDC_FP32", outDtype);
         if (numTokens == 0) return EPDC_OK;
         if (!landing || !recvCount || !sendMap || !out)
             return fail(EPDC_ERR_NULLPTR, "a required reduce pointer is NULL");
@@ -287,6 +313,7 @@ int epdc_combine_reduce(const epdc_cfg *cfg, int32_t numTokens, const void *land
         P.useWeights = cfg->useWeights;
         P.eprShift = log2_exact(cfg->numExpertPerRank);
         P.rowBytes = cfg->hiddenDim * elem_bytes(cfg->dtype, true);
+        P.outRowBytes = cfg->hiddenDim * out_elem_bytes(outDtype);
         P.nChunks = epdc::ceil_div(P.rowBytes, epdc::kChunkBytes);
         P.y = static_cast<const uint8_t *>(landing);
         P.sendMap = sendMap;
@@ -294,7 +321,8 @@ int epdc_combine_reduce(const epdc_cfg *cfg, int32_t numTokens, const void *land
         P.landScale = cfg->useWeights ? landScale : nullptr;
         P.recvCount = recvCount;
         P.landRows = landing_rows(cfg, numTokens);
-        return hip_status(epdc::launch_combine(P, cfg->dtype == EPDC_FP32, true, static_cast<hipStream_t>(stream)),
+        return hip_status(epdc::launch_combine(P, cfg->dtype == EPDC_FP32, outDtype == EPDC_FP32, true,
+                                               static_cast<hipStream_t>(stream)),
                           "reduce launch");
     } catch (...) {
         return fail(EPDC_ERR_HIP, "unexpected C++ exception in epdc_combine_reduce");

@@ -43,55 +43,20 @@ __device__ __forceinline__ void wait_vmcnt() {
     __builtin_amdgcn_s_waitcnt((N & 0xF) | (0x7 << 4) | (0xF << 8) | ((N >> 4) << 14));
 }
 
-// Tuning knobs (compile-time; the defaults are the measured choices).
-#ifndef EPDC_DISPATCH_NT_LOAD
-#define EPDC_DISPATCH_NT_LOAD 0  // non-temporal loads of x
-#endif
-#ifndef EPDC_DISPATCH_NT_STORE
-#define EPDC_DISPATCH_NT_STORE 1  // non-temporal stores of recvX rows
-#endif
-#ifndef EPDC_COMBINE_NT_LOAD
-#define EPDC_COMBINE_NT_LOAD 1  // non-temporal loads of returned rows
-#endif
-#ifndef EPDC_COMBINE_NT_STORE
-#define EPDC_COMBINE_NT_STORE 1  // non-temporal stores of out rows
-#endif
-#ifndef EPDC_DISPATCH_CPW
-#define EPDC_DISPATCH_CPW 0  // 0: chosen from the shape
-#endif
-#ifndef EPDC_DISPATCH_NTW
-#define EPDC_DISPATCH_NTW 0  // tokens per wave; 0: chosen from the shape
-#endif
-#ifndef EPDC_DISPATCH_XEARLY_BLOCKS
-#define EPDC_DISPATCH_XEARLY_BLOCKS 2560  // launches of more blocks request x before COUNT
-#endif
-#ifndef EPDC_DISPATCH_SELF_SCAN_BLOCKS
-#define EPDC_DISPATCH_SELF_SCAN_BLOCKS 1024  // launches of up to this many blocks sum the tile counts in every block
-#endif
-#ifndef EPDC_DISPATCH_XEARLY_SELF_CPW
-#define EPDC_DISPATCH_XEARLY_SELF_CPW 4  // ... and self-summing launches with slabs of at most this many chunks
-#endif
-#ifndef EPDC_DISPATCH_NARROW_TILES
-#define EPDC_DISPATCH_NARROW_TILES 4  // launches of up to this many tiles use 1- or 2-chunk slabs
-#endif
-#ifndef EPDC_DISPATCH_LOCAL_SCAN_TILES
-#define EPDC_DISPATCH_LOCAL_SCAN_TILES 8  // launches of up to this many 64-token tiles scan in every block
-#endif
-#ifndef EPDC_COMBINE_GROUP
-#define EPDC_COMBINE_GROUP 8  // returned rows requested together per wave (1..8)
-#endif
-#ifndef EPDC_COMBINE_CPW
-#define EPDC_COMBINE_CPW 0  // 0: chosen from the shape
-#endif
-#ifndef EPDC_PUSH_NT_LOAD
-#define EPDC_PUSH_NT_LOAD 1  // non-temporal loads of the returned rows the push moves
-#endif
-#ifndef EPDC_PUSH_NT_STORE
-#define EPDC_PUSH_NT_STORE 1  // non-temporal stores of landing rows
-#endif
-#ifndef EPDC_PUSH_CPW
-#define EPDC_PUSH_CPW 0  // 0: chosen from the shape
-#endif
+// Measured choices (each was timed against its alternatives; the reasons
+// are with the code that uses them).
+constexpr bool kDispatchNtLoad = false;     // x rows: plain loads
+constexpr bool kDispatchNtStore = true;     // recvX rows: non-temporal stores
+constexpr bool kCombineNtLoad = true;       // returned rows: non-temporal loads
+constexpr bool kCombineNtStore = true;      // out rows: non-temporal stores
+constexpr bool kPushNtLoad = true;          // rows the push moves: non-temporal loads
+constexpr bool kPushNtStore = true;         // landing rows: non-temporal stores
+constexpr int kXEarlyBlocks = 2560;         // launches of more blocks request x before COUNT
+constexpr int kSelfScanBlocks = 1024;       // launches of up to this many blocks sum the tile counts in every block
+constexpr int kXEarlySelfCpw = 4;           // ... and self-summing launches with slabs of at most this many chunks
+constexpr int kNarrowTiles = 4;             // launches of up to this many tiles use 1- or 2-chunk slabs
+constexpr int kLocalScanTiles = 8;          // launches of up to this many 64-token tiles scan in every block
+constexpr int kCombineGroup = 8;            // returned rows requested together per wave (gather combine)
 
 // 16-byte access, optionally with the non-temporal (streaming) hint.
 template <bool NT>
@@ -108,6 +73,17 @@ __device__ __forceinline__ void store16(uint8_t *p, u32x4 v) {
         *reinterpret_cast<u32x4 *>(p) = v;
 }
 
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+// 8-byte store (four bf16 values), optionally non-temporal.
+template <bool NT>
+__device__ __forceinline__ void store8(uint8_t *p, u32x2 v) {
+    if (NT)
+        __builtin_nontemporal_store(v, reinterpret_cast<u32x2 *>(p));
+    else
+        *reinterpret_cast<u32x2 *>(p) = v;
+}
+
 // Routing tile: 64 tokens, one per lane of a wave64.
 constexpr int kTile = 64;
 // One 16-byte access per lane of a wave64 moves a 1 KiB chunk of a row
@@ -116,6 +92,7 @@ constexpr int kChunkBytes = 1024;
 
 struct DispatchParams {
     int32_t W, H, M, Epr, K, T, useWeights;
+    int32_t S;         // scaleDim: fp32 scales per token (0: none)
     int32_t rowBytes;  // H * element size of the wire dtype (a multiple of 16)
     int32_t Wp;        // W rounded up to a power of two (tile-count row stride)
     // e / Epr for any 32-bit e without a divide (div_magic): magic, shifts
@@ -125,10 +102,12 @@ struct DispatchParams {
     const uint8_t *x;
     const int32_t *expertIds;
     const float *weights;
+    const float *scales;   // [T][S], NULL when S == 0
     uint8_t *recvX;
     int32_t *recvTokIdx;
     int32_t *recvExpertIds;
     float *recvWeights;
+    float *recvScales;     // [W][M][S], NULL when S == 0
     int32_t *recvCount;
     int32_t *sendMap;
     uint32_t *scratch;  // scratch: header words, then tile counts [nTilesMax][Wp]
@@ -137,7 +116,9 @@ struct DispatchParams {
 // Dispatch scratch layout (32-bit words).  Zero-filled by the caller before
 // first use; every dispatch leaves it zeroed again (the error word aside).
 constexpr int kScratchDone = 0;    // groups finished (wraps to 0 after the last)
-constexpr int kScratchError = 2;   // set nonzero if a bounded wait ever timed out
+constexpr int kScratchError = 2;   // status word: nonzero if this buffer's outputs are invalid
+constexpr uint32_t kStatusWaitTimeout = 1;  // a bounded wait gave up
+constexpr uint32_t kStatusRowOutside = 2;   // a computed row fell outside its window
 constexpr int kDoneGroups = 32;    // blocks finished, per group b % 32, one 128-byte line each
 constexpr int kDoneStride = 32;    // words between group counters
 constexpr int kScratchGroupBase = 32;
@@ -146,12 +127,13 @@ constexpr int kScratchHeaderWords = kScratchGroupBase + kDoneGroups * kDoneStrid
 
 struct CombineParams {
     int32_t W, H, M, Epr, K, T, useWeights;
-    int32_t rowBytes;  // H * 2 (bf16) or H * 4 (fp32)
+    int32_t rowBytes;  // returned rows: H * 2 (bf16) or H * 4 (fp32)
+    int32_t outRowBytes;  // output rows: H * 2 (bf16) or H * 4 (fp32)
     int32_t eprShift;
     int32_t nChunks;   // ceil(rowBytes / kChunkBytes)
     const uint8_t *y;  // returned rows [W][M] (gather) or landing rows [landRows] (reduce)
-    const int32_t *expertIds;  // gather only
-    const float *weights;      // gather only
+    const int32_t *expertIds;  // gather with useWeights only
+    const float *weights;      // gather with useWeights only
     const int32_t *sendMap;
     uint8_t *out;
     // reduce over landing rows (scatter combine) only
@@ -215,11 +197,7 @@ inline DispatchPlan plan_dispatch(int32_t T, int32_t rowBytes) {
     const int32_t nTiles = ceil_div(T, kTile);
     const int32_t nChunks = ceil_div(rowBytes, kChunkBytes);
     const bool whole = rowBytes % kChunkBytes == 0;
-#if EPDC_DISPATCH_CPW != 0 && EPDC_DISPATCH_NTW != 0
-    pl.cpw = EPDC_DISPATCH_CPW;
-    pl.ntw = EPDC_DISPATCH_NTW;
-#else
-    // Slab width.  Launches of at most EPDC_DISPATCH_NARROW_TILES tiles are
+    // Slab width.  Launches of at most kNarrowTiles tiles are
     // bound by round trips, not bytes: 2-chunk slabs (1 for an odd chunk
     // count) spread a token's stores over more waves (64 tokens x h7168:
     // 4.9 -> 4.2 us).  Otherwise the widest of 8/7/4/2 chunks that divides
@@ -227,7 +205,7 @@ inline DispatchPlan plan_dispatch(int32_t T, int32_t rowBytes) {
     // checks); other rows (not a whole number of 1 KiB chunks, e.g. 3.5 KiB
     // fp4x2 rows at hidden 7168) take the narrowest of 1/2/4/7/8 chunks that
     // covers the row (8 beyond that) with bound checks on the tail.
-    if (nTiles <= EPDC_DISPATCH_NARROW_TILES)
+    if (nTiles <= kNarrowTiles)
         pl.cpw = nChunks <= 1 ? 1 : (!whole || nChunks % 2 == 0) ? 2 : 1;
     else if (whole)
         pl.cpw = nChunks % 8 == 0 ? 8 : nChunks % 7 == 0 ? 7 : nChunks % 4 == 0 ? 4 : nChunks % 2 == 0 ? 2 : 1;
@@ -237,7 +215,6 @@ inline DispatchPlan plan_dispatch(int32_t T, int32_t rowBytes) {
     // tokens) unless that would exceed 16384 blocks.
     const int64_t perTokenWave = (int64_t)nTiles * (kTile / 4) * ceil_div(nChunks, pl.cpw);
     pl.ntw = perTokenWave <= 16384 ? 1 : perTokenWave <= 2 * 16384 ? 2 : 4;
-#endif
     pl.nSubs = kTile / (4 * pl.ntw);
     pl.nSlabs = ceil_div(nChunks, pl.cpw);
     pl.nBlocks = (int64_t)nTiles * pl.nSubs * pl.nSlabs;
@@ -246,13 +223,13 @@ inline DispatchPlan plan_dispatch(int32_t T, int32_t rowBytes) {
     // wave within 8 tiles takes over 128 slabs per row (rows of 128 KiB and
     // up), and its id registers would then cost occupancy; such launches scan
     // through the scratch.
-    pl.local = pl.ntw == 1 && nTiles <= EPDC_DISPATCH_LOCAL_SCAN_TILES;
+    pl.local = pl.ntw == 1 && nTiles <= kLocalScanTiles;
     // Every block sums the earlier tiles' counts itself in launches of up to
     // 4 blocks per CU, where it saves a round trip (measured at 4096 tokens:
     // fp4x2 rows 2.6%, h2048 2.3%; 640 / 1024 tokens at h7168 5.3% / 3.6%).
     // In larger launches the tile leader's one published line is faster
     // (1.5% at 2048 blocks, 1.6% for fp8 rows at 1536).
-    pl.selfScan = !pl.local && pl.nBlocks <= EPDC_DISPATCH_SELF_SCAN_BLOCKS;
+    pl.selfScan = !pl.local && pl.nBlocks <= kSelfScanBlocks;
     // x before COUNT in launches of well over one round of resident blocks
     // (about 7 per CU, 1792 on the chip): blocks that start once HBM is
     // saturated would otherwise idle through the SCAN's round trips, each
@@ -264,8 +241,7 @@ inline DispatchPlan plan_dispatch(int32_t T, int32_t rowBytes) {
     // at h4096 1% faster); with wider slabs there the early x delays the SCAN
     // (2-3.5% slower with 7-chunk slabs).  (A local scan requests every load
     // up front anyway.)
-    pl.xEarly = !pl.local && (pl.nBlocks > EPDC_DISPATCH_XEARLY_BLOCKS ||
-                              (pl.selfScan && pl.cpw <= EPDC_DISPATCH_XEARLY_SELF_CPW));
+    pl.xEarly = !pl.local && (pl.nBlocks > kXEarlyBlocks || (pl.selfScan && pl.cpw <= kXEarlySelfCpw));
     return pl;
 }
 
@@ -292,19 +268,14 @@ inline RowPlan row_plan(int64_t rows, int32_t rowBytes, int32_t cpw) {
 }
 
 inline RowPlan plan_combine(int32_t T, int32_t rowBytes) {
-#if EPDC_COMBINE_CPW == 0
     // 2-chunk slabs when the row splits into them evenly and that still
     // leaves at least 8192 waves; 1-chunk slabs otherwise.
     const int32_t nChunks = ceil_div(rowBytes, kChunkBytes);
     const int32_t cpw = nChunks % 2 == 0 && (int64_t)T * (nChunks / 2) >= 8192 ? 2 : 1;
-#else
-    const int32_t cpw = EPDC_COMBINE_CPW;
-#endif
     return row_plan(T, rowBytes, cpw);
 }
 
 inline RowPlan plan_push(int32_t landRows, int32_t rowBytes) {
-#if EPDC_PUSH_CPW == 0
     // Slab width as in the dispatch: the widest of 8/7/4/2 chunks dividing a
     // whole-chunk row, else the narrowest width covering the row (8 beyond).
     const int32_t nChunks = ceil_div(rowBytes, kChunkBytes);
@@ -313,15 +284,12 @@ inline RowPlan plan_push(int32_t landRows, int32_t rowBytes) {
         cpw = nChunks % 8 == 0 ? 8 : nChunks % 7 == 0 ? 7 : nChunks % 4 == 0 ? 4 : nChunks % 2 == 0 ? 2 : 1;
     else
         cpw = nChunks <= 1 ? 1 : nChunks <= 2 ? 2 : nChunks <= 4 ? 4 : nChunks <= 7 ? 7 : 8;
-#else
-    const int32_t cpw = EPDC_PUSH_CPW;
-#endif
     return row_plan(landRows, rowBytes, cpw);
 }
 
 // Launchers: enqueue on `stream`, return the hipGetLastError() after launch.
 hipError_t launch_dispatch(const DispatchParams &p, hipStream_t stream);
-hipError_t launch_combine(const CombineParams &p, bool fp32, bool landing, hipStream_t stream);
+hipError_t launch_combine(const CombineParams &p, bool fp32, bool out32, bool landing, hipStream_t stream);
 hipError_t launch_combine_push(const PushParams &p, hipStream_t stream);
 
 }  // namespace epdc

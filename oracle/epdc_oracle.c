@@ -17,8 +17,13 @@
  *   M  = maxTokPerRank       T   = numTokens (0 <= T <= M)
  * Row element types (the pages' EpDType, MORI JIT v2 design doc, §3.7):
  * dispatch moves rows of H elements of 2 (bf16), 4 (fp32) or 1 byte (fp8,
- * and fp4x2 where H counts bytes); combine reduces bf16 or fp32 rows.
+ * and fp4x2 where H counts bytes); combine reduces bf16 or fp32 rows and
+ * writes bf16 or fp32 rows (§5: the combine's output is bf16 or fp32).
  * bf16 values travel as their 16-bit patterns (uint16_t).
+ *   S  = scaleDim: fp32 quantisation scales per token that the dispatch
+ *        forwards with the token (0 = none; MORI JIT v2 §4 and §5, the
+ *        dispatch's `scales` argument and the `out_scales` region that exists
+ *        only when scale_dim > 0).
  *
  * The scatter (push) combine at the end of this file is a second form of
  * combine: the rows go to packed landing rows first, then a reduction.
@@ -80,6 +85,12 @@ static int32_t dest_pe(int32_t e, int32_t W, int32_t Epr) {
  *   - window stride maxTokPerRank rows, flat index p*M + r, null = -1;
  *   - per received row: source token index, the token's K expert ids and
  *     its K weights (weights only when useWeights);
+ *   - with S > 0, also the token's S scales: a fourth metadata field that
+ *     travels with the row (the mori PR #599 page, in the merge notes of the
+ *     branch that transports scales, keeps a per-token scale row beside the
+ *     other metadata fields; MORI JIT v2 §9 names forwarding of per-token
+ *     scales as a FlyDSL-backend feature).  Like the others it is copied
+ *     bitwise;
  *   - ids outside [0, E) are dropped slots (null entry, no row);
  *   - recvCount is stored, not accumulated (mori PR #599 follow-up commits:
  *     the dispatch stores the received count so callers need no reset).
@@ -89,11 +100,12 @@ static int32_t dest_pe(int32_t e, int32_t W, int32_t Epr) {
  * Returns 0, or -1 on a bad size.
  */
 int oracle_dispatch(int32_t W, int32_t H, int32_t M, int32_t Epr, int32_t K,
-                    int32_t useWeights, int32_t T, int32_t elemBytes,
+                    int32_t useWeights, int32_t T, int32_t elemBytes, int32_t S,
                     const void *x, const int32_t *expertIds, const float *weights,
-                    void *recvX, int32_t *recvTokIdx, int32_t *recvExpertIds,
-                    float *recvWeights, int32_t *recvCount, int32_t *sendMap) {
-    if (W <= 0 || H <= 0 || M <= 0 || Epr <= 0 || K <= 0 || T < 0 || T > M) return -1;
+                    const float *scales, void *recvX, int32_t *recvTokIdx,
+                    int32_t *recvExpertIds, float *recvWeights, float *recvScales,
+                    int32_t *recvCount, int32_t *sendMap) {
+    if (W <= 0 || H <= 0 || M <= 0 || Epr <= 0 || K <= 0 || T < 0 || T > M || S < 0) return -1;
     if (elemBytes != 1 && elemBytes != 2 && elemBytes != 4) return -1;
     const int64_t rowBytes = (int64_t)H * elemBytes;
     const unsigned char *xb = (const unsigned char *)x;
@@ -119,6 +131,8 @@ int oracle_dispatch(int32_t W, int32_t H, int32_t M, int32_t Epr, int32_t K,
             memcpy(recvExpertIds + row * K, expertIds + (int64_t)t * K, (size_t)K * sizeof(int32_t));
             if (useWeights)
                 memcpy(recvWeights + row * K, weights + (int64_t)t * K, (size_t)K * sizeof(float));
+            if (S > 0)
+                memcpy(recvScales + row * S, scales + (int64_t)t * S, (size_t)S * sizeof(float));
             sendMap[(int64_t)t * K + k] = (int32_t)row;
         }
     }
@@ -138,9 +152,11 @@ int oracle_dispatch(int32_t W, int32_t H, int32_t M, int32_t Epr, int32_t K,
  *     the weights of every slot of t whose expert lives on p (valid ids
  *     only); with useWeights == 0 it is 1;
  *   - accumulation in fp32 from +0 with one fused multiply-add per PE;
- *   - bf16 rows: output rounded to bf16, nearest-even; fp32 rows: the fp32
- *     accumulator is the output (MORI JIT v2 §5: the combine reduces bf16 or
- *     fp32 rows; byte types cannot be summed, §3.7);
+ *   - the returned rows are bf16 or fp32 (inFp32), and so is the output
+ *     (outFp32), chosen independently (MORI JIT v2 §5: the combine reduces
+ *     bf16 or fp32 rows and outputs bf16 or fp32; byte types cannot be
+ *     summed, §3.7): a bf16 output is the accumulator rounded to bf16,
+ *     nearest-even, an fp32 output is the accumulator itself;
  *   - a token with no kept slot gives a +0 row.
  */
 /* acc[h] = fmaf(s, row[h], acc[h]) over one returned row (bf16 bits or fp32). */
@@ -165,7 +181,7 @@ static void store_row(void *outRow, const float *acc, int32_t H, int32_t fp32) {
 }
 
 static void combine_token(int32_t W, int32_t H, int32_t M, int32_t Epr, int32_t K,
-                          int32_t useWeights, int32_t fp32, int32_t t,
+                          int32_t useWeights, int32_t inFp32, int32_t outFp32, int32_t t,
                           const void *y, const int32_t *expertIds, const float *weights,
                           const int32_t *sendMap, float *acc, void *outRow) {
     for (int32_t h = 0; h < H; ++h) acc[h] = 0.0f;
@@ -182,31 +198,32 @@ static void combine_token(int32_t W, int32_t H, int32_t M, int32_t Epr, int32_t 
                     s = s + weights[(int64_t)t * K + k];
         }
         const int64_t row = (int64_t)p * M + r;
-        fma_row(acc, s, (const unsigned char *)y + row * H * (fp32 ? 4 : 2), H, fp32);
+        fma_row(acc, s, (const unsigned char *)y + row * H * (inFp32 ? 4 : 2), H, inFp32);
     }
-    store_row(outRow, acc, H, fp32);
+    store_row(outRow, acc, H, outFp32);
 }
 
 /*
- * COMBINE over tokens, of bf16 rows (fp32 == 0) or fp32 rows (fp32 == 1).
+ * COMBINE over tokens, of bf16 rows (inFp32 == 0) or fp32 rows (inFp32 ==
+ * 1) into bf16 (outFp32 == 0) or fp32 (outFp32 == 1) output rows.
  * With tokens == NULL every token t in [0, T) is combined into out[t][:].  Otherwise out[i][:] receives token tokens[i]
  * for i in [0, nList): the per-token form used to check sampled outputs of
  * large runs.  acc is caller scratch of H floats.
  * Returns 0, or -1 on a bad size or token index.
  */
 int oracle_combine(int32_t W, int32_t H, int32_t M, int32_t Epr, int32_t K,
-                   int32_t useWeights, int32_t T, int32_t fp32,
+                   int32_t useWeights, int32_t T, int32_t inFp32, int32_t outFp32,
                    const void *y, const int32_t *expertIds, const float *weights,
                    const int32_t *sendMap, const int32_t *tokens, int32_t nList,
                    float *acc, void *out) {
     if (W <= 0 || H <= 0 || M <= 0 || Epr <= 0 || K <= 0 || T < 0 || T > M) return -1;
-    if (fp32 != 0 && fp32 != 1) return -1;
-    const int64_t outRowBytes = (int64_t)H * (fp32 ? 4 : 2);
+    if ((inFp32 != 0 && inFp32 != 1) || (outFp32 != 0 && outFp32 != 1)) return -1;
+    const int64_t outRowBytes = (int64_t)H * (outFp32 ? 4 : 2);
     int32_t n = tokens ? nList : T;
     for (int32_t i = 0; i < n; ++i) {
         int32_t t = tokens ? tokens[i] : i;
         if (t < 0 || t >= T) return -1;
-        combine_token(W, H, M, Epr, K, useWeights, fp32, t, y, expertIds, weights, sendMap,
+        combine_token(W, H, M, Epr, K, useWeights, inFp32, outFp32, t, y, expertIds, weights, sendMap,
                       acc, (unsigned char *)out + (int64_t)i * outRowBytes);
     }
     return 0;
@@ -238,7 +255,7 @@ int oracle_combine(int32_t W, int32_t H, int32_t M, int32_t Epr, int32_t K,
  *   - REDUCE is what the source does: for token t, its kept slots (sendMap
  *     >= 0) in ascending order give (p, r) and so the landing row; from +0,
  *     acc = fmaf(scale, row, acc) in fp32 (scale 1 without useWeights),
- *     then bf16 nearest-even or the fp32 value, as in oracle_combine.
+ *     then a bf16 (nearest-even) or fp32 output row, as in oracle_combine.
  *   So push then reduce gives oracle_combine's bits.
  */
 
@@ -282,14 +299,15 @@ int oracle_combine_push(int32_t W, int32_t H, int32_t M, int32_t Epr, int32_t K,
  * Returns 0, or -1 on a bad size, count or token index, or a kept slot whose
  * landing row is outside [0, U). */
 int oracle_combine_reduce(int32_t W, int32_t H, int32_t M, int32_t Epr, int32_t K,
-                          int32_t useWeights, int32_t T, int32_t fp32,
+                          int32_t useWeights, int32_t T, int32_t inFp32, int32_t outFp32,
                           const void *landing, const float *landScale, const int32_t *recvCount,
                           const int32_t *sendMap, const int32_t *tokens, int32_t nList,
                           float *acc, void *out) {
     if (W <= 0 || H <= 0 || M <= 0 || Epr <= 0 || K <= 0 || T < 0 || T > M) return -1;
-    if (fp32 != 0 && fp32 != 1) return -1;
+    if ((inFp32 != 0 && inFp32 != 1) || (outFp32 != 0 && outFp32 != 1)) return -1;
     (void)Epr;
-    const int64_t rowBytes = (int64_t)H * (fp32 ? 4 : 2);
+    const int64_t rowBytes = (int64_t)H * (inFp32 ? 4 : 2);
+    const int64_t outRowBytes = (int64_t)H * (outFp32 ? 4 : 2);
     int64_t *landOff = (int64_t *)malloc(sizeof(int64_t) * (size_t)(W + 1));
     if (!landOff) return -1;
     landOff[0] = 0;
@@ -312,9 +330,9 @@ int oracle_combine_reduce(int32_t W, int32_t H, int32_t M, int32_t Epr, int32_t 
             if (p >= W || landOff[p] + r >= landOff[W]) { rc = -1; break; }
             int64_t L = landOff[p] + r;
             float s = useWeights ? landScale[L] : 1.0f;
-            fma_row(acc, s, lb + L * rowBytes, H, fp32);
+            fma_row(acc, s, lb + L * rowBytes, H, inFp32);
         }
-        store_row((unsigned char *)out + (int64_t)i * rowBytes, acc, H, fp32);
+        store_row((unsigned char *)out + (int64_t)i * outRowBytes, acc, H, outFp32);
     }
     free(landOff);
     return rc;

@@ -28,7 +28,10 @@ SENT_W = -3.5
 SENT_MAP = -99
 SENT_LAND_BYTE = 0xA5     # landing rows before the push (the oracle's fill too)
 SENT_SCALE = -3.25
-FILL = {"recvX_byte": SENT_X_BYTE, "recvTokIdx": SENT_I32, "recvExpertIds": SENT_IDS, "recvWeights": SENT_W}
+SENT_RECV_SCALES = -6.75
+FILL = {"recvX_byte": SENT_X_BYTE, "recvTokIdx": SENT_I32, "recvExpertIds": SENT_IDS, "recvWeights": SENT_W,
+        "recvScales": SENT_RECV_SCALES}
+OUT_BYTES = {"bf16": 2, "fp32": 4}
 
 
 def cfg_of(w: workloads.Workload, combine: bool = False) -> epdc.EpCfg:
@@ -38,7 +41,7 @@ def cfg_of(w: workloads.Workload, combine: bool = False) -> epdc.EpCfg:
         return epdc.EpCfg(w.worldSize, w.hiddenDim, w.maxTokPerRank, w.numExpertPerRank, w.numExpertPerToken,
                           workloads.EPDC_DTYPE[w.combineDtype], w.useWeights)
     return epdc.EpCfg(w.worldSize, w.dispatchHidden, w.maxTokPerRank, w.numExpertPerRank, w.numExpertPerToken,
-                      workloads.EPDC_DTYPE[w.wire], w.useWeights)
+                      workloads.EPDC_DTYPE[w.wire], w.useWeights, w.scaleDim)
 
 
 def to_dev_bytes(a: np.ndarray, dev="cuda") -> torch.Tensor:
@@ -65,10 +68,14 @@ class DeviceRun:
         self.ccfg = cfg_of(w, combine=True)
         W, M, K, T = w.worldSize, w.maxTokPerRank, w.numExpertPerToken, w.numTokens
         rowB = w.dispatchHidden * workloads.WIRE_BYTES[w.wire]
-        outB = w.hiddenDim * workloads.WIRE_BYTES[w.combineDtype]
+        outB = w.hiddenDim * OUT_BYTES[w.outType]
+        self.outDtype = workloads.EPDC_DTYPE[w.outType]
         self.x = to_dev_bytes(inp.x, dev)
         self.ids = torch.from_numpy(inp.expertIds).to(dev)
         self.wts = torch.from_numpy(inp.weights).to(dev) if w.useWeights else None
+        S = w.scaleDim
+        self.scales = torch.from_numpy(inp.scales).to(dev) if S else None
+        self.recvScales = torch.full((W, M, S), SENT_RECV_SCALES, dtype=torch.float32, device=dev) if S else None
         self.y = to_dev_bytes(inp.y, dev) if inp.y is not None else None
         self.recvX = torch.full((W, M, rowB), SENT_X_BYTE, dtype=torch.uint8, device=dev)
         self.recvTokIdx = torch.full((W, M), SENT_I32, dtype=torch.int32, device=dev)
@@ -99,7 +106,7 @@ class DeviceRun:
         w = self.w
         return epdc.epdc_combine_reduce(self.ccfg, w.numTokens, self.landing,
                                         self.landScale if w.useWeights else None, self.recvCount, self.sendMap,
-                                        self.out, stream=stream)
+                                        self.out, self.outDtype, stream=stream)
 
     def prepare(self):
         """Prepared calls (arguments marshalled once) for the same buffers:
@@ -107,11 +114,12 @@ class DeviceRun:
         p_reduce."""
         w = self.w
         wt = self.wts if w.useWeights else None
-        self.p_dispatch = epdc.prepare_dispatch(self.cfg, w.numTokens, self.x, self.ids, wt, self.recvX,
+        self.p_dispatch = epdc.prepare_dispatch(self.cfg, w.numTokens, self.x, self.ids, wt, self.scales, self.recvX,
                                                 self.recvTokIdx, self.recvExpertIds,
-                                                self.recvWeights if w.useWeights else None, self.recvCount,
-                                                self.sendMap, self.scratch)
-        self.p_combine = epdc.prepare_combine(self.ccfg, w.numTokens, self.y, self.ids, wt, self.sendMap, self.out)
+                                                self.recvWeights if w.useWeights else None, self.recvScales,
+                                                self.recvCount, self.sendMap, self.scratch)
+        self.p_combine = epdc.prepare_combine(self.ccfg, w.numTokens, self.y, self.ids if w.useWeights else None, wt,
+                                              self.sendMap, self.out, self.outDtype)
         if hasattr(self, "landing"):
             self.p_push = epdc.prepare_combine_push(self.ccfg, w.numTokens, self.y,
                                                     self.recvExpertIds if w.useWeights else None,
@@ -119,38 +127,39 @@ class DeviceRun:
                                                     self.landing, self.landScale if w.useWeights else None)
             self.p_reduce = epdc.prepare_combine_reduce(self.ccfg, w.numTokens, self.landing,
                                                         self.landScale if w.useWeights else None, self.recvCount,
-                                                        self.sendMap, self.out)
+                                                        self.sendMap, self.out, self.outDtype)
         return self
 
     def scratch_clean(self) -> bool:
-        """After a dispatch the scratch is all zero again (error flag included)."""
+        """After a dispatch the scratch is all zero again (status word included)."""
         return bool((self.scratch == 0).all().item())
 
     def dispatch(self, stream=None):
         w = self.w
-        return epdc.epdc_dispatch(self.cfg, w.numTokens, self.x, self.ids, self.wts, self.recvX,
+        return epdc.epdc_dispatch(self.cfg, w.numTokens, self.x, self.ids, self.wts, self.scales, self.recvX,
                                   self.recvTokIdx, self.recvExpertIds,
-                                  self.recvWeights if w.useWeights else None, self.recvCount,
+                                  self.recvWeights if w.useWeights else None, self.recvScales, self.recvCount,
                                   self.sendMap, self.scratch, stream=stream)
 
     def combine(self, y=None, weights="default", stream=None):
         w = self.w
         wts = self.wts if weights == "default" else weights
-        return epdc.epdc_combine(self.ccfg, w.numTokens, self.y if y is None else y, self.ids,
-                                 wts if w.useWeights else None, self.sendMap, self.out, stream=stream)
+        return epdc.epdc_combine(self.ccfg, w.numTokens, self.y if y is None else y,
+                                 self.ids if w.useWeights else None, wts if w.useWeights else None, self.sendMap,
+                                 self.out, self.outDtype, stream=stream)
 
 
 def oracle_dispatch(w: workloads.Workload, inp: workloads.Inputs):
     return _oracle().dispatch(w.worldSize, w.dispatchHidden, w.maxTokPerRank, w.numExpertPerRank,
                            w.numExpertPerToken, w.useWeights, inp.x, inp.expertIds,
-                           inp.weights if w.useWeights else None, fill=FILL)
+                           inp.weights if w.useWeights else None, inp.scales, fill=FILL)
 
 
 def oracle_combine(w: workloads.Workload, y_bits, inp: workloads.Inputs, sendMap, tokens=None, weights=None):
     wts = inp.weights if weights is None else weights
     return _oracle().combine(w.worldSize, w.hiddenDim, w.maxTokPerRank, w.numExpertPerRank,
                           w.numExpertPerToken, w.useWeights, y_bits, inp.expertIds,
-                          wts if w.useWeights else None, sendMap, tokens=tokens)
+                          wts if w.useWeights else None, sendMap, tokens=tokens, out_fp32=w.outType == "fp32")
 
 
 def oracle_push(w: workloads.Workload, y, o):
@@ -164,7 +173,7 @@ def oracle_push(w: workloads.Workload, y, o):
 def oracle_reduce(w: workloads.Workload, landing, landScale, o, tokens=None):
     return _oracle().combine_reduce(w.worldSize, w.hiddenDim, w.maxTokPerRank, w.numExpertPerRank,
                                  w.numExpertPerToken, w.useWeights, landing, landScale, o.recvCount, o.sendMap,
-                                 tokens=tokens)
+                                 tokens=tokens, out_fp32=w.outType == "fp32")
 
 
 def assert_landing_equal(g: DeviceRun, landing, landScale, tag=""):
@@ -199,6 +208,12 @@ def assert_dispatch_equal(g: DeviceRun, o, tag=""):
         assert np.array_equal(wt.view(np.uint32), o.recvWeights.view(np.uint32)), f"{tag} recvWeights differs"
     else:
         assert (wt == np.float32(SENT_W)).all(), f"{tag} recvWeights written with useWeights=0"
+    if w.scaleDim:
+        sc = g.recvScales.cpu().numpy()
+        if not np.array_equal(sc.view(np.uint32), o.recvScales.view(np.uint32)):
+            bad = np.argwhere(sc.view(np.uint32) != o.recvScales.view(np.uint32))[0]
+            raise AssertionError(f"{tag} recvScales differs first at {bad.tolist()}: {sc[tuple(bad)]} vs "
+                                 f"{o.recvScales[tuple(bad)]}")
     rx = g.recvX.cpu().numpy()
     ox = o.recvX.view(np.uint8).reshape(rx.shape)
     if not np.array_equal(rx, ox):
@@ -207,8 +222,8 @@ def assert_dispatch_equal(g: DeviceRun, o, tag=""):
 
 
 def out_as(g: DeviceRun) -> np.ndarray:
-    """The device out rows as the combine type (uint16 bf16 bits or float32)."""
-    dt = np.uint16 if g.w.combineDtype == "bf16" else np.float32
+    """The device out rows as the output type (uint16 bf16 bits or float32)."""
+    dt = np.uint16 if g.w.outType == "bf16" else np.float32
     return g.out.cpu().numpy().view(dt)
 
 

@@ -41,7 +41,8 @@ import workloads
 
 GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
 
-SENTINEL = {"recvX_byte": 0xAD, "recvTokIdx": -12345, "recvExpertIds": -777, "recvWeights": -3.5}
+SENTINEL = {"recvX_byte": 0xAD, "recvTokIdx": -12345, "recvExpertIds": -777, "recvWeights": -3.5,
+            "recvScales": -6.75}
 
 
 # --------------------------------------------------------------------------
@@ -71,9 +72,9 @@ def brute_dispatch(W, Epr, K, M, ids):
     return count, rowOf, firstSlot
 
 
-def compare_dispatch_with_brute(W, Epr, K, M, H, useWeights, x, ids, wts, lib, tag):
+def compare_dispatch_with_brute(W, Epr, K, M, H, useWeights, x, ids, wts, lib, tag, scales=None):
     fails = []
-    out = oracle.dispatch(W, H, M, Epr, K, useWeights, x, ids, wts if useWeights else None,
+    out = oracle.dispatch(W, H, M, Epr, K, useWeights, x, ids, wts if useWeights else None, scales,
                           fill=SENTINEL, lib=lib)
     count, rowOf, firstSlot = brute_dispatch(W, Epr, K, M, ids)
     T = ids.shape[0]
@@ -94,7 +95,12 @@ def compare_dispatch_with_brute(W, Epr, K, M, H, useWeights, x, ids, wts, lib, t
             fails.append(f"{tag}: recvExpertIds[{p}][{r}] != ids[{t}]")
         if useWeights and not np.array_equal(out.recvWeights[p, r].view(np.uint32), wts[t].view(np.uint32)):
             fails.append(f"{tag}: recvWeights[{p}][{r}] != weights[{t}]")
+        if scales is not None and not np.array_equal(out.recvScales[p, r].view(np.uint32),
+                                                     scales[t].view(np.uint32)):
+            fails.append(f"{tag}: recvScales[{p}][{r}] != scales[{t}]")
     for p in range(W):
+        if scales is not None and not (out.recvScales[p, count[p]:] == np.float32(SENTINEL["recvScales"])).all():
+            fails.append(f"{tag}: rows past recvCount[{p}] of recvScales were written")
         if not (out.recvX[p, count[p]:].view(np.uint8) == SENTINEL["recvX_byte"]).all():
             fails.append(f"{tag}: rows past recvCount[{p}] of recvX were written")
         if not (out.recvTokIdx[p, count[p]:] == SENTINEL["recvTokIdx"]).all():
@@ -124,8 +130,11 @@ def check_brute_force_exhaustive(lib, max_cases=6000):
             x = rng.integers(0, 1 << 16, size=(T, H), dtype=np.uint16)
             wts = rng.standard_normal((T, K)).astype(np.float32)
             useW = int(cases % 2 == 0)
+            # every third case forwards 1..5 per-token scales (bit patterns of any kind, NaNs included)
+            sc = (rng.integers(0, 1 << 32, size=(T, cases % 5 + 1), dtype=np.uint64).astype(np.uint32)
+                  .view(np.float32) if cases % 3 == 0 else None)
             fails += compare_dispatch_with_brute(W, Epr, K, M, H, useW, x, ids, wts, lib,
-                                                 f"W{W} Epr{Epr} T{T} K{K} ids{c}")
+                                                 f"W{W} Epr{Epr} T{T} K{K} ids{c}", scales=sc)
             cases += 1
             if fails or cases >= max_cases:
                 return fails
@@ -159,8 +168,9 @@ def check_brute_force_random(lib):
         ids = rng.integers(-1, E + 1, size=(T, K)).astype(np.int32)
         x = _random_rows(rng, T, H, i)
         wts = rng.standard_normal((T, K)).astype(np.float32)
+        sc = rng.standard_normal((T, int(rng.integers(1, 71)))).astype(np.float32) if i % 2 else None
         fails += compare_dispatch_with_brute(W, Epr, K, M, H, (i // 4) % 2, x, ids, wts, lib,
-                                             f"rand{i} {x.dtype}")
+                                             f"rand{i} {x.dtype} S={0 if sc is None else sc.shape[1]}", scales=sc)
         if fails:
             break
     return fails
@@ -208,6 +218,8 @@ def check_worked_example(lib):
                for part in d["expect_recvTokIdx"].split(";")}
     exp_ids = _per_pe(d["expect_recvExpertIds"], int)
     exp_wts = _per_pe(d["expect_recvWeights"], float)
+    scales = np.array([[float(v) for v in r.split()] for r in d["scales"].split(";")], dtype=np.float32)
+    exp_scl = _per_pe(d["expect_recvScales"], float)
     # returned rows: constant per (PE, window row), as bf16 bits and as fp32
     y32 = np.zeros((W, M, H), dtype=np.float32)
     for part in d["y_row_values"].split(";"):
@@ -222,7 +234,8 @@ def check_worked_example(lib):
         x, y = (x32, y32) if fp32 else (x16, y16)
         tag = "fp32" if fp32 else "bf16"
         for useW in (1, 0):
-            out = oracle.dispatch(W, H, M, Epr, K, useW, x, ids, wts if useW else None, fill=SENTINEL, lib=lib)
+            out = oracle.dispatch(W, H, M, Epr, K, useW, x, ids, wts if useW else None, scales, fill=SENTINEL,
+                                  lib=lib)
             if list(out.recvCount) != exp_cnt:
                 fails.append(f"worked example: recvCount {list(out.recvCount)} != {exp_cnt}")
             if not np.array_equal(out.sendMap, exp_map):
@@ -236,6 +249,9 @@ def check_worked_example(lib):
                     if list(out.recvExpertIds[p, r]) != exp_ids[p][r]:
                         fails.append(f"worked example: recvExpertIds[{p}][{r}] "
                                      f"{list(out.recvExpertIds[p, r])} != {exp_ids[p][r]}")
+                    if list(out.recvScales[p, r]) != [float(np.float32(v)) for v in exp_scl[p][r]]:
+                        fails.append(f"worked example: recvScales[{p}][{r}] {list(out.recvScales[p, r])} "
+                                     f"!= {exp_scl[p][r]}")
                     got_w = list(out.recvWeights[p, r])
                     want_w = [float(np.float32(v)) for v in exp_wts[p][r]] if useW else [SENTINEL["recvWeights"]] * K
                     if got_w != want_w:
@@ -243,6 +259,8 @@ def check_worked_example(lib):
                 # rows past the count stay untouched
                 if out.recvX[p, len(exp):].size and (out.recvX[p, len(exp):].view(np.uint8) != 0xAD).any():
                     fails.append(f"worked example {tag}: recvX[{p}] written past its count")
+                if (out.recvScales[p, len(exp):] != np.float32(SENTINEL["recvScales"])).any():
+                    fails.append(f"worked example: recvScales[{p}] written past its count")
             key = f"expect_out_{'weighted' if useW else 'unweighted'}_{tag}"
             exp_out = [int(v, 16) for v in d[key].split()]
             got = oracle.combine(W, H, M, Epr, K, useW, y, ids, wts if useW else None, out.sendMap, lib=lib)
@@ -251,6 +269,18 @@ def check_worked_example(lib):
                 if not (bits[t] == exp_out[t]).all():
                     fails.append(f"worked example {tag} useWeights={useW}: out[{t}] = {hex(int(bits[t][0]))} "
                                  f"!= {hex(exp_out[t])}")
+            # the other output type from the same rows: every y value is exact in bf16, so bf16 rows
+            # into fp32 output give the fp32 accumulators, and fp32 rows into bf16 output the bf16 values
+            otag = "bf16" if fp32 else "fp32"
+            okey = f"expect_out_{'weighted' if useW else 'unweighted'}_{tag}_rows_{otag}_out"
+            exp_o = [int(v, 16) for v in d[okey].split()]
+            got = oracle.combine(W, H, M, Epr, K, useW, y, ids, wts if useW else None, out.sendMap,
+                                 out_fp32=not fp32, lib=lib)
+            obits = got if fp32 else _f32_bits(got)
+            for t in range(T):
+                if not (obits[t] == exp_o[t]).all():
+                    fails.append(f"worked example {tag} rows, {otag} out, useWeights={useW}: out[{t}] = "
+                                 f"{hex(int(obits[t][0]))} != {hex(exp_o[t])}")
             # scatter combine: push lands the returned rows, reduce gives the same bits
             cap = oracle.landing_rows(W, K, T)
             if cap != int(d["landing_capacity"]):
@@ -278,6 +308,13 @@ def check_worked_example(lib):
                 if not (rbits[t] == exp_out[t]).all():
                     fails.append(f"worked example scatter {tag} useWeights={useW}: out[{t}] = "
                                  f"{hex(int(rbits[t][0]))} != {hex(exp_out[t])}")
+            red = oracle.combine_reduce(W, H, M, Epr, K, useW, land, scale, out.recvCount, out.sendMap,
+                                        out_fp32=not fp32, lib=lib)
+            rbits = red if fp32 else _f32_bits(red)
+            for t in range(T):
+                if not (rbits[t] == exp_o[t]).all():
+                    fails.append(f"worked example scatter {tag} rows, {otag} out, useWeights={useW}: out[{t}] = "
+                                 f"{hex(int(rbits[t][0]))} != {hex(exp_o[t])}")
     return fails
 
 
@@ -389,8 +426,9 @@ def check_invariants(lib, names=None, seeds=(1, 2, 3), h_cap=None):
                               w.maxTokPerRank, w.hiddenDim, w.numTokens)
         for s in seeds:
             inp = workloads.make_inputs(w, s, with_y=False)
+            scales = workloads.token_scales(w, s, 56)
             o = oracle.dispatch(W, H, M, Epr, K, w.useWeights, inp.x, inp.expertIds,
-                                inp.weights if w.useWeights else None, fill=SENTINEL, lib=lib)
+                                inp.weights if w.useWeights else None, scales, fill=SENTINEL, lib=lib)
             tag = f"{name} seed {s}"
             kept = o.sendMap >= 0
             if int(o.recvCount.sum()) != int(kept.sum()):
@@ -405,6 +443,8 @@ def check_invariants(lib, names=None, seeds=(1, 2, 3), h_cap=None):
                     fails.append(f"{tag}: I3 window {p} not strictly ascending")
                 if c and not np.array_equal(o.recvX[p, :c], inp.x[toks]):
                     fails.append(f"{tag}: I3 window {p} rows are not copies of their tokens")
+                if c and not np.array_equal(o.recvScales[p, :c].view(np.uint32), scales[toks].view(np.uint32)):
+                    fails.append(f"{tag}: I3 window {p} scale rows are not their tokens' scales")
             tt, kk = np.nonzero(kept)
             flat = o.sendMap[tt, kk]
             pp, rr = flat // M, flat % M
@@ -680,6 +720,55 @@ def check_reading_fma_fp32(lib, n=64, seed=31):
     return []
 
 
+def check_combine_out_types(lib, names=("tiny", "pr_scale", "epcfg_defaults", "gen_zipf_h2048"), seed=6,
+                            h_cap=256, t_cap=1024):
+    """The combine's output type apart from its row type (MORI JIT v2 §5:
+    bf16 or fp32 out).  The accumulator is the same whatever the output, so:
+    a bf16 output is torch's own nearest-even cast of the fp32 output (for
+    bf16 and for fp32 rows); bf16 rows widened exactly to fp32 give the same
+    fp32 output as the bf16 rows; and the scatter combine's reduce follows
+    the same rules."""
+    fails = []
+    for name in names:
+        w = workloads.CONFIGS[name]
+        w = w.with_(hiddenDim=min(w.hiddenDim, h_cap), numTokens=min(w.numTokens, t_cap),
+                    maxTokPerRank=min(w.maxTokPerRank, t_cap))
+        W, Epr, K, M, H, T = (w.worldSize, w.numExpertPerRank, w.numExpertPerToken,
+                              w.maxTokPerRank, w.hiddenDim, w.numTokens)
+        inp = workloads.make_inputs(w, seed)
+        wts = inp.weights if w.useWeights else None
+        o = oracle.dispatch(W, H, M, Epr, K, w.useWeights, inp.x, inp.expertIds, wts, lib=lib)
+        y16 = inp.y
+        y32 = (y16.astype(np.uint32) << 16).view(np.float32)  # bf16 -> fp32 is exact
+        rng = np.random.Generator(np.random.PCG64(seed))
+        yf = rng.standard_normal(y16.shape).astype(np.float32)  # fp32 rows that bf16 cannot hold
+        for tag, y in (("bf16 rows", y16), ("fp32 rows", yf)):
+            f32 = oracle.combine(W, H, M, Epr, K, w.useWeights, y, inp.expertIds, wts, o.sendMap, out_fp32=True,
+                                 lib=lib)
+            b16 = oracle.combine(W, H, M, Epr, K, w.useWeights, y, inp.expertIds, wts, o.sendMap, out_fp32=False,
+                                 lib=lib)
+            if f32.dtype != np.float32 or b16.dtype != np.uint16 or f32.shape != (T, H) or b16.shape != (T, H):
+                fails.append(f"{name} {tag}: output types/shapes {f32.dtype}{f32.shape} {b16.dtype}{b16.shape}")
+                continue
+            if not np.array_equal(b16, _bf16_rne_torch(f32)):
+                fails.append(f"{name} {tag}: bf16 output is not the nearest-even cast of the fp32 output")
+            land, sc = oracle.combine_push(W, H, M, Epr, K, w.useWeights, T, y, o.recvExpertIds,
+                                           o.recvWeights if w.useWeights else None, o.recvCount, lib=lib)
+            for ofp in (True, False):
+                red = oracle.combine_reduce(W, H, M, Epr, K, w.useWeights, land, sc, o.recvCount, o.sendMap,
+                                            out_fp32=ofp, lib=lib)
+                want = f32 if ofp else b16
+                if red.dtype != want.dtype or not np.array_equal(red.view(np.uint8), want.view(np.uint8)):
+                    fails.append(f"{name} {tag}: reduce with {'fp32' if ofp else 'bf16'} out differs from the gather")
+        wide = oracle.combine(W, H, M, Epr, K, w.useWeights, y32, inp.expertIds, wts, o.sendMap, out_fp32=True,
+                              lib=lib)
+        narrow = oracle.combine(W, H, M, Epr, K, w.useWeights, y16, inp.expertIds, wts, o.sendMap, out_fp32=True,
+                                lib=lib)
+        if not np.array_equal(wide.view(np.uint32), narrow.view(np.uint32)):
+            fails.append(f"{name}: bf16 rows and their exact fp32 widening give different fp32 outputs")
+    return fails
+
+
 # --------------------------------------------------------------------------
 # scatter (push) combine
 # --------------------------------------------------------------------------
@@ -831,4 +920,5 @@ ALL_CHECKS = [
     check_push_landing_brute,
     check_push_capacity,
     check_push_reduce_matches_gather,
+    check_combine_out_types,
 ]

@@ -15,7 +15,7 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "epdc.h")
 
 OK_CFG = dict(worldSize=8, hiddenDim=7168, maxTokPerRank=4096, numExpertPerRank=32,
-              numExpertPerToken=8, dtype=0, useWeights=1)
+              numExpertPerToken=8, dtype=0, useWeights=1, scaleDim=0)
 P16 = 0x10000  # a fake, 16-byte aligned device address: never dereferenced on these paths
 
 
@@ -57,20 +57,20 @@ def test_scratch_bytes():
 
 
 def _dispatch(c, T, **ptrs):
-    args = dict(x=P16, expertIds=P16, weights=P16, recvX=P16, recvTokIdx=P16, recvExpertIds=P16,
-                recvWeights=P16, recvCount=P16, sendMap=P16, scratch=P16)
+    args = dict(x=P16, expertIds=P16, weights=P16, scales=P16, recvX=P16, recvTokIdx=P16, recvExpertIds=P16,
+                recvWeights=P16, recvScales=P16, recvCount=P16, sendMap=P16, scratch=P16)
     args.update(ptrs)
-    return epdc.epdc_dispatch(c, T, args["x"], args["expertIds"], args["weights"], args["recvX"],
-                              args["recvTokIdx"], args["recvExpertIds"], args["recvWeights"],
+    return epdc.epdc_dispatch(c, T, args["x"], args["expertIds"], args["weights"], args["scales"], args["recvX"],
+                              args["recvTokIdx"], args["recvExpertIds"], args["recvWeights"], args["recvScales"],
                               args["recvCount"], args["sendMap"], args["scratch"],
                               scratchBytes=ptrs.get("scratchBytes", 1 << 20), stream=0, check=False)
 
 
-def _combine(c, T, **ptrs):
+def _combine(c, T, outDtype=None, **ptrs):
     args = dict(y=P16, expertIds=P16, weights=P16, sendMap=P16, out=P16)
     args.update(ptrs)
     return epdc.epdc_combine(c, T, args["y"], args["expertIds"], args["weights"], args["sendMap"],
-                             args["out"], stream=0, check=False)
+                             args["out"], outDtype, stream=0, check=False)
 
 
 REJECT = [
@@ -103,6 +103,12 @@ REJECT = [
     ("weights null with useWeights", {}, 8, dict(weights=None), -5),
     ("recvWeights null with useWeights", {}, 8, dict(recvWeights=None), -5),
     ("scratch too small", {}, 8, dict(scratchBytes=16), -6),
+    ("scaleDim -1", dict(scaleDim=-1), 8, {}, -1),
+    ("scaleDim above the maximum", dict(scaleDim=1025), 8, {}, -1),
+    ("scales null with scaleDim", dict(scaleDim=4), 8, dict(scales=None), -5),
+    ("recvScales null with scaleDim", dict(scaleDim=4), 8, dict(recvScales=None), -5),
+    ("scales misaligned", dict(scaleDim=4), 8, dict(scales=P16 + 2), -4),
+    ("recvScales misaligned", dict(scaleDim=4), 8, dict(recvScales=P16 + 1), -4),
 ]
 
 
@@ -123,6 +129,11 @@ COMBINE_REJECT = [
     ("y misaligned", {}, 8, dict(y=P16 + 2), -4),
     ("y null", {}, 8, dict(y=None), -5),
     ("weights null with useWeights", {}, 8, dict(weights=None), -5),
+    ("expertIds null with useWeights", {}, 8, dict(expertIds=None), -5),
+    ("sendMap null", {}, 8, dict(sendMap=None), -5),
+    ("outDtype fp8", {}, 8, dict(outDtype=2), -2),
+    ("outDtype 7", {}, 8, dict(outDtype=7), -2),
+    ("outDtype fp4x2 with no tokens", {}, 0, dict(outDtype=3), -2),
 ]
 
 
@@ -139,11 +150,11 @@ def _push(c, T, **ptrs):
                                   args["landing"], args["landScale"], stream=0, check=False)
 
 
-def _reduce(c, T, **ptrs):
+def _reduce(c, T, outDtype=None, **ptrs):
     args = dict(landing=P16, landScale=P16, recvCount=P16, sendMap=P16, out=P16)
     args.update(ptrs)
     return epdc.epdc_combine_reduce(c, T, args["landing"], args["landScale"], args["recvCount"], args["sendMap"],
-                                    args["out"], stream=0, check=False)
+                                    args["out"], outDtype, stream=0, check=False)
 
 
 PUSH_REJECT = [
@@ -183,6 +194,8 @@ REDUCE_REJECT = [
     ("sendMap null", {}, 8, dict(sendMap=None), -5),
     ("recvCount null", {}, 8, dict(recvCount=None), -5),
     ("landScale null with useWeights", {}, 8, dict(landScale=None), -5),
+    ("outDtype fp8", {}, 8, dict(outDtype=2), -2),
+    ("outDtype -1", {}, 8, dict(outDtype=-1), -2),
 ]
 
 
@@ -228,6 +241,7 @@ def test_unweighted_accepts_null_weights_without_gpu():
     c = cfg(useWeights=0)
     assert _dispatch(c, 8, weights=None, recvWeights=None) == -7
     assert _combine(c, 8, weights=None) == -7
+    assert _combine(c, 8, weights=None, expertIds=None) == -7  # unweighted: no expert ids needed
     assert "dispatch" in epdc.epdc_last_error() or "combine" in epdc.epdc_last_error()
 
 
@@ -241,7 +255,13 @@ def test_every_wire_dtype_passes_dispatch_checks_without_gpu():
     for dt, h in ((0, 7168), (1, 7168), (2, 7168), (3, 3584), (2, 16), (1, 4)):
         assert _dispatch(cfg(dtype=dt, hiddenDim=h), 8) == -7, (dt, h, epdc.epdc_last_error())
     for dt in (0, 1):
-        assert _combine(cfg(dtype=dt), 8) == -7
+        for odt in (0, 1):  # either row type into either output type
+            assert _combine(cfg(dtype=dt), 8, outDtype=odt) == -7
+            assert _reduce(cfg(dtype=dt), 8, outDtype=odt) == -7
+    # scales: any scaleDim in range with both pointers
+    for S in (1, 56, 64, 65, 1024):
+        assert _dispatch(cfg(scaleDim=S), 8) == -7, (S, epdc.epdc_last_error())
+    assert _dispatch(cfg(scaleDim=0), 8, scales=None, recvScales=None) == -7
 
 
 def test_zero_tokens_needs_only_recvcount_without_gpu():
@@ -261,7 +281,7 @@ def test_prepared_calls_check_like_direct_calls():
     import torch
     if torch.cuda.is_available():
         pytest.skip("host without a GPU only")
-    ptrs = [P16] * 10
+    ptrs = [P16] * 12
     bad = epdc.prepare_dispatch(cfg(), 4097, *ptrs, scratchBytes=1 << 20)
     assert bad(stream=0, check=False) == -3
     mis = epdc.prepare_dispatch(cfg(), 8, P16 + 8, *ptrs[1:], scratchBytes=1 << 20)
@@ -274,6 +294,8 @@ def test_prepared_calls_check_like_direct_calls():
     assert epdc.prepare_combine_push(cfg(), 8, *[P16] * 6)(stream=0, check=False) == -7
     assert epdc.prepare_combine_reduce(cfg(), 8, *[P16] * 5)(stream=0, check=False) == -7
     assert epdc.prepare_combine_reduce(cfg(), 8, P16, None, P16, P16, P16)(stream=0, check=False) == -5
+    assert epdc.prepare_combine(cfg(), 8, *[P16] * 5, outDtype=2)(stream=0, check=False) == -2
+    assert epdc.prepare_combine(cfg(dtype=1), 8, *[P16] * 5, outDtype=0)(stream=0, check=False) == -7
 
 
 class _FakeDeviceTensor:
@@ -297,7 +319,7 @@ class _FakeDeviceTensor:
 def test_binding_refuses_host_and_strided_tensors_before_any_call():
     import torch
     host = torch.zeros(64, dtype=torch.int32)
-    ptrs = [P16] * 10
+    ptrs = [P16] * 12
     with pytest.raises(ValueError, match="device tensor"):
         epdc.epdc_dispatch(cfg(), 8, host, *ptrs[1:], scratchBytes=1 << 20, stream=0)
     with pytest.raises(ValueError, match="contiguous"):
@@ -307,3 +329,76 @@ def test_binding_refuses_host_and_strided_tensors_before_any_call():
     # a contiguous device tensor passes the binding (the library then runs its own checks)
     assert epdc.epdc_combine(cfg(dtype=2), 8, _FakeDeviceTensor(True), P16, P16, P16, P16, stream=0,
                              check=False) == -2
+
+
+class _FakeSized(_FakeDeviceTensor):
+    """A contiguous device tensor of a given byte size."""
+
+    def __init__(self, nbytes):
+        super().__init__(True)
+        self._n = nbytes
+
+    def numel(self):
+        return self._n
+
+    def element_size(self):
+        return 1
+
+
+def test_binding_refuses_short_buffers_before_any_call():
+    """A tensor smaller than the call needs would be read or written past its
+    end on the device: the binding refuses it, naming it, before the launch."""
+    c = cfg(maxTokPerRank=64, scaleDim=4)  # W 8, H 7168 bf16, K 8, 8 tokens
+    T, W, M, K, rb = 8, 8, 64, 8, 7168 * 2
+    ok = dict(x=T * rb, expertIds=T * K * 4, weights=T * K * 4, scales=T * 4 * 4, recvX=W * M * rb,
+              recvTokIdx=W * M * 4, recvExpertIds=W * M * K * 4, recvWeights=W * M * K * 4, recvScales=W * M * 4 * 4,
+              recvCount=W * 4, sendMap=T * K * 4)
+    names = list(ok)
+    for short in names:
+        args = [_FakeSized(ok[n] - (4 if n == short else 0)) for n in names]
+        with pytest.raises(ValueError, match=f"^{short} holds"):
+            epdc.epdc_dispatch(c, T, *args, P16, scratchBytes=1 << 20, stream=0)
+        with pytest.raises(ValueError, match=f"^{short} holds"):
+            epdc.prepare_dispatch(c, T, *args, P16, scratchBytes=1 << 20)
+    cc = cfg(maxTokPerRank=64)
+    full = dict(y=W * M * rb, expertIds=T * K * 4, weights=T * K * 4, sendMap=T * K * 4, out=T * 7168 * 4)
+    for short in full:
+        args = [_FakeSized(full[n] - (4 if n == short else 0)) for n in full]
+        with pytest.raises(ValueError, match=f"^{short} holds"):
+            epdc.epdc_combine(cc, T, *args, epdc.EPDC_FP32, stream=0)
+    # an fp32 output needs twice the bytes of a bf16 one
+    args = [_FakeSized(full[n] if n != "out" else T * 7168 * 2) for n in full]
+    with pytest.raises(ValueError, match="^out holds"):
+        epdc.epdc_combine(cc, T, *args, epdc.EPDC_FP32, stream=0)
+    R = T * 8
+    land = dict(landing=R * rb, landScale=R * 4, recvCount=W * 4, sendMap=T * K * 4, out=T * rb)
+    for short in land:
+        args = [_FakeSized(land[n] - (4 if n == short else 0)) for n in land]
+        with pytest.raises(ValueError, match=f"^{short} holds"):
+            epdc.epdc_combine_reduce(cc, T, *args, stream=0)
+    push = dict(y=W * M * rb, recvExpertIds=W * M * K * 4, recvWeights=W * M * K * 4, recvCount=W * 4,
+                landing=R * rb, landScale=R * 4)
+    for short in push:
+        args = [_FakeSized(push[n] - (4 if n == short else 0)) for n in push]
+        with pytest.raises(ValueError, match=f"^{short} holds"):
+            epdc.epdc_combine_push(cc, T, *args, stream=0)
+
+
+def test_status_constants_match_the_header():
+    """The binding's status-word constants are the header's (the library
+    checks the header against its kernels' own at compile time)."""
+    src = open(HEADER).read()
+    for name in ("EPDC_STATUS_WORD", "EPDC_STATUS_WAIT_TIMEOUT", "EPDC_STATUS_ROW_OUTSIDE", "EPDC_MAX_SCALE_DIM"):
+        m = re.search(rf"#define {name} (\d+)", src)
+        assert m and int(m.group(1)) == getattr(epdc, name), name
+    api = open(os.path.join(ROOT, "combine_count_amd", "csrc", "epdc_api.cpp")).read()
+    assert "static_assert(EPDC_STATUS_WORD == epdc::kScratchError" in api
+
+
+def test_dispatch_status_reads_the_status_word():
+    import torch
+    s = torch.zeros(1100, dtype=torch.int32)
+    assert epdc.dispatch_status(s) == 0
+    s[epdc.EPDC_STATUS_WORD] = epdc.EPDC_STATUS_WAIT_TIMEOUT
+    assert epdc.dispatch_status(s) == 1
+    assert epdc.dispatch_status(s.view(torch.uint8)) == 1

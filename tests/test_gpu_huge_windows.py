@@ -62,8 +62,8 @@ def _run():
     scratch = torch.zeros(nb // 4 + 1, dtype=torch.int32, device=dev)
 
     print("[huge windows] dispatch", flush=True)
-    epdc.epdc_dispatch(cfg, T, x, ids, wts, recvX, recvTokIdx, recvExpertIds, recvWeights, recvCount, sendMap,
-                       scratch)
+    epdc.epdc_dispatch(cfg, T, x, ids, wts, None, recvX, recvTokIdx, recvExpertIds, recvWeights, None, recvCount,
+                       sendMap, scratch)
     torch.cuda.synchronize()
     assert recvCount.cpu().numpy().tolist() == counts
     assert bool((scratch == 0).all().item()), "scratch not left zeroed"

@@ -139,6 +139,22 @@ EDGE = [
     ("ragged_ntw2_cpw8_t33000_h4864", 2, 4, 33000, 33000, 2, 4864, "uniform", 1),  # 8, 2, checked
     ("ntw4_cpw2_t26300_h5120", 2, 4, 26300, 26300, 2, 5120, "uniform", 1),       # 2, 4
     ("ntw4_cpw4_t43700_h6144", 2, 4, 43700, 43700, 2, 6144, "uniform", 1),       # 4, 4
+    # one token per wave, scanned by tile leaders with x after the SCAN (1024 < blocks <= 2560),
+    # for the slab widths the wider rows above never reach there: 1, 2, 4 chunks
+    ("x_late_cpw1_t6000_h512", 2, 4, 6000, 6000, 3, 512, "uniform", 1),          # 1, 1
+    ("x_late_cpw1_ragged_t6000_h264", 2, 4, 6000, 6000, 3, 264, "zipf", 1),      # 1, 1, checked
+    ("x_late_cpw2_t6000_h1024", 2, 4, 6000, 6000, 3, 1024, "uniform", 0),        # 2, 1
+    ("x_late_cpw2_ragged_t6000_h768", 2, 4, 6000, 6000, 3, 768, "uniform", 1),   # 2, 1, checked
+    ("x_late_cpw4_t6000_h2048", 2, 4, 6000, 6000, 3, 2048, "zipf", 1),           # 4, 1
+    ("x_late_cpw4_ragged_t6000_h1792", 2, 4, 6000, 6000, 3, 1792, "uniform", 1),  # 4, 1, checked
+    # 8-chunk slabs with x before COUNT (over 2560 blocks)
+    ("x_early_cpw8_t12000_h4096", 2, 4, 12000, 12000, 3, 4096, "uniform", 1),    # 8, 1
+    ("x_early_cpw8_ragged_t6000_h4864", 2, 4, 6000, 6000, 3, 4864, "zipf", 1),   # 8, 1, checked
+    # four tokens per wave with 7- and 8-chunk slabs (over 32768 one-token waves)
+    ("ntw4_cpw7_t132000_h3584", 2, 4, 132000, 132000, 2, 3584, "uniform", 1),    # 7, 4
+    ("ntw4_cpw7_ragged_t132000_h3328", 2, 4, 132000, 132000, 2, 3328, "zipf", 0),  # 7, 4, checked
+    ("ntw4_cpw8_t132000_h4096", 2, 4, 132000, 132000, 2, 4096, "uniform", 1),    # 8, 4
+    ("ntw4_cpw8_ragged_t66000_h4864", 2, 4, 66000, 66000, 2, 4864, "uniform", 1),  # 8, 4, checked
 ]
 
 
@@ -194,6 +210,79 @@ def test_dtype_parity(case):
             assert np.array_equal(got[p_, :c], scales[tok]), "forwarded scales differ"
         return
     _check_case(w, inp, name)
+
+
+SCALES = [
+    # name, base workload (None: ragged rows, 5 PEs, 3 experts each, topk 7), wire, scaleDim.
+    # The scale rows travel as the fourth metadata field of every received row (MORI JIT v2
+    # §4/§5: the dispatch's scales and the out_scales region; mori PR #599's merge notes).
+    ("fp8_scales56_h7168", "gen_zipf_h7168", "fp8", 56),  # one scale per 128 values; self-summing scan
+    ("fp4x2_scales1_h7168", "gen_zipf_h7168", "fp4x2", 1),  # one per token; x before COUNT
+    ("bf16_scales56_leader_scan", "gen_zipf_h7168", "bf16", 56),  # 2048 blocks: tile leaders publish
+    ("fp32_scales8_x_early", "gen_zipf_h7168", "fp32", 8),  # 4096 blocks: x before COUNT
+    ("bf16_scales64_defaults", "epcfg_defaults", "bf16", 64),  # local scan, exactly one wave of scales
+    ("fp8_scales65_pr_scale", "pr_scale", "fp8", 65),  # one past a wave: the scale-tail loop
+    ("fp8_scales1024_tiny", "tiny", "fp8", 1024),  # the maximum scaleDim
+    ("fp8_scales130_ragged", None, "fp8", 130),  # three waves of scales, bound-checked rows
+    ("fp8_scales56_edge_t1", "gen_edge_t1", "fp8", 56),
+    ("fp8_scales56_large", "large_weighted", "fp8", 56),
+    ("bf16_scales3_more_than_8_dest", "more_than_8_dest", "bf16", 3),
+    ("bf16_scales5_empty", "empty", "bf16", 5),
+]
+
+
+def _edge_workload(name):
+    for e in EDGE:
+        if e[0] == name:
+            return workloads.Workload(*e)
+    raise KeyError(name)
+
+
+@pytest.mark.parametrize("case", SCALES, ids=[c[0] for c in SCALES])
+def test_scale_forwarding(case):
+    """Per-token scales are copied bitwise beside every row of their token:
+    recvScales whole-buffer equal to the oracle's (sentinels past the counts
+    untouched), through every SCAN form and x order."""
+    name, base, wire, S = case
+    if base is None:
+        w = workloads.Workload(name, 5, 3, 700, 650, 7, 1056, "uniform", 1)
+    elif base in workloads.CONFIGS:
+        w = workloads.CONFIGS[base]
+    else:
+        w = _edge_workload(base)
+    w = w.with_(name=name, wire=wire, combineDtype="bf16", scaleDim=S)
+    _check_case(w, workloads.make_inputs(w, 4), name)
+
+
+OUT_TYPES = [
+    # name, base workload (None: ragged), row (combine input) type, output type.  MORI JIT v2
+    # §5: the combine outputs bf16 or fp32, chosen apart from the type of the rows it sums.
+    ("bf16_rows_fp32_out_tiny", "tiny", "bf16", "fp32"),
+    ("bf16_rows_fp32_out_pr_scale", "pr_scale", "bf16", "fp32"),
+    ("bf16_rows_fp32_out_defaults", "epcfg_defaults", "bf16", "fp32"),
+    ("bf16_rows_fp32_out_h2048", "gen_zipf_h2048", "bf16", "fp32"),
+    ("bf16_rows_fp32_out_h7168", "gen_zipf_h7168", "bf16", "fp32"),
+    ("bf16_rows_fp32_out_edge_t8", "gen_edge_t8", "bf16", "fp32"),
+    ("bf16_rows_fp32_out_large_unweighted", "large_unweighted", "bf16", "fp32"),
+    ("bf16_rows_fp32_out_ragged", None, "bf16", "fp32"),
+    ("fp32_rows_bf16_out_defaults", "epcfg_defaults", "fp32", "bf16"),
+    ("fp32_rows_bf16_out_h7168", "gen_zipf_h7168", "fp32", "bf16"),
+    ("fp32_rows_bf16_out_ragged", None, "fp32", "bf16"),
+]
+
+
+@pytest.mark.parametrize("case", OUT_TYPES, ids=[c[0] for c in OUT_TYPES])
+def test_combine_output_types(case):
+    """Either row type into either output type, bit for bit (a bf16 output
+    is the fp32 accumulator rounded to nearest even, an fp32 output the
+    accumulator itself)."""
+    name, base, rows, out = case
+    if base is None:
+        w = workloads.Workload(name, 5, 3, 700, 650, 7, 1056, "uniform", 1)
+    else:
+        w = workloads.CONFIGS[base]
+    w = w.with_(name=name, wire=rows, combineDtype=rows, outDtype=out)
+    _check_case(w, workloads.make_inputs(w, 2), name)
 
 
 INVALID = [

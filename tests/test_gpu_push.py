@@ -82,6 +82,16 @@ def test_push_fp32_rows(base, wire):
     _check_push(w, workloads.make_inputs(w, 7), w.name)
 
 
+@pytest.mark.parametrize("base,rows,out", [("pr_scale", "bf16", "fp32"), ("epcfg_defaults", "fp32", "bf16"),
+                                          ("gen_zipf_h7168", "bf16", "fp32")])
+def test_push_reduce_output_types(base, rows, out):
+    """The reduce writes either output type from either landing-row type,
+    bit-identical to the gather combine's."""
+    w = workloads.CONFIGS[base].with_(name=f"{base}_{rows}_rows_{out}_out", wire=rows, combineDtype=rows,
+                                      outDtype=out)
+    _check_push(w, workloads.make_inputs(w, 8), w.name)
+
+
 def test_push_invalid_expert_ids():
     """Dropped slots (ids outside [0, E)) land no row and add no weight."""
     w = workloads.Workload("push_invalid_ids", 8, 4, 256, 250, 6, 1024, "uniform", 1)
@@ -213,8 +223,8 @@ def test_buffer_helpers_drive_every_call():
     wts = torch.from_numpy(inp.weights).cuda()
     out_g = torch.empty((w.numTokens, w.hiddenDim), dtype=torch.bfloat16, device="cuda")
     out_r = torch.empty_like(out_g)
-    epdc.epdc_dispatch(c, w.numTokens, x, ids, wts, b.recvX, b.recvTokIdx, b.recvExpertIds, b.recvWeights,
-                       b.recvCount, b.sendMap, b.scratch)
+    epdc.epdc_dispatch(c, w.numTokens, x, ids, wts, None, b.recvX, b.recvTokIdx, b.recvExpertIds, b.recvWeights,
+                       None, b.recvCount, b.sendMap, b.scratch)
     epdc.epdc_combine(c, w.numTokens, y, ids, wts, b.sendMap, out_g)
     epdc.epdc_combine_push(c, w.numTokens, y, b.recvExpertIds, b.recvWeights, b.recvCount, lb.landing, lb.landScale)
     epdc.epdc_combine_reduce(c, w.numTokens, lb.landing, lb.landScale, b.recvCount, b.sendMap, out_r)

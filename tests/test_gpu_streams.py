@@ -80,4 +80,4 @@ def test_strided_device_tensor_is_refused():
     wide = torch.zeros((w.numTokens, 2 * w.hiddenDim), dtype=torch.bfloat16, device="cuda")
     strided = wide[:, ::2]
     with pytest.raises(ValueError, match="contiguous"):
-        epdc.epdc_combine(g.ccfg, w.numTokens, g.y, g.ids, g.wts, g.sendMap, strided)
+        epdc.epdc_combine(g.ccfg, w.numTokens, g.y, g.ids, g.wts, g.sendMap, strided, g.outDtype)

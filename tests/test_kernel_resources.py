@@ -63,10 +63,12 @@ def test_default_variants_keep_their_occupancy(compiled):
     # launches of at most 4 tiles: 2- (or 1-) chunk slabs under the local scan
     assert _kernel(d, r"dispatch_kernelILi2ELi1ELb1ELb1ELb0EE")["Occupancy"] == 8
     assert _kernel(d, r"dispatch_kernelILi1ELi1ELb1ELb1ELb0EE")["Occupancy"] == 8
-    # gather combine, 2-chunk slabs, bf16 (up to 8 rows in flight), and its landing-row twin
-    assert _kernel(c, r"combine_kernelILi2ELb1ELb0ELb0EE")["Occupancy"] >= 4
-    assert _kernel(c, r"combine_kernelILi2ELb1ELb0ELb1EE")["Occupancy"] >= 4
-    assert _kernel(c, r"combine_kernelILi1ELb1ELb0ELb0EE")["Occupancy"] == 8
+    # gather combine, 2-chunk slabs, bf16 rows and output (up to 8 rows in flight), its
+    # landing-row twin, and bf16 rows into an fp32 output
+    assert _kernel(c, r"combine_kernelILi2ELb1ELb0ELb0ELb0EE")["Occupancy"] >= 4
+    assert _kernel(c, r"combine_kernelILi2ELb1ELb0ELb0ELb1EE")["Occupancy"] >= 4
+    assert _kernel(c, r"combine_kernelILi2ELb1ELb0ELb1ELb0EE")["Occupancy"] >= 4
+    assert _kernel(c, r"combine_kernelILi1ELb1ELb0ELb0ELb0EE")["Occupancy"] == 8
     assert _kernel(p, r"push_kernelILi7ELb1EE")["Occupancy"] == 8
     for src, (res, _) in compiled.items():
         for name, r in res.items():

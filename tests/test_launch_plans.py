@@ -125,13 +125,24 @@ def _gpu_parity_shapes():
     return sorted(shapes)
 
 
-def test_gpu_parity_reaches_the_dispatch_variants(tmp_path):
-    """The GPU parity cases reach 36 of the 40 dispatch geometries (slab width x
-    tokens per wave x bound checks, and the local scan's) -- all but 7- and
-    8-chunk slabs at four tokens per wave (rows of 5.5 KiB and more at over
-    132,000 tokens, the same code as the reached ones) -- and every combination
-    of SCAN form (tile leader / every block) and x order (each non-local
-    geometry is compiled once per x order)."""
+def _launchable_variants():
+    """(cpw, ntw, full, local, xEarly) of every dispatch kernel the launcher
+    can run (dispatch.hip, launch_fused): one token per wave with the local
+    scan, or scanning through the scratch with either x order; two or four
+    tokens per wave only with x before COUNT (plan_dispatch gives them only
+    to launches of over 8192 blocks, which always take that order)."""
+    out = set()
+    for c in (1, 2, 4, 7, 8):
+        for f in (0, 1):
+            out |= {(c, 1, f, 1, 0), (c, 1, f, 0, 0), (c, 1, f, 0, 1), (c, 2, f, 0, 1), (c, 4, f, 0, 1)}
+    return out
+
+
+def test_gpu_parity_reaches_every_dispatch_variant(tmp_path):
+    """The GPU parity cases reach all 50 compiled dispatch kernels (slab width x
+    tokens per wave x bound checks x SCAN form x x order), and every
+    combination of SCAN form (tile leader / every block) and x order; no plan
+    asks for a kernel that is not compiled."""
     import sys
     sys.path.insert(0, ROOT)
     sys.path.insert(0, os.path.join(ROOT, "tests"))
@@ -144,11 +155,31 @@ def test_gpu_parity_reaches_the_dispatch_variants(tmp_path):
     got = _run(exe, "dispatch", shapes)
     variants, modes = set(), set()
     for cpw, ntw, _nSlabs, _nSubs, _nBlocks, full, local, self_scan, x_early in got.values():
-        variants.add((cpw, ntw, full, local))
+        variants.add((cpw, ntw, full, local, x_early))
         if not local:
             modes.add((self_scan, x_early))
-    compiled = {(c, n, f, 0) for c in (1, 2, 4, 7, 8) for n in (1, 2, 4) for f in (0, 1)}
-    compiled |= {(c, 1, f, 1) for c in (1, 2, 4, 7, 8) for f in (0, 1)}
-    missing = compiled - variants
-    assert missing <= {(7, 4, 0, 0), (7, 4, 1, 0), (8, 4, 0, 0), (8, 4, 1, 0)}, sorted(missing)
+    compiled = _launchable_variants()
+    assert variants <= compiled, sorted(variants - compiled)
+    assert compiled == variants, sorted(compiled - variants)
     assert modes == {(0, 0), (0, 1), (1, 0), (1, 1)}, sorted(modes)
+
+
+def test_random_plans_only_ask_for_compiled_kernels(tmp_path):
+    """Over a sweep of token counts (1..300000) and row sizes (16 B..64 KiB),
+    every plan names a compiled kernel."""
+    import sys
+    sys.path.insert(0, ROOT)
+    from combine_count_amd import _build as B
+    exe = str(tmp_path / "launch_plan_check")
+    r = subprocess.run([B.HIPCC, *B.COMMON, os.path.join(ROOT, "tests", "host", "launch_plan_check.cpp"), "-o", exe],
+                       capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr
+    import numpy as np
+    rng = np.random.Generator(np.random.PCG64(3))
+    shapes = {(int(t), 16 * int(c)) for t, c in zip(rng.integers(1, 300001, 3000), rng.integers(1, 4097, 3000))}
+    shapes |= {(t, rb) for t in (1, 64, 512, 513, 4096, 16384, 65536, 131072, 131073)
+               for rb in (16, 1024, 3584, 7168, 14336, 28672, 65536)}
+    got = _run(exe, "dispatch", sorted(shapes))
+    compiled = _launchable_variants()
+    for (T, rb), (cpw, ntw, _s, _u, nB, full, local, _ss, xe) in got.items():
+        assert (cpw, ntw, full, local, xe) in compiled, (T, rb)

@@ -41,6 +41,12 @@ class Workload:
     zipf_s: float = 1.1
     wire: str = "bf16"          # dispatch row type: bf16, fp32, fp8 or fp4x2
     combineDtype: str = "bf16"  # combine row type: bf16 or fp32
+    outDtype: str = ""          # combine output type: bf16 or fp32 ("" = combineDtype)
+    scaleDim: int = 0           # fp32 scales per token forwarded by the dispatch
+
+    @property
+    def outType(self) -> str:
+        return self.outDtype or self.combineDtype
 
     @property
     def numExperts(self) -> int:
@@ -160,6 +166,7 @@ class Inputs:
     expertIds: np.ndarray  # int32  [T][K]
     weights: np.ndarray    # fp32   [T][K]
     y: np.ndarray | None   # [W][M][H] returned rows of the combine type
+    scales: np.ndarray | None = None  # fp32 [T][scaleDim], None when scaleDim == 0
 
 
 def make_inputs(w: Workload, seed: int, with_y: bool = True) -> Inputs:
@@ -173,7 +180,17 @@ def make_inputs(w: Workload, seed: int, with_y: bool = True) -> Inputs:
         y = np.empty((w.worldSize, w.maxTokPerRank, w.hiddenDim), dtype=ydt)
         for p in range(w.worldSize):
             y[p] = rows_of(rng, (w.maxTokPerRank, w.hiddenDim), w.combineDtype)
-    return Inputs(w, seed, x, ids, weights, y)
+    scales = token_scales(w, seed, w.scaleDim) if w.scaleDim else None
+    return Inputs(w, seed, x, ids, weights, y, scales)
+
+
+def token_scales(w: Workload, seed: int, scaleDim: int) -> np.ndarray:
+    """Per-token quantisation scales forwarded by the dispatch: float32
+    [T][scaleDim], drawn from their own PCG64 stream (the seed and a fixed
+    tag), so that adding them changes no other input.  Values in the range
+    of fp8 e4m3 block scales of N(0,1) rows (block max magnitude / 448)."""
+    rng = np.random.Generator(np.random.PCG64([seed, 0x5CA1E]))
+    return rng.uniform(0.004, 0.012, size=(w.numTokens, scaleDim)).astype(np.float32)
 
 
 @functools.lru_cache(maxsize=4)
