@@ -99,6 +99,21 @@ MUTANTS = [
     ("reduce: accumulator not cleared per token",
      "memset(acc, 0, (size_t)H * sizeof(float)); /* +0.0f */",
      ";"),
+    ("scales copied from the mirrored token",
+     "memcpy(recvScales + row * S, scales + (int64_t)t * S,",
+     "memcpy(recvScales + row * S, scales + (int64_t)(T - 1 - t) * S,"),
+    ("scales not forwarded",
+     "if (S > 0)\n                memcpy(recvScales",
+     "if (S > (1 << 30))\n                memcpy(recvScales"),
+    ("scale row stored at the token's index instead of its row",
+     "memcpy(recvScales + row * S,",
+     "memcpy(recvScales + ((int64_t)p * M + t % M) * S,"),
+    ("combine: output type taken from the rows when they are bf16",
+     "    store_row(outRow, acc, H, outFp32);",
+     "    store_row(outRow, acc, H, outFp32 & inFp32);"),
+    ("reduce: output type taken from the landing rows when they are bf16",
+     "store_row((unsigned char *)out + (int64_t)i * outRowBytes, acc, H, outFp32);",
+     "store_row((unsigned char *)out + (int64_t)i * outRowBytes, acc, H, outFp32 & inFp32);"),
     ("bf16 rounding by truncation",
      "u += 0x7fffu + lsb;",
      "u += 0u * lsb;"),
