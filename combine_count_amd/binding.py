@@ -25,8 +25,8 @@ ERRORS = {
     -6: "EPDC_ERR_SCRATCH",
     -7: "EPDC_ERR_HIP",
 }
-EXPORTS = ("epdc_dispatch_scratch_bytes", "epdc_dispatch", "epdc_combine", "epdc_landing_rows",
-           "epdc_combine_push", "epdc_combine_reduce", "epdc_last_error")
+EXPORTS = ("epdc_dispatch_scratch_bytes", "epdc_dispatch", "epdc_dispatch_noalloc", "epdc_combine",
+           "epdc_landing_rows", "epdc_combine_push", "epdc_combine_reduce", "epdc_last_error")
 # include/epdc.h: the dispatch scratch's status word (index in 32-bit words) and its values
 EPDC_STATUS_WORD = 2
 EPDC_STATUS_WAIT_TIMEOUT = 1
@@ -74,6 +74,8 @@ def load_library() -> ctypes.CDLL:
     lib.epdc_dispatch_scratch_bytes.argtypes = [cfgp]
     lib.epdc_dispatch.restype = ctypes.c_int
     lib.epdc_dispatch.argtypes = [cfgp, i32] + [p] * 12 + [sz, p]
+    lib.epdc_dispatch_noalloc.restype = ctypes.c_int
+    lib.epdc_dispatch_noalloc.argtypes = [cfgp, i32] + [p] * 11 + [p]
     lib.epdc_combine.restype = ctypes.c_int
     lib.epdc_combine.argtypes = [cfgp, i32] + [p] * 5 + [i32, p]
     lib.epdc_landing_rows.restype = i32
@@ -214,6 +216,18 @@ def epdc_dispatch(cfg: EpCfg, numTokens: int, x, expertIds, weights, scales, rec
         ctypes.byref(cfg), int(numTokens), _ptr(x), _ptr(expertIds), _ptr(weights), _ptr(scales), _ptr(recvX),
         _ptr(recvTokIdx), _ptr(recvExpertIds), _ptr(recvWeights), _ptr(recvScales), _ptr(recvCount),
         _ptr(sendMap), _ptr(scratch), int(scratchBytes), _stream(stream))
+    return _check(rc, check)
+
+
+def epdc_dispatch_noalloc(cfg: EpCfg, numTokens: int, x, expertIds, weights, scales, recvX, recvTokIdx,
+                          recvExpertIds, recvWeights, recvScales, recvCount, sendMap, stream=None,
+                          check: bool = True) -> int:
+    _sizes_dispatch(cfg, numTokens, x, expertIds, weights, scales, recvX, recvTokIdx, recvExpertIds, recvWeights,
+                    recvScales, recvCount, sendMap)
+    rc = (_lib or load_library()).epdc_dispatch_noalloc(
+        ctypes.byref(cfg), int(numTokens), _ptr(x), _ptr(expertIds), _ptr(weights), _ptr(scales), _ptr(recvX),
+        _ptr(recvTokIdx), _ptr(recvExpertIds), _ptr(recvWeights), _ptr(recvScales), _ptr(recvCount),
+        _ptr(sendMap), _stream(stream))
     return _check(rc, check)
 
 

@@ -20,6 +20,8 @@
 //     loaded once and stored to every destination.
 #include "epdc_internal.h"
 
+#include <mutex>
+
 namespace epdc {
 namespace {
 
@@ -534,6 +536,56 @@ hipError_t launch_dispatch(const DispatchParams &P, hipStream_t stream) {
         case 8: return launch_cpw<8>(P, pl, stream);
         default: return hipErrorInvalidConfiguration;
     }
+}
+
+// ------------------------------------------- allocation-free dispatch
+// The scratch of epdc_dispatch_noalloc: a device array of this library's
+// code object, one copy per GPU, held until the process ends.  In host code
+// `scratch` names a host-side stand-in, not device memory: its device address
+// comes from hipGetSymbolAddress, once per device, and only that address is
+// used (as the kernels' scratch argument and for the clearing kernel).
+namespace {
+
+static __device__ __align__(256) uint32_t scratch[kStaticScratchWords];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_staticMutex;
+uint32_t *g_staticScratch[kMaxDevices] = {};  // device address per device, once resolved
+
+__global__ __launch_bounds__(256) void clear_words_kernel(uint32_t *words, int32_t n) {
+    for (int32_t i = blockIdx.x * 256 + threadIdx.x; i < n; i += gridDim.x * 256) words[i] = 0u;
+}
+
+}  // namespace
+
+int64_t dispatch_scratch_words(int32_t numTokens, int32_t W) {
+    int32_t wp = 1;
+    while (wp < W) wp <<= 1;
+    return kScratchHeaderWords + 2 * (int64_t)ceil_div(numTokens, kTile) * wp;
+}
+
+hipError_t static_scratch(uint32_t **out, hipStream_t stream) {
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(g_staticMutex);
+    if (!g_staticScratch[dev]) {
+        void *p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        if (p == nullptr) return hipErrorInvalidSymbol;
+        // Zero it once, on the caller's stream, before its first use (a
+        // kernel, not a memset, so that it is also right inside a captured
+        // graph); every dispatch leaves it zeroed again.
+        hipLaunchKernelGGL(clear_words_kernel, dim3(256), dim3(256), 0, stream, static_cast<uint32_t *>(p),
+                           kStaticScratchWords);
+        e = hipGetLastError();
+        if (e != hipSuccess) return e;
+        g_staticScratch[dev] = static_cast<uint32_t *>(p);
+    }
+    *out = g_staticScratch[dev];
+    return hipSuccess;
 }
 
 }  // namespace epdc

@@ -122,6 +122,59 @@ int hip_status(hipError_t e, const char *what) {
     return fail(EPDC_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
 }
 
+// Checks of every dispatch argument but the scratch, and the kernel
+// parameters (the scratch pointer left for the caller to set).
+int dispatch_params(const epdc_cfg *cfg, int32_t numTokens, const void *x, const int32_t *expertIds,
+                    const float *weights, const float *scales, void *recvX, int32_t *recvTokIdx,
+                    int32_t *recvExpertIds, float *recvWeights, float *recvScales, int32_t *recvCount,
+                    int32_t *sendMap, epdc::DispatchParams &P) {
+    int rc = check_cfg(cfg, numTokens, false);
+    if (rc != EPDC_OK) return rc;
+    if (!recvCount) return fail(EPDC_ERR_NULLPTR, "recvCount is NULL");
+    if (!aligned(recvCount, 4)) return fail(EPDC_ERR_ALIGN, "recvCount not 4-byte aligned");
+    if (numTokens > 0) {
+        if (!x || !expertIds || !recvX || !recvTokIdx || !recvExpertIds || !sendMap)
+            return fail(EPDC_ERR_NULLPTR, "a required dispatch pointer is NULL");
+        if (cfg->useWeights && (!weights || !recvWeights))
+            return fail(EPDC_ERR_NULLPTR, "useWeights=1 needs weights and recvWeights");
+        if (cfg->scaleDim > 0 && (!scales || !recvScales))
+            return fail(EPDC_ERR_NULLPTR, "scaleDim > 0 needs scales and recvScales");
+        if (cfg->scaleDim > 0 && (!aligned(scales, 4) || !aligned(recvScales, 4)))
+            return fail(EPDC_ERR_ALIGN, "scales and recvScales must be 4-byte aligned");
+        if (!aligned(x, 16) || !aligned(recvX, 16)) return fail(EPDC_ERR_ALIGN, "x and recvX must be 16-byte aligned");
+        if (!aligned(expertIds, 4) || !aligned(recvTokIdx, 4) || !aligned(recvExpertIds, 4) ||
+            !aligned(sendMap, 4) || (cfg->useWeights && (!aligned(weights, 4) || !aligned(recvWeights, 4))))
+            return fail(EPDC_ERR_ALIGN, "int32/fp32 arrays must be 4-byte aligned");
+    }
+    P.W = cfg->worldSize;
+    P.H = cfg->hiddenDim;
+    P.M = cfg->maxTokPerRank;
+    P.Epr = cfg->numExpertPerRank;
+    P.K = cfg->numExpertPerToken;
+    P.T = numTokens;
+    P.useWeights = cfg->useWeights;
+    P.S = cfg->scaleDim;
+    P.Wp = pow2_ceil(cfg->worldSize);
+    const epdc::DivMagic dm = epdc::div_magic((uint32_t)cfg->numExpertPerRank);
+    P.eprMagic = dm.magic;
+    P.eprSh1 = dm.sh1;
+    P.eprSh2 = dm.sh2;
+    P.rowBytes = cfg->hiddenDim * elem_bytes(cfg->dtype, false);
+    P.nChunks = epdc::ceil_div(P.rowBytes, epdc::kChunkBytes);
+    P.x = static_cast<const uint8_t *>(x);
+    P.expertIds = expertIds;
+    P.weights = cfg->useWeights ? weights : nullptr;
+    P.scales = cfg->scaleDim > 0 ? scales : nullptr;
+    P.recvX = static_cast<uint8_t *>(recvX);
+    P.recvTokIdx = recvTokIdx;
+    P.recvExpertIds = recvExpertIds;
+    P.recvWeights = cfg->useWeights ? recvWeights : nullptr;
+    P.recvScales = cfg->scaleDim > 0 ? recvScales : nullptr;
+    P.recvCount = recvCount;
+    P.sendMap = sendMap;
+    return EPDC_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -141,60 +194,47 @@ int epdc_dispatch(const epdc_cfg *cfg, int32_t numTokens, const void *x, const i
                   int32_t *sendMap, void *scratch, size_t scratchBytes, void *stream) {
     try {
         g_lastError.clear();
-        int rc = check_cfg(cfg, numTokens, false);
+        epdc::DispatchParams P{};
+        int rc = dispatch_params(cfg, numTokens, x, expertIds, weights, scales, recvX, recvTokIdx, recvExpertIds,
+                                 recvWeights, recvScales, recvCount, sendMap, P);
         if (rc != EPDC_OK) return rc;
-        if (!recvCount) return fail(EPDC_ERR_NULLPTR, "recvCount is NULL");
-        if (!aligned(recvCount, 4)) return fail(EPDC_ERR_ALIGN, "recvCount not 4-byte aligned");
         if (numTokens > 0) {
-            if (!x || !expertIds || !recvX || !recvTokIdx || !recvExpertIds || !sendMap || !scratch)
-                return fail(EPDC_ERR_NULLPTR, "a required dispatch pointer is NULL");
-            if (cfg->useWeights && (!weights || !recvWeights))
-                return fail(EPDC_ERR_NULLPTR, "useWeights=1 needs weights and recvWeights");
-            if (cfg->scaleDim > 0 && (!scales || !recvScales))
-                return fail(EPDC_ERR_NULLPTR, "scaleDim > 0 needs scales and recvScales");
-            if (cfg->scaleDim > 0 && (!aligned(scales, 4) || !aligned(recvScales, 4)))
-                return fail(EPDC_ERR_ALIGN, "scales and recvScales must be 4-byte aligned");
-            if (!aligned(x, 16) || !aligned(recvX, 16))
-                return fail(EPDC_ERR_ALIGN, "x and recvX must be 16-byte aligned");
-            if (!aligned(expertIds, 4) || !aligned(recvTokIdx, 4) || !aligned(recvExpertIds, 4) ||
-                !aligned(sendMap, 4) || !aligned(scratch, 16) ||
-                (cfg->useWeights && (!aligned(weights, 4) || !aligned(recvWeights, 4))))
-                return fail(EPDC_ERR_ALIGN, "int32/fp32 arrays must be 4-byte aligned, scratch 16-byte");
+            if (!scratch) return fail(EPDC_ERR_NULLPTR, "scratch is NULL");
+            if (!aligned(scratch, 16)) return fail(EPDC_ERR_ALIGN, "scratch must be 16-byte aligned");
             if (scratchBytes < scratch_bytes(cfg))
                 return fail(EPDC_ERR_SCRATCH, "scratchBytes %zu < %zu required", scratchBytes,
                             scratch_bytes(cfg));
         }
-        epdc::DispatchParams P{};
-        P.W = cfg->worldSize;
-        P.H = cfg->hiddenDim;
-        P.M = cfg->maxTokPerRank;
-        P.Epr = cfg->numExpertPerRank;
-        P.K = cfg->numExpertPerToken;
-        P.T = numTokens;
-        P.useWeights = cfg->useWeights;
-        P.S = cfg->scaleDim;
-        P.Wp = pow2_ceil(cfg->worldSize);
-        const epdc::DivMagic dm = epdc::div_magic((uint32_t)cfg->numExpertPerRank);
-        P.eprMagic = dm.magic;
-        P.eprSh1 = dm.sh1;
-        P.eprSh2 = dm.sh2;
-        P.rowBytes = cfg->hiddenDim * elem_bytes(cfg->dtype, false);
-        P.nChunks = epdc::ceil_div(P.rowBytes, epdc::kChunkBytes);
-        P.x = static_cast<const uint8_t *>(x);
-        P.expertIds = expertIds;
-        P.weights = cfg->useWeights ? weights : nullptr;
-        P.scales = cfg->scaleDim > 0 ? scales : nullptr;
-        P.recvX = static_cast<uint8_t *>(recvX);
-        P.recvTokIdx = recvTokIdx;
-        P.recvExpertIds = recvExpertIds;
-        P.recvWeights = cfg->useWeights ? recvWeights : nullptr;
-        P.recvScales = cfg->scaleDim > 0 ? recvScales : nullptr;
-        P.recvCount = recvCount;
-        P.sendMap = sendMap;
         P.scratch = static_cast<uint32_t *>(scratch);
         return hip_status(epdc::launch_dispatch(P, static_cast<hipStream_t>(stream)), "dispatch launch");
     } catch (...) {
         return fail(EPDC_ERR_HIP, "unexpected C++ exception in epdc_dispatch");
+    }
+}
+
+int epdc_dispatch_noalloc(const epdc_cfg *cfg, int32_t numTokens, const void *x, const int32_t *expertIds,
+                          const float *weights, const float *scales, void *recvX, int32_t *recvTokIdx,
+                          int32_t *recvExpertIds, float *recvWeights, float *recvScales, int32_t *recvCount,
+                          int32_t *sendMap, void *stream) {
+    try {
+        g_lastError.clear();
+        epdc::DispatchParams P{};
+        int rc = dispatch_params(cfg, numTokens, x, expertIds, weights, scales, recvX, recvTokIdx, recvExpertIds,
+                                 recvWeights, recvScales, recvCount, sendMap, P);
+        if (rc != EPDC_OK) return rc;
+        const int64_t words = epdc::dispatch_scratch_words(numTokens, cfg->worldSize);
+        if (words > epdc::kStaticScratchWords)
+            return fail(EPDC_ERR_SCRATCH,
+                        "%d tokens to %d PEs need %lld bytes of scratch; the library's own holds %d "
+                        "(use epdc_dispatch with a caller scratch buffer)",
+                        numTokens, cfg->worldSize, (long long)words * 4, epdc::kStaticScratchWords * 4);
+        uint32_t *dev = nullptr;
+        rc = hip_status(epdc::static_scratch(&dev, static_cast<hipStream_t>(stream)), "library scratch");
+        if (rc != EPDC_OK) return rc;
+        P.scratch = dev;
+        return hip_status(epdc::launch_dispatch(P, static_cast<hipStream_t>(stream)), "dispatch launch");
+    } catch (...) {
+        return fail(EPDC_ERR_HIP, "unexpected C++ exception in epdc_dispatch_noalloc");
     }
 }
 

@@ -289,6 +289,15 @@ inline RowPlan plan_push(int32_t landRows, int32_t rowBytes) {
 
 // Launchers: enqueue on `stream`, return the hipGetLastError() after launch.
 hipError_t launch_dispatch(const DispatchParams &p, hipStream_t stream);
+
+// Allocation-free dispatch: the library's own scratch, a 1 MiB device array
+// per GPU (dispatch.hip).  dispatch_scratch_words gives the 32-bit words a
+// dispatch of numTokens tokens to W PEs uses; static_scratch resolves (once
+// per device, clearing it on `stream` that first time) the current device's
+// copy.
+constexpr int32_t kStaticScratchWords = 1 << 18;
+int64_t dispatch_scratch_words(int32_t numTokens, int32_t W);
+hipError_t static_scratch(uint32_t **out, hipStream_t stream);
 hipError_t launch_combine(const CombineParams &p, bool fp32, bool out32, bool landing, hipStream_t stream);
 hipError_t launch_combine_push(const PushParams &p, hipStream_t stream);
 

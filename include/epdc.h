@@ -177,6 +177,30 @@ int epdc_dispatch(const epdc_cfg *cfg, int32_t numTokens,
                   void *scratch, size_t scratchBytes, void *stream);
 
 /*
+ * epdc_dispatch without a caller scratch buffer, for callers that cannot
+ * allocate device memory: code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation.  Same arguments (minus scratch and
+ * scratchBytes), same kernels and bit-identical outputs.  The scratch is the
+ * library's own: a 1 MiB device array per GPU, held until the process ends,
+ * zeroed by a small kernel on `stream` at the first call on that device and
+ * left zeroed by every call.  It allocates nothing (no hipMalloc, no library
+ * allocator) on any call.
+ *
+ * Limit: the scratch must hold 4224 + 8 * ceil(numTokens / 64) * W' bytes (W'
+ * = worldSize rounded up to a power of two), i.e. up to 130,496 tokens at 64
+ * PEs, 1,044,352 at 8; beyond that the call fails with EPDC_ERR_SCRATCH and
+ * launches nothing.  Calls on one GPU share its array: calls that may run at
+ * the same time on that GPU (on different streams, or from several threads)
+ * race and give invalid outputs -- serialise them, or use epdc_dispatch with
+ * a buffer per stream.  The array's status word is not exposed.
+ */
+int epdc_dispatch_noalloc(const epdc_cfg *cfg, int32_t numTokens,
+                          const void *x, const int32_t *expertIds, const float *weights, const float *scales,
+                          void *recvX, int32_t *recvTokIdx, int32_t *recvExpertIds,
+                          float *recvWeights, float *recvScales, int32_t *recvCount, int32_t *sendMap,
+                          void *stream);
+
+/*
  * Combine numTokens tokens from the rows their PEs returned.
  *
  * cfg->dtype is EPDC_BF16 or EPDC_FP32: the type of y.  outDtype is
