@@ -68,7 +68,9 @@ def test_default_variants_keep_their_occupancy(compiled):
     assert _kernel(c, r"combine_kernelILi2ELb1ELb0ELb0ELb0EE")["Occupancy"] >= 4
     assert _kernel(c, r"combine_kernelILi2ELb1ELb0ELb0ELb1EE")["Occupancy"] >= 4
     assert _kernel(c, r"combine_kernelILi2ELb1ELb0ELb1ELb0EE")["Occupancy"] >= 4
-    assert _kernel(c, r"combine_kernelILi1ELb1ELb0ELb0ELb0EE")["Occupancy"] == 8
+    # 1-chunk slabs (fewer than 8192 two-chunk waves): 7, with the first group's rows in flight
+    # while the weights' scales are summed (faster than 8 without that overlap: PR-scale, EpCfg defaults)
+    assert _kernel(c, r"combine_kernelILi1ELb1ELb0ELb0ELb0EE")["Occupancy"] >= 7
     assert _kernel(p, r"push_kernelILi7ELb1EE")["Occupancy"] == 8
     for src, (res, _) in compiled.items():
         for name, r in res.items():
