@@ -46,7 +46,7 @@ __device__ __forceinline__ void wait_vmcnt() {
 // Measured choices (each was timed against its alternatives; the reasons
 // are with the code that uses them).
 constexpr bool kDispatchNtLoad = false;     // x rows: plain loads
-constexpr bool kDispatchNtStore = true;     // recvX rows: non-temporal stores
+constexpr bool kDispatchNtStore = true;     // recvX rows: non-temporal, device-scope stores (store16_nt_dev)
 constexpr bool kCombineNtLoad = true;       // returned rows: non-temporal loads
 constexpr bool kCombineNtStore = true;      // out rows: non-temporal stores
 constexpr bool kPushNtLoad = true;          // rows the push moves: non-temporal loads
@@ -71,6 +71,15 @@ __device__ __forceinline__ void store16(uint8_t *p, u32x4 v) {
         __builtin_nontemporal_store(v, reinterpret_cast<u32x4 *>(p));
     else
         *reinterpret_cast<u32x4 *>(p) = v;
+}
+
+// 16-byte store with the non-temporal hint and device scope (nt sc1: the
+// line streams through the caches towards memory instead of staying dirty in
+// this XCD's L2).  `row` is wave-uniform (it becomes a buffer descriptor in
+// scalar registers); off is the lane's byte offset in it, below 2^31.
+__device__ __forceinline__ void store16_nt_dev(uint8_t *row, int off, u32x4 v) {
+    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(row, 0, 0x7fffffff, 0x00020000);
+    __builtin_amdgcn_raw_buffer_store_b128(v, rs, off, 0, /*nt*/ 2 | /*sc1*/ 16);
 }
 
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));

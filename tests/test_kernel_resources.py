@@ -1,7 +1,8 @@
 """Build guard on the gfx950 code itself (CPU: hipcc cross-compiles with the
 library's own flags): no kernel spills to scratch, the variants the default
 workloads run keep the occupancy they were tuned at, payload rows move as
-16-byte non-temporal accesses, and no packed-fp32 instruction is emitted."""
+16-byte non-temporal accesses (the dispatch's stores also device-scope), and
+no packed-fp32 instruction is emitted."""
 import os
 import re
 import subprocess
@@ -80,7 +81,7 @@ def test_default_variants_keep_their_occupancy(compiled):
 
 def test_rows_move_as_16_byte_non_temporal_accesses(compiled):
     d, c, p = (compiled[s][1] for s in SOURCES)
-    assert re.search(r"global_store_dwordx4 .* nt", d), "dispatch row stores"
+    assert re.search(r"buffer_store_dwordx4 .* nt sc1", d), "dispatch row stores (non-temporal, device scope)"
     assert re.search(r"global_load_dwordx4 .* nt", c) and re.search(r"global_store_dwordx4 .* nt", c), "combine"
     assert re.search(r"global_load_dwordx4 .* nt", p) and re.search(r"global_store_dwordx4 .* nt", p), "push"
 
