@@ -22,8 +22,11 @@
 //     before its first FMA; every lane owns 16 contiguous bytes per chunk
 //     (8 bf16 or 4 fp32 elements), one 16-byte access;
 //   * the lane's elements go out as 16 bytes (bf16 rows to bf16 output, fp32
-//     to fp32), 32 bytes (bf16 rows to fp32 output) or 8 bytes (fp32 rows to
-//     bf16 output).
+//     to fp32), 8 bytes (fp32 rows to bf16 output) or, for bf16 rows to an
+//     fp32 output, two 16-byte stores, each instruction one contiguous 1 KiB:
+//     there a lane loads two 8-byte pieces of the chunk, one from each half
+//     (two 16-byte stores 32 bytes apart wrote partial lines: 7.7% more
+//     write traffic than the output's size).
 // The same kernel (LAND = true) is the reduce half of the scatter combine:
 // the rows come from the packed landing rows the push wrote and each row's
 // scale from the push's forwarded scales (combine_push.hip).
@@ -57,16 +60,29 @@ __device__ __forceinline__ void fma8(float (&a)[8], float s, u32x4 v) {
 // Loads chunks [slab*CPW, slab*CPW + CPW) of a row, 16 bytes per lane; with
 // FULL every chunk is known to be inside the row (the row a whole number of
 // 1 KiB chunks, the chunk count a multiple of CPW).
-template <int CPW, bool FULL>
+// SPLIT (bf16 rows, fp32 output): the lane's 16 bytes are instead bytes
+// [8 lane, 8 lane + 8) of each half of the chunk, so that its 8 results are
+// output elements 4 lane.. and 256 + 4 lane.. of the chunk: each of the two
+// output stores is then one contiguous 1 KiB.
+template <int CPW, bool FULL, bool SPLIT>
 __device__ __forceinline__ void load_slab(u32x4 (&v)[CPW], const uint8_t *row, int slab, int nChunks,
                                           int rowBytes, int lane) {
 #pragma unroll
     for (int c = 0; c < CPW; ++c) {
         const int gc = slab * CPW + c;
-        const int e = gc * kChunkBytes + lane * 16;
-        // A lane past the row's end loads the row's first 16 bytes (in
-        // bounds; its sums are never stored): no branch or wait per load.
-        v[c] = load16<kCombineNtLoad>(row + ((FULL || (gc < nChunks && e < rowBytes)) ? e : 0));
+        if constexpr (SPLIT) {
+            // Rows are whole 16-byte units, so a piece that starts inside
+            // the row ends inside it.
+            const int e0 = gc * kChunkBytes + lane * 8, e1 = e0 + kChunkBytes / 2;
+            const u32x2 a = load8<kCombineNtLoad>(row + ((FULL || (gc < nChunks && e0 < rowBytes)) ? e0 : 0));
+            const u32x2 b = load8<kCombineNtLoad>(row + ((FULL || (gc < nChunks && e1 < rowBytes)) ? e1 : 0));
+            v[c] = u32x4{a.x, a.y, b.x, b.y};
+        } else {
+            const int e = gc * kChunkBytes + lane * 16;
+            // A lane past the row's end loads the row's first 16 bytes (in
+            // bounds; its sums are never stored): no branch or wait per load.
+            v[c] = load16<kCombineNtLoad>(row + ((FULL || (gc < nChunks && e < rowBytes)) ? e : 0));
+        }
     }
 }
 
@@ -90,14 +106,14 @@ __device__ __forceinline__ void fma_chunk(float (&a)[8], float s, u32x4 v) {
 // VGPRs at 4 rows, 107 against 89 at 6).
 // mid(sc) runs between the loads and the first FMA: it fills the group's
 // scales (computing them first for the token's first group).
-template <int N, int CPW, bool FULL, bool FP32, class Mid>
+template <int N, int CPW, bool FULL, bool FP32, bool SPLIT, class Mid>
 __device__ __forceinline__ void gather_reduce(float (&acc)[CPW][8], const CombineParams &P,
                                               const int32_t (&fl)[8], float (&sc)[8], int slab,
                                               int lane, Mid &mid) {
     u32x4 v[N][CPW];
 #pragma unroll
     for (int j = 0; j < N; ++j)
-        load_slab<CPW, FULL>(v[j], P.y + (int64_t)fl[j] * P.rowBytes, slab, P.nChunks, P.rowBytes, lane);
+        load_slab<CPW, FULL, SPLIT>(v[j], P.y + (int64_t)fl[j] * P.rowBytes, slab, P.nChunks, P.rowBytes, lane);
     mid(sc);
 #pragma unroll
     for (int j = 0; j < N; ++j) {
@@ -172,6 +188,7 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineParams P, int nSlab
         ew = w;
     }
 
+    constexpr bool kSplit = OUT32 && !FP32;
     float acc[CPW][8];
 #pragma unroll
     for (int c = 0; c < CPW; ++c)
@@ -215,14 +232,14 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineParams P, int nSlab
             for (int j = 0; j < kGroup; ++j) scl[j] = __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(s), ks[j]));
         };
         switch (n) {
-            case 1: gather_reduce<1, CPW, FULL, FP32>(acc, P, fl, sc, slab, lane, mid); break;
-            case 2: if constexpr (kGroup >= 2) gather_reduce<2, CPW, FULL, FP32>(acc, P, fl, sc, slab, lane, mid); break;
-            case 3: if constexpr (kGroup >= 3) gather_reduce<3, CPW, FULL, FP32>(acc, P, fl, sc, slab, lane, mid); break;
-            case 4: if constexpr (kGroup >= 4) gather_reduce<4, CPW, FULL, FP32>(acc, P, fl, sc, slab, lane, mid); break;
-            case 5: if constexpr (kGroup >= 5) gather_reduce<5, CPW, FULL, FP32>(acc, P, fl, sc, slab, lane, mid); break;
-            case 6: if constexpr (kGroup >= 6) gather_reduce<6, CPW, FULL, FP32>(acc, P, fl, sc, slab, lane, mid); break;
-            case 7: if constexpr (kGroup >= 7) gather_reduce<7, CPW, FULL, FP32>(acc, P, fl, sc, slab, lane, mid); break;
-            default: if constexpr (kGroup >= 8) gather_reduce<8, CPW, FULL, FP32>(acc, P, fl, sc, slab, lane, mid); break;
+            case 1: gather_reduce<1, CPW, FULL, FP32, kSplit>(acc, P, fl, sc, slab, lane, mid); break;
+            case 2: if constexpr (kGroup >= 2) gather_reduce<2, CPW, FULL, FP32, kSplit>(acc, P, fl, sc, slab, lane, mid); break;
+            case 3: if constexpr (kGroup >= 3) gather_reduce<3, CPW, FULL, FP32, kSplit>(acc, P, fl, sc, slab, lane, mid); break;
+            case 4: if constexpr (kGroup >= 4) gather_reduce<4, CPW, FULL, FP32, kSplit>(acc, P, fl, sc, slab, lane, mid); break;
+            case 5: if constexpr (kGroup >= 5) gather_reduce<5, CPW, FULL, FP32, kSplit>(acc, P, fl, sc, slab, lane, mid); break;
+            case 6: if constexpr (kGroup >= 6) gather_reduce<6, CPW, FULL, FP32, kSplit>(acc, P, fl, sc, slab, lane, mid); break;
+            case 7: if constexpr (kGroup >= 7) gather_reduce<7, CPW, FULL, FP32, kSplit>(acc, P, fl, sc, slab, lane, mid); break;
+            default: if constexpr (kGroup >= 8) gather_reduce<8, CPW, FULL, FP32, kSplit>(acc, P, fl, sc, slab, lane, mid); break;
         }
     }
 
@@ -233,6 +250,16 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineParams P, int nSlab
 #pragma unroll
     for (int c = 0; c < CPW; ++c) {
         const int gc = slab * CPW + c;
+        if constexpr (kSplit) {  // row bytes e0 / e1 -> output bytes 2 e0 / 2 e1
+            const int e0 = gc * kChunkBytes + lane * 8, e1 = e0 + kChunkBytes / 2;
+            if (FULL || (gc < P.nChunks && e0 < P.rowBytes))
+                store16<kCombineNtStore>(orow + 2 * e0, u32x4{__float_as_uint(acc[c][0]), __float_as_uint(acc[c][1]),
+                                                              __float_as_uint(acc[c][2]), __float_as_uint(acc[c][3])});
+            if (FULL || (gc < P.nChunks && e1 < P.rowBytes))
+                store16<kCombineNtStore>(orow + 2 * e1, u32x4{__float_as_uint(acc[c][4]), __float_as_uint(acc[c][5]),
+                                                              __float_as_uint(acc[c][6]), __float_as_uint(acc[c][7])});
+            continue;
+        }
         const int e = gc * kChunkBytes + lane * 16;
         if (FULL || (gc < P.nChunks && e < P.rowBytes)) {
             if (FP32 && OUT32) {
@@ -241,12 +268,6 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineParams P, int nSlab
             } else if (FP32) {  // 4 fp32 elements -> 8 bytes of bf16
                 store8<kCombineNtStore>(orow + e / 2, u32x2{f32_to_bf16(acc[c][0]) | (f32_to_bf16(acc[c][1]) << 16),
                                                             f32_to_bf16(acc[c][2]) | (f32_to_bf16(acc[c][3]) << 16)});
-            } else if (OUT32) {  // 8 bf16 elements -> 32 bytes of fp32
-                store16<kCombineNtStore>(orow + 2 * e, u32x4{__float_as_uint(acc[c][0]), __float_as_uint(acc[c][1]),
-                                                             __float_as_uint(acc[c][2]), __float_as_uint(acc[c][3])});
-                store16<kCombineNtStore>(orow + 2 * e + 16,
-                                         u32x4{__float_as_uint(acc[c][4]), __float_as_uint(acc[c][5]),
-                                               __float_as_uint(acc[c][6]), __float_as_uint(acc[c][7])});
             } else {
                 store16<kCombineNtStore>(orow + e, u32x4{f32_to_bf16(acc[c][0]) | (f32_to_bf16(acc[c][1]) << 16),
                                                          f32_to_bf16(acc[c][2]) | (f32_to_bf16(acc[c][3]) << 16),

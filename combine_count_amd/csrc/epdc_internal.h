@@ -84,6 +84,13 @@ __device__ __forceinline__ void store16_nt_dev(uint8_t *row, int off, u32x4 v) {
 
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
+// 8-byte load (four bf16 values), optionally non-temporal.
+template <bool NT>
+__device__ __forceinline__ u32x2 load8(const uint8_t *p) {
+    if (NT) return __builtin_nontemporal_load(reinterpret_cast<const u32x2 *>(p));
+    return *reinterpret_cast<const u32x2 *>(p);
+}
+
 // 8-byte store (four bf16 values), optionally non-temporal.
 template <bool NT>
 __device__ __forceinline__ void store8(uint8_t *p, u32x2 v) {

@@ -265,6 +265,9 @@ OUT_TYPES = [
     ("bf16_rows_fp32_out_edge_t8", "gen_edge_t8", "bf16", "fp32"),
     ("bf16_rows_fp32_out_large_unweighted", "large_unweighted", "bf16", "fp32"),
     ("bf16_rows_fp32_out_ragged", None, "bf16", "fp32"),
+    # H 1408: 2816-byte rows, the last chunk filling its lower half and a quarter of the upper one
+    # (a lane's two 8-byte pieces sit in different halves of the chunk, each checked apart)
+    ("bf16_rows_fp32_out_ragged_upper_half", "ragged:1408", "bf16", "fp32"),
     ("fp32_rows_bf16_out_defaults", "epcfg_defaults", "fp32", "bf16"),
     ("fp32_rows_bf16_out_h7168", "gen_zipf_h7168", "fp32", "bf16"),
     ("fp32_rows_bf16_out_ragged", None, "fp32", "bf16"),
@@ -277,8 +280,9 @@ def test_combine_output_types(case):
     is the fp32 accumulator rounded to nearest even, an fp32 output the
     accumulator itself)."""
     name, base, rows, out = case
-    if base is None:
-        w = workloads.Workload(name, 5, 3, 700, 650, 7, 1056, "uniform", 1)
+    if base is None or base.startswith("ragged:"):
+        H = 1056 if base is None else int(base.split(":")[1])
+        w = workloads.Workload(name, 5, 3, 700, 650, 7, H, "uniform", 1)
     else:
         w = workloads.CONFIGS[base]
     w = w.with_(name=name, wire=rows, combineDtype=rows, outDtype=out)
