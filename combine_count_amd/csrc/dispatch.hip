@@ -215,9 +215,11 @@ __device__ __forceinline__ void copy_scale_tail(const DispatchParams &P, int32_t
 //      counts itself (selfScan), which takes the publish-and-poll round
 //      trip off the path.
 //   3. Loads: the slab-0 waves' metadata rows (ids, weights and scales),
-//      then every wave's NTW x
-//      slabs (with xEarly, the x slabs go out before COUNT instead; see
-//      plan_dispatch in epdc_internal.h).
+//      then every wave's NTW x slabs, once the SCAN is done (XO late); or
+//      the x slabs before COUNT (XO early); or, once COUNT is done, the
+//      SCAN's reads first, then the metadata rows and the x slabs, and only
+//      then the wait for the SCAN's reads (XO mid).  See plan_dispatch in
+//      epdc_internal.h for which launch takes which order.
 //   4. FINALIZE: one wait for the wave's loads, then every store of its NTW
 //      tokens to every destination, with no further wait (vmcnt is one
 //      in-order counter for loads and stores on this ISA, so waiting on a
@@ -227,13 +229,15 @@ __device__ __forceinline__ void copy_scale_tail(const DispatchParams &P, int32_t
 //   5. The last block to finish clears the published counts; the done
 //      counters wrap to zero by themselves, so the scratch is zero again for
 //      the next call (and for every replay of a captured graph).
-// XE (x before COUNT) is a compile-time choice: with it a runtime flag, the
-// compiler's waits had to cover both load orders at once (measured: the
+// XO (the x order) is a compile-time choice: with it a runtime flag, the
+// compiler's waits had to cover every load order at once (measured: the
 // 4096-token h7168 launch, which never takes the early order, 1.4% slower).
-template <int CPW, int NTW, bool FULL, bool LOCAL, bool XE>
+template <int CPW, int NTW, bool FULL, bool LOCAL, int XO>
 __global__ __launch_bounds__(256) void dispatch_kernel(DispatchParams P, int nSlabs, int nSubs, int nBlocks,
                                                             int selfScan) {
-    constexpr bool xEarly = XE;
+    constexpr bool xEarly = XO == kXOrderEarly;
+    constexpr bool xMid = XO == kXOrderMid;
+    static_assert(!(LOCAL && XO != kXOrderLate), "a local scan requests every load up front");
     __shared__ uint64_t sMask[kTile];  // destination-PE set of each token of the tile
     __shared__ uint64_t sBal[64];      // per PE: which tokens of the tile go there
     __shared__ int32_t sPre[64];       // per PE: rows taken by earlier tiles
@@ -351,6 +355,9 @@ __global__ __launch_bounds__(256) void dispatch_kernel(DispatchParams P, int nSl
             __hip_atomic_store(published + (int64_t)tile * P.Wp + lane, (uint32_t)cnt + 1u, __ATOMIC_RELAXED,
                                __HIP_MEMORY_SCOPE_AGENT);
     }
+    // x mid: every wave waits for COUNT (its ids' round trip runs alone), so
+    // that the SCAN's reads go out before the x flood.
+    if constexpr (xMid) __syncthreads();
 
     // 3. SCAN: exclusive base of this tile on each PE.  The leader sums the
     // published counts of all earlier tiles (the row stride Wp is a power of
@@ -378,6 +385,25 @@ __global__ __launch_bounds__(256) void dispatch_kernel(DispatchParams P, int nSl
         const int n = tile * P.Wp;
         uint32_t acc = 0;
         int idx = tid;
+        if constexpr (xMid) {
+            // The first 1024 published words are requested, then the
+            // metadata rows and the x slabs; a word's use waits for it
+            // alone (loads complete in order).  A word not yet published is
+            // polled again behind the x loads.
+            uint32_t v[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) v[i] = idx + i * 256 < n ? load_published(published + idx + i * 256) : 1u;
+            load_meta();
+            load_x();
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                if (idx + i * 256 < n) {
+                    if (v[i] == 0) v[i] = wait_published(published + idx + i * 256, hdr + kScratchError);
+                    acc += v[i] - 1u;
+                }
+            }
+            idx += 4 * 256;
+        }
         for (; idx + 3 * 256 < n; idx += 4 * 256) {
             uint32_t v0 = load_published(published + idx), v1 = load_published(published + idx + 256);
             uint32_t v2 = load_published(published + idx + 512), v3 = load_published(published + idx + 768);
@@ -399,19 +425,28 @@ __global__ __launch_bounds__(256) void dispatch_kernel(DispatchParams P, int nSl
                 __hip_atomic_store(prefixes + (int64_t)tile * P.Wp + tid, (uint32_t)sPre[tid] + 1u,
                                    __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }
-    } else if (tile > 0 && tid < P.Wp) {
-        uint32_t v = load_published(prefixes + (int64_t)tile * P.Wp + tid);
-        if (v == 0) v = wait_published(prefixes + (int64_t)tile * P.Wp + tid, hdr + kScratchError);
-        sPre[tid] = (int32_t)(v - 1u);
+    } else if (tile > 0) {
+        uint32_t v = tid < P.Wp ? load_published(prefixes + (int64_t)tile * P.Wp + tid) : 1u;
+        if constexpr (xMid) {
+            load_meta();
+            load_x();
+        }
+        if (tid < P.Wp) {
+            if (v == 0) v = wait_published(prefixes + (int64_t)tile * P.Wp + tid, hdr + kScratchError);
+            sPre[tid] = (int32_t)(v - 1u);
+        }
+    } else if constexpr (xMid) {  // tile 0: no SCAN to wait for
+        load_meta();
+        load_x();
     }
     __syncthreads();
 
-    // Scanning through the scratch, the metadata rows and then (without
-    // xEarly) the x slabs are requested only now: issued before the SCAN, the
-    // x flood would delay the SCAN's own small reads.  Either way no wait
-    // below follows a store.
+    // Scanning through the scratch with x late, the metadata rows and then
+    // the x slabs are requested only now: issued before the SCAN, the x flood
+    // would delay the SCAN's own small reads (with x early only the metadata
+    // rows are left).  In every order no wait below follows a store.
     const int32_t E = P.W * P.Epr;
-    if constexpr (!localScan) {
+    if constexpr (!localScan && !xMid) {
         load_meta();
         if (!xEarly) load_x();
     }
@@ -489,9 +524,9 @@ __global__ __launch_bounds__(256) void dispatch_kernel(DispatchParams P, int nSl
 }
 
 // Runs a plan (plan_dispatch in epdc_internal.h) with its compiled variant.
-template <int CPW, int NTW, bool FULL, bool LOCAL, bool XE>
+template <int CPW, int NTW, bool FULL, bool LOCAL, int XO>
 hipError_t launch_variant(const DispatchParams &P, const DispatchPlan &pl, hipStream_t stream) {
-    hipLaunchKernelGGL((dispatch_kernel<CPW, NTW, FULL, LOCAL, XE>), dim3((uint32_t)pl.nBlocks), dim3(256), 0, stream,
+    hipLaunchKernelGGL((dispatch_kernel<CPW, NTW, FULL, LOCAL, XO>), dim3((uint32_t)pl.nBlocks), dim3(256), 0, stream,
                        P, pl.nSlabs, pl.nSubs, (int)pl.nBlocks, pl.selfScan ? 1 : 0);
     return hipGetLastError();
 }
@@ -501,18 +536,25 @@ hipError_t launch_fused(const DispatchParams &P, const DispatchPlan &pl, hipStre
     static_assert(kTile % (4 * NTW) == 0, "a block's tokens must tile the 64-token tile");
     if (pl.nBlocks > INT32_MAX) return hipErrorInvalidConfiguration;
     if constexpr (NTW == 1) {
-        if (pl.local)  // every load is requested up front: no x-early variant
-            return pl.full ? launch_variant<CPW, NTW, true, true, false>(P, pl, stream)
-                           : launch_variant<CPW, NTW, false, true, false>(P, pl, stream);
-        if (!pl.xEarly)
-            return pl.full ? launch_variant<CPW, NTW, true, false, false>(P, pl, stream)
-                           : launch_variant<CPW, NTW, false, false, false>(P, pl, stream);
+        if (pl.local)  // every load is requested up front: no other x order
+            return pl.full ? launch_variant<CPW, NTW, true, true, kXOrderLate>(P, pl, stream)
+                           : launch_variant<CPW, NTW, false, true, kXOrderLate>(P, pl, stream);
+        if (pl.xOrder == kXOrderLate)
+            return pl.full ? launch_variant<CPW, NTW, true, false, kXOrderLate>(P, pl, stream)
+                           : launch_variant<CPW, NTW, false, false, kXOrderLate>(P, pl, stream);
+        // x mid: only self-summing launches of slabs of at most kXMidSelfCpw
+        // chunks (plan_dispatch)
+        if constexpr (CPW <= kXMidSelfCpw) {
+            if (pl.xOrder == kXOrderMid)
+                return pl.full ? launch_variant<CPW, NTW, true, false, kXOrderMid>(P, pl, stream)
+                               : launch_variant<CPW, NTW, false, false, kXOrderMid>(P, pl, stream);
+        }
     }
     // Several tokens per wave only come with launches of over 8192 blocks,
     // which always request x before COUNT (plan_dispatch).
-    if (!pl.xEarly) return hipErrorInvalidConfiguration;
-    return pl.full ? launch_variant<CPW, NTW, true, false, true>(P, pl, stream)
-                   : launch_variant<CPW, NTW, false, false, true>(P, pl, stream);
+    if (pl.xOrder != kXOrderEarly) return hipErrorInvalidConfiguration;
+    return pl.full ? launch_variant<CPW, NTW, true, false, kXOrderEarly>(P, pl, stream)
+                   : launch_variant<CPW, NTW, false, false, kXOrderEarly>(P, pl, stream);
 }
 
 template <int CPW>

@@ -53,7 +53,8 @@ constexpr bool kPushNtLoad = true;          // rows the push moves: non-temporal
 constexpr bool kPushNtStore = true;         // landing rows: non-temporal stores
 constexpr int kXEarlyBlocks = 2560;         // launches of more blocks request x before COUNT
 constexpr int kSelfScanBlocks = 1024;       // launches of up to this many blocks sum the tile counts in every block
-constexpr int kXEarlySelfCpw = 4;           // ... and self-summing launches with slabs of at most this many chunks
+constexpr int kXMidSelfCpw = 4;             // self-summing launches with slabs of at most this many chunks request
+                                            // x between COUNT and the SCAN's wait
 constexpr int kNarrowTiles = 4;             // launches of up to this many tiles use 1- or 2-chunk slabs
 constexpr int kLocalScanTiles = 8;          // launches of up to this many 64-token tiles scan in every block
 constexpr int kCombineGroup = 8;            // returned rows requested together per wave (gather combine)
@@ -195,6 +196,13 @@ inline DivMagic div_magic(uint32_t d) {
 // Launch geometry of one dispatch, chosen from the token count and the row
 // size alone (host code; the launcher runs exactly this plan, and a host test
 // pins it for the documented shapes).
+// When a dispatch wave requests its x slabs (a compile-time choice of the
+// kernel): after the SCAN, before COUNT, or between COUNT and the SCAN's wait
+// (once the SCAN's own reads are out).
+constexpr int kXOrderLate = 0;
+constexpr int kXOrderEarly = 1;
+constexpr int kXOrderMid = 2;
+
 struct DispatchPlan {
     int32_t cpw;      // 1 KiB chunks per slab: 1, 2, 4, 7 or 8
     int32_t ntw;      // tokens per wave: 1, 2 or 4
@@ -204,7 +212,7 @@ struct DispatchPlan {
     bool full;        // every slab lies inside the row: no per-lane bound checks
     bool local;       // local scan: every block counts the earlier tiles' ids
     bool selfScan;    // every block sums the published tile counts
-    bool xEarly;      // x slabs requested before COUNT
+    int32_t xOrder;   // when the x slabs are requested: kXOrderLate / kXOrderEarly / kXOrderMid
 };
 
 inline DispatchPlan plan_dispatch(int32_t T, int32_t rowBytes) {
@@ -252,12 +260,24 @@ inline DispatchPlan plan_dispatch(int32_t T, int32_t rowBytes) {
     // queued behind streaming traffic.  In smaller launches the early x flood
     // delays the SCAN instead.  Measured crossover: between 2048 blocks (after
     // the SCAN 1-3% faster) and 3072 (before COUNT 4% faster; 8-10% at 4096).
-    // Self-summing launches whose slabs are at most 4 chunks also request x
-    // before COUNT (4096 tokens: fp4x2 rows 2.6%, h1024 2%, h2048 1%, fp8 rows
-    // at h4096 1% faster); with wider slabs there the early x delays the SCAN
-    // (2-3.5% slower with 7-chunk slabs).  (A local scan requests every load
-    // up front anyway.)
-    pl.xEarly = !pl.local && (pl.nBlocks > kXEarlyBlocks || (pl.selfScan && pl.cpw <= kXEarlySelfCpw));
+    // Self-summing launches whose slabs are at most 4 chunks request x once
+    // COUNT is done and the SCAN's reads are out, before waiting for them:
+    // the ids' round trip then runs without the x flood and the x loads
+    // overlap the SCAN's (4096 tokens, one library per process, 3 rounds,
+    // against x before COUNT: fp4x2 rows 16.06 -> 15.62 us, h2048 17.27 ->
+    // 16.67, h1024 12.04 -> 11.59, fp8 rows at h4096 17.25 -> 16.62; x after
+    // the SCAN was slower than both).  With 7- or 8-chunk slabs the order
+    // between COUNT and the SCAN's wait was mixed (fp8 rows at h7168 1.7%
+    // slower, 2000 tokens at h7168 1.5% faster), so they keep x after the
+    // SCAN.  (A local scan requests every load up front anyway.)
+    if (pl.local)
+        pl.xOrder = kXOrderLate;
+    else if (pl.nBlocks > kXEarlyBlocks)
+        pl.xOrder = kXOrderEarly;
+    else if (pl.selfScan && pl.cpw <= kXMidSelfCpw)
+        pl.xOrder = kXOrderMid;
+    else
+        pl.xOrder = kXOrderLate;
     return pl;
 }
 

@@ -1,6 +1,7 @@
 // Prints the launch plans of csrc/epdc_internal.h (host code the launchers
 // run) for shapes given on the command line:
-//   dispatch T rowBytes ...  -> T rowBytes cpw ntw nSlabs nSubs nBlocks full local selfScan xEarly
+//   dispatch T rowBytes ...  -> T rowBytes cpw ntw nSlabs nSubs nBlocks full local selfScan xOrder
+//                               (xOrder: 0 after the SCAN, 1 before COUNT, 2 between COUNT and the SCAN's wait)
 //   combine  T rowBytes ...  -> T rowBytes cpw nSlabs waves nBlocks full
 //   push     L rowBytes ...  -> L rowBytes cpw nSlabs waves nBlocks full   (L = landing rows)
 #include <cstdio>
@@ -17,7 +18,7 @@ int main(int argc, char **argv) {
         if (!std::strcmp(kind, "dispatch")) {
             const epdc::DispatchPlan p = epdc::plan_dispatch(n, rowBytes);
             std::printf("%d %d %d %d %d %d %lld %d %d %d %d\n", n, rowBytes, p.cpw, p.ntw, p.nSlabs, p.nSubs,
-                        (long long)p.nBlocks, (int)p.full, (int)p.local, (int)p.selfScan, (int)p.xEarly);
+                        (long long)p.nBlocks, (int)p.full, (int)p.local, (int)p.selfScan, (int)p.xOrder);
         } else {
             const epdc::RowPlan p =
                 !std::strcmp(kind, "combine") ? epdc::plan_combine(n, rowBytes) : epdc::plan_push(n, rowBytes);

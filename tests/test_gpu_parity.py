@@ -101,8 +101,9 @@ EDGE = [
     # before COUNT, a last tile of one token)
     ("x_late_2560_blocks_t5120", 8, 32, 5120, 5120, 8, 7168, "zipf", 1),
     ("x_early_2592_blocks_t5121", 8, 32, 5121, 5121, 8, 7168, "zipf", 1),
-    # self-summing with x requested before COUNT (slabs of at most 4 chunks), ragged 3.5 KiB rows
-    ("self_scan_x_early_ragged_h1792", 4, 8, 1000, 1000, 5, 1792, "uniform", 1),
+    # self-summing with x requested between COUNT and the SCAN's wait (slabs of at most 4
+    # chunks), ragged 3.5 KiB rows
+    ("self_scan_x_mid_ragged_h1792", 4, 8, 1000, 1000, 5, 1792, "uniform", 1),
     # the token-count x topk grid of mori PR #599's checks, at 8 PEs / 256 experts / h7168
     # (uniform routing; the Zipf workloads cover the skewed case)
     ("pr_grid_ct512_topk6", 8, 32, 512, 512, 6, 7168, "uniform", 1),
@@ -138,6 +139,14 @@ EDGE = [
     ("ragged_ntw2_cpw7_t66000_h2816", 2, 4, 66000, 66000, 2, 2816, "zipf", 1),   # 7, 2, checked
     ("ragged_ntw2_cpw8_t33000_h4864", 2, 4, 33000, 33000, 2, 4864, "uniform", 1),  # 8, 2, checked
     ("ntw4_cpw2_t26300_h5120", 2, 4, 26300, 26300, 2, 5120, "uniform", 1),       # 2, 4
+    # one token per wave with x before COUNT (over 2560 blocks) and slabs of at most 4 chunks
+    ("x_early_cpw4_t10300_h2048", 2, 4, 10300, 10300, 3, 2048, "uniform", 1),        # 4, full
+    ("x_early_cpw4_ragged_t10300_h1792", 2, 4, 10300, 10300, 3, 1792, "zipf", 1),    # 4, checked
+    ("x_early_cpw2_t3400_h3072", 2, 4, 3400, 3400, 3, 3072, "uniform", 1),           # 2, full, 3 slabs
+    ("x_early_cpw2_ragged_t10300_h768", 2, 4, 10300, 10300, 3, 768, "uniform", 0),   # 2, checked
+    ("x_early_cpw1_ragged_t10300_h264", 2, 4, 10300, 10300, 2, 264, "uniform", 1),   # 1, checked
+    # x between COUNT and the SCAN's wait with 1-chunk slabs (3 KiB rows: three slabs per row)
+    ("x_mid_cpw1_t1000_h1536", 4, 8, 1000, 1000, 5, 1536, "zipf", 1),
     ("ntw4_cpw4_t43700_h6144", 2, 4, 43700, 43700, 2, 6144, "uniform", 1),       # 4, 4
     # one token per wave, scanned by tile leaders with x after the SCAN (1024 < blocks <= 2560),
     # for the slab widths the wider rows above never reach there: 1, 2, 4 chunks

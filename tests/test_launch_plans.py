@@ -8,18 +8,19 @@ import subprocess
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
-FIELDS = ("cpw", "ntw", "nSlabs", "nSubs", "nBlocks", "full", "local", "selfScan", "xEarly")
+FIELDS = ("cpw", "ntw", "nSlabs", "nSubs", "nBlocks", "full", "local", "selfScan", "xOrder")
 ROW_FIELDS = ("cpw", "nSlabs", "waves", "nBlocks", "full")
 EXPECT = {
-    # (numTokens, rowBytes): (cpw, ntw, nSlabs, nSubs, nBlocks, full, local, selfScan, xEarly)
+    # (numTokens, rowBytes): (cpw, ntw, nSlabs, nSubs, nBlocks, full, local, selfScan, xOrder)
+    # xOrder: 0 x after the SCAN, 1 x before COUNT, 2 x between COUNT and the SCAN's wait
     # 4096 tokens x h7168 bf16: two 7-chunk slabs, 2048 blocks, tile leaders publish, x after the SCAN
     (4096, 14336): (7, 1, 2, 16, 2048, 1, 0, 0, 0),
     # fp8 rows: one 7-chunk slab, 1024 blocks: every block sums the counts, x after the SCAN
     (4096, 7168): (7, 1, 1, 16, 1024, 1, 0, 1, 0),
-    # fp4x2 rows (3.5 KiB): one bound-checked 4-chunk slab, self-summing, x before COUNT
-    (4096, 3584): (4, 1, 1, 16, 1024, 0, 0, 1, 1),
-    # h2048 bf16: one 4-chunk slab, self-summing, x before COUNT
-    (4096, 4096): (4, 1, 1, 16, 1024, 1, 0, 1, 1),
+    # fp4x2 rows (3.5 KiB): one bound-checked 4-chunk slab, self-summing, x between COUNT and SCAN
+    (4096, 3584): (4, 1, 1, 16, 1024, 0, 0, 1, 2),
+    # h2048 bf16: one 4-chunk slab, self-summing, x between COUNT and SCAN
+    (4096, 4096): (4, 1, 1, 16, 1024, 1, 0, 1, 2),
     # fp32 rows: four 7-chunk slabs, 4096 blocks: x before COUNT
     (4096, 28672): (7, 1, 4, 16, 4096, 1, 0, 0, 1),
     # 16384 tokens: 8192 blocks, x before COUNT
@@ -126,23 +127,27 @@ def _gpu_parity_shapes():
 
 
 def _launchable_variants():
-    """(cpw, ntw, full, local, xEarly) of every dispatch kernel the launcher
+    """(cpw, ntw, full, local, xOrder) of every dispatch kernel the launcher
     can run (dispatch.hip, launch_fused): one token per wave with the local
-    scan, or scanning through the scratch with either x order; two or four
-    tokens per wave only with x before COUNT (plan_dispatch gives them only
-    to launches of over 8192 blocks, which always take that order)."""
+    scan, or scanning through the scratch with x after the SCAN or before
+    COUNT, or (slabs of at most 4 chunks) between COUNT and the SCAN's wait;
+    two or four tokens per wave only with x before COUNT (plan_dispatch
+    gives them only to launches of over 8192 blocks, which always take that
+    order)."""
     out = set()
     for c in (1, 2, 4, 7, 8):
         for f in (0, 1):
             out |= {(c, 1, f, 1, 0), (c, 1, f, 0, 0), (c, 1, f, 0, 1), (c, 2, f, 0, 1), (c, 4, f, 0, 1)}
+            if c <= 4:
+                out.add((c, 1, f, 0, 2))
     return out
 
 
 def test_gpu_parity_reaches_every_dispatch_variant(tmp_path):
-    """The GPU parity cases reach all 50 compiled dispatch kernels (slab width x
+    """The GPU parity cases reach all 56 compiled dispatch kernels (slab width x
     tokens per wave x bound checks x SCAN form x x order), and every
-    combination of SCAN form (tile leader / every block) and x order; no plan
-    asks for a kernel that is not compiled."""
+    combination of SCAN form (tile leader / every block) and x order that a
+    plan can give; no plan asks for a kernel that is not compiled."""
     import sys
     sys.path.insert(0, ROOT)
     sys.path.insert(0, os.path.join(ROOT, "tests"))
@@ -161,7 +166,9 @@ def test_gpu_parity_reaches_every_dispatch_variant(tmp_path):
     compiled = _launchable_variants()
     assert variants <= compiled, sorted(variants - compiled)
     assert compiled == variants, sorted(compiled - variants)
-    assert modes == {(0, 0), (0, 1), (1, 0), (1, 1)}, sorted(modes)
+    assert len(compiled) == 56
+    # a self-summing launch (<= 1024 blocks) never requests x before COUNT (> 2560 blocks)
+    assert modes == {(0, 0), (0, 1), (1, 0), (1, 2)}, sorted(modes)
 
 
 def test_random_plans_only_ask_for_compiled_kernels(tmp_path):
