@@ -574,7 +574,7 @@ hipError_t launch_dispatch(const DispatchParams &P, hipStream_t stream) {
         hipLaunchKernelGGL(zero_count_kernel, dim3(1), dim3(64), 0, stream, P.recvCount, P.W);
         return hipGetLastError();
     }
-    const DispatchPlan pl = plan_dispatch(P.T, P.rowBytes);
+    const DispatchPlan pl = plan_dispatch(P.T, P.rowBytes, P.W);
     switch (pl.cpw) {
         case 1: return launch_cpw<1>(P, pl, stream);
         case 2: return launch_cpw<2>(P, pl, stream);

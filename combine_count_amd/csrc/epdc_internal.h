@@ -55,6 +55,7 @@ constexpr int kXEarlyBlocks = 2560;         // launches of more blocks request x
 constexpr int kSelfScanBlocks = 1024;       // launches of up to this many blocks sum the tile counts in every block
 constexpr int kXMidSelfCpw = 4;             // self-summing launches with slabs of at most this many chunks request
                                             // x between COUNT and the SCAN's wait
+constexpr int kSelfScanWords = 8192;        // ... and sum up to this many published words per block at any size
 constexpr int kNarrowTiles = 4;             // launches of up to this many tiles use 1- or 2-chunk slabs
 constexpr int kLocalScanTiles = 8;          // launches of up to this many 64-token tiles scan in every block
 constexpr int kCombineGroup = 8;            // returned rows requested together per wave (gather combine)
@@ -215,7 +216,7 @@ struct DispatchPlan {
     int32_t xOrder;   // when the x slabs are requested: kXOrderLate / kXOrderEarly / kXOrderMid
 };
 
-inline DispatchPlan plan_dispatch(int32_t T, int32_t rowBytes) {
+inline DispatchPlan plan_dispatch(int32_t T, int32_t rowBytes, int32_t W) {
     DispatchPlan pl{};
     if (T <= 0) return pl;
     const int32_t nTiles = ceil_div(T, kTile);
@@ -228,9 +229,15 @@ inline DispatchPlan plan_dispatch(int32_t T, int32_t rowBytes) {
     // the row (a wave then moves up to 8 KiB of a token with no bound
     // checks); other rows (not a whole number of 1 KiB chunks, e.g. 3.5 KiB
     // fp4x2 rows at hidden 7168) take the narrowest of 1/2/4/7/8 chunks that
-    // covers the row (8 beyond that) with bound checks on the tail.
+    // covers the row (8 beyond that) with bound checks on the tail.  Rows of
+    // exactly 7 chunks (fp8 rows at h7168, bf16 at h3584) take two
+    // bound-checked 4-chunk slabs (4 + 3), which puts them under the
+    // self-summing SCAN with x mid below (4096 tokens: fp8 rows 24.33 ->
+    // 23.97 us, h3584 24.24 -> 23.91; 8192 fp8 tokens 44.2 -> 41.7).
     if (nTiles <= kNarrowTiles)
         pl.cpw = nChunks <= 1 ? 1 : (!whole || nChunks % 2 == 0) ? 2 : 1;
+    else if (whole && nChunks == 7)
+        pl.cpw = 4;
     else if (whole)
         pl.cpw = nChunks % 8 == 0 ? 8 : nChunks % 7 == 0 ? 7 : nChunks % 4 == 0 ? 4 : nChunks % 2 == 0 ? 2 : 1;
     else
@@ -251,9 +258,20 @@ inline DispatchPlan plan_dispatch(int32_t T, int32_t rowBytes) {
     // Every block sums the earlier tiles' counts itself in launches of up to
     // 4 blocks per CU, where it saves a round trip (measured at 4096 tokens:
     // fp4x2 rows 2.6%, h2048 2.3%; 640 / 1024 tokens at h7168 5.3% / 3.6%).
-    // In larger launches the tile leader's one published line is faster
-    // (1.5% at 2048 blocks, 1.6% for fp8 rows at 1536).
-    pl.selfScan = !pl.local && pl.nBlocks <= kSelfScanBlocks;
+    // In larger launches of 7- and 8-chunk slabs the tile leader's one
+    // published line is faster (1.5% at 2048 blocks, 1.6% for fp8 rows at
+    // 1536; every block summing with x mid: 16384 tokens 5% slower).  One-
+    // token-per-wave launches of slabs of at most 4 chunks sum in every
+    // block at any size, with x mid, while a block's sum stays within
+    // kSelfScanWords published words (one library per process, 3 rounds,
+    // against the leader's line with x before COUNT: fp4x2 rows at 8192 /
+    // 16384 / 65536 tokens 28.6 -> 24.3, 49.4 -> 43.0, 236.4 -> 188.0 us;
+    // h2048 at 16384 tokens 53.3 -> 48.0; h1024 at 16384 / 65536 tokens
+    // 37.6 -> 29.5, 173.3 -> 131.8).
+    int32_t wp = 1;
+    while (wp < W) wp <<= 1;
+    pl.selfScan = !pl.local && (pl.nBlocks <= kSelfScanBlocks ||
+                                (pl.cpw <= kXMidSelfCpw && pl.ntw == 1 && (int64_t)nTiles * wp <= kSelfScanWords));
     // x before COUNT in launches of well over one round of resident blocks
     // (about 7 per CU, 1792 on the chip): blocks that start once HBM is
     // saturated would otherwise idle through the SCAN's round trips, each
@@ -272,10 +290,10 @@ inline DispatchPlan plan_dispatch(int32_t T, int32_t rowBytes) {
     // SCAN.  (A local scan requests every load up front anyway.)
     if (pl.local)
         pl.xOrder = kXOrderLate;
-    else if (pl.nBlocks > kXEarlyBlocks)
-        pl.xOrder = kXOrderEarly;
     else if (pl.selfScan && pl.cpw <= kXMidSelfCpw)
         pl.xOrder = kXOrderMid;
+    else if (pl.nBlocks > kXEarlyBlocks)
+        pl.xOrder = kXOrderEarly;
     else
         pl.xOrder = kXOrderLate;
     return pl;

@@ -1,9 +1,9 @@
 // Prints the launch plans of csrc/epdc_internal.h (host code the launchers
 // run) for shapes given on the command line:
-//   dispatch T rowBytes ...  -> T rowBytes cpw ntw nSlabs nSubs nBlocks full local selfScan xOrder
-//                               (xOrder: 0 after the SCAN, 1 before COUNT, 2 between COUNT and the SCAN's wait)
-//   combine  T rowBytes ...  -> T rowBytes cpw nSlabs waves nBlocks full
-//   push     L rowBytes ...  -> L rowBytes cpw nSlabs waves nBlocks full   (L = landing rows)
+//   dispatch T rowBytes W ...  -> T rowBytes W cpw ntw nSlabs nSubs nBlocks full local selfScan xOrder
+//                                 (xOrder: 0 after the SCAN, 1 before COUNT, 2 between COUNT and the SCAN's wait)
+//   combine  T rowBytes ...    -> T rowBytes cpw nSlabs waves nBlocks full
+//   push     L rowBytes ...    -> L rowBytes cpw nSlabs waves nBlocks full   (L = landing rows)
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
@@ -13,11 +13,14 @@
 int main(int argc, char **argv) {
     if (argc < 2) return 2;
     const char *kind = argv[1];
-    for (int i = 2; i + 1 < argc; i += 2) {
+    const bool dispatch = !std::strcmp(kind, "dispatch");
+    const int step = dispatch ? 3 : 2;
+    for (int i = 2; i + step - 1 < argc; i += step) {
         const int n = std::atoi(argv[i]), rowBytes = std::atoi(argv[i + 1]);
-        if (!std::strcmp(kind, "dispatch")) {
-            const epdc::DispatchPlan p = epdc::plan_dispatch(n, rowBytes);
-            std::printf("%d %d %d %d %d %d %lld %d %d %d %d\n", n, rowBytes, p.cpw, p.ntw, p.nSlabs, p.nSubs,
+        if (dispatch) {
+            const int W = std::atoi(argv[i + 2]);
+            const epdc::DispatchPlan p = epdc::plan_dispatch(n, rowBytes, W);
+            std::printf("%d %d %d %d %d %d %d %lld %d %d %d %d\n", n, rowBytes, W, p.cpw, p.ntw, p.nSlabs, p.nSubs,
                         (long long)p.nBlocks, (int)p.full, (int)p.local, (int)p.selfScan, (int)p.xOrder);
         } else {
             const epdc::RowPlan p =

@@ -147,6 +147,21 @@ EDGE = [
     ("x_early_cpw1_ragged_t10300_h264", 2, 4, 10300, 10300, 2, 264, "uniform", 1),   # 1, checked
     # x between COUNT and the SCAN's wait with 1-chunk slabs (3 KiB rows: three slabs per row)
     ("x_mid_cpw1_t1000_h1536", 4, 8, 1000, 1000, 5, 1536, "zipf", 1),
+    # slabs of at most 4 chunks where a block would sum over 8192 published words (64 PEs,
+    # over 128 tiles): the tile leaders publish, x after the SCAN (<= 2560 blocks) or before
+    # COUNT (over 2560)
+    ("w64_x_late_cpw1_ragged_t8256_h264", 64, 2, 8256, 8256, 2, 264, "uniform", 1),
+    ("w64_x_late_cpw1_t8256_h512", 64, 2, 8256, 8256, 2, 512, "uniform", 0),
+    ("w64_x_late_cpw2_ragged_t8256_h768", 64, 2, 8256, 8256, 2, 768, "uniform", 1),
+    ("w64_x_late_cpw2_t8256_h1024", 64, 2, 8256, 8256, 2, 1024, "zipf", 1),
+    ("w64_x_late_cpw4_ragged_t8256_h1792", 64, 2, 8256, 8256, 2, 1792, "uniform", 0),
+    ("w64_x_late_cpw4_t8256_h2048", 64, 2, 8256, 8256, 2, 2048, "uniform", 1),
+    ("w64_x_early_cpw1_ragged_t10300_h264", 64, 2, 10300, 10300, 2, 264, "zipf", 1),
+    ("w64_x_early_cpw1_t10300_h512", 64, 2, 10300, 10300, 2, 512, "uniform", 1),
+    ("w64_x_early_cpw2_ragged_t10300_h768", 64, 2, 10300, 10300, 2, 768, "uniform", 0),
+    ("w64_x_early_cpw2_t10300_h1024", 64, 2, 10300, 10300, 2, 1024, "uniform", 1),
+    ("w64_x_early_cpw4_ragged_t10300_h1792", 64, 2, 10300, 10300, 2, 1792, "zipf", 1),
+    ("w64_x_early_cpw4_t10300_h2048", 64, 2, 10300, 10300, 2, 2048, "uniform", 1),
     ("ntw4_cpw4_t43700_h6144", 2, 4, 43700, 43700, 2, 6144, "uniform", 1),       # 4, 4
     # one token per wave, scanned by tile leaders with x after the SCAN (1024 < blocks <= 2560),
     # for the slab widths the wider rows above never reach there: 1, 2, 4 chunks
@@ -160,7 +175,8 @@ EDGE = [
     ("x_early_cpw8_t12000_h4096", 2, 4, 12000, 12000, 3, 4096, "uniform", 1),    # 8, 1
     ("x_early_cpw8_ragged_t6000_h4864", 2, 4, 6000, 6000, 3, 4864, "zipf", 1),   # 8, 1, checked
     # four tokens per wave with 7- and 8-chunk slabs (over 32768 one-token waves)
-    ("ntw4_cpw7_t132000_h3584", 2, 4, 132000, 132000, 2, 3584, "uniform", 1),    # 7, 4
+    ("ntw4_4plus3_t132000_h3584", 2, 4, 132000, 132000, 2, 3584, "uniform", 1),  # 4, 4, checked (7 = 4 + 3)
+    ("ntw4_cpw7_w1_t65601_h7168", 1, 4, 65601, 65601, 2, 7168, "uniform", 1),    # 7, 4
     ("ntw4_cpw7_ragged_t132000_h3328", 2, 4, 132000, 132000, 2, 3328, "zipf", 0),  # 7, 4, checked
     ("ntw4_cpw8_t132000_h4096", 2, 4, 132000, 132000, 2, 4096, "uniform", 1),    # 8, 4
     ("ntw4_cpw8_ragged_t66000_h4864", 2, 4, 66000, 66000, 2, 4864, "uniform", 1),  # 8, 4, checked

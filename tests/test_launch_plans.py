@@ -11,42 +11,49 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 FIELDS = ("cpw", "ntw", "nSlabs", "nSubs", "nBlocks", "full", "local", "selfScan", "xOrder")
 ROW_FIELDS = ("cpw", "nSlabs", "waves", "nBlocks", "full")
 EXPECT = {
-    # (numTokens, rowBytes): (cpw, ntw, nSlabs, nSubs, nBlocks, full, local, selfScan, xOrder)
+    # (numTokens, rowBytes, worldSize): (cpw, ntw, nSlabs, nSubs, nBlocks, full, local, selfScan, xOrder)
     # xOrder: 0 x after the SCAN, 1 x before COUNT, 2 x between COUNT and the SCAN's wait
     # 4096 tokens x h7168 bf16: two 7-chunk slabs, 2048 blocks, tile leaders publish, x after the SCAN
-    (4096, 14336): (7, 1, 2, 16, 2048, 1, 0, 0, 0),
-    # fp8 rows: one 7-chunk slab, 1024 blocks: every block sums the counts, x after the SCAN
-    (4096, 7168): (7, 1, 1, 16, 1024, 1, 0, 1, 0),
-    # fp4x2 rows (3.5 KiB): one bound-checked 4-chunk slab, self-summing, x between COUNT and SCAN
-    (4096, 3584): (4, 1, 1, 16, 1024, 0, 0, 1, 2),
-    # h2048 bf16: one 4-chunk slab, self-summing, x between COUNT and SCAN
-    (4096, 4096): (4, 1, 1, 16, 1024, 1, 0, 1, 2),
+    (4096, 14336, 8): (7, 1, 2, 16, 2048, 1, 0, 0, 0),
+    # fp8 rows (7 chunks): two bound-checked 4-chunk slabs, every block sums the counts, x mid
+    (4096, 7168, 8): (4, 1, 2, 16, 2048, 0, 0, 1, 2),
+    # fp4x2 rows (3.5 KiB): one bound-checked 4-chunk slab, self-summing, x mid
+    (4096, 3584, 8): (4, 1, 1, 16, 1024, 0, 0, 1, 2),
+    # h2048 bf16: one 4-chunk slab, self-summing, x mid
+    (4096, 4096, 8): (4, 1, 1, 16, 1024, 1, 0, 1, 2),
     # fp32 rows: four 7-chunk slabs, 4096 blocks: x before COUNT
-    (4096, 28672): (7, 1, 4, 16, 4096, 1, 0, 0, 1),
+    (4096, 28672, 8): (7, 1, 4, 16, 4096, 1, 0, 0, 1),
     # 16384 tokens: 8192 blocks, x before COUNT
-    (16384, 14336): (7, 1, 2, 16, 8192, 1, 0, 0, 1),
+    (16384, 14336, 8): (7, 1, 2, 16, 8192, 1, 0, 0, 1),
     # one tile: 2-chunk slabs (at most 4 tiles), local scan
-    (1, 14336): (2, 1, 7, 16, 112, 1, 1, 0, 0),
-    (8, 14336): (2, 1, 7, 16, 112, 1, 1, 0, 0),
+    (1, 14336, 8): (2, 1, 7, 16, 112, 1, 1, 0, 0),
+    (8, 14336, 8): (2, 1, 7, 16, 112, 1, 1, 0, 0),
     # two tiles of odd-chunk fp8 rows: 1-chunk slabs, local scan
-    (128, 7168): (1, 1, 7, 16, 224, 1, 1, 0, 0),
+    (128, 7168, 8): (1, 1, 7, 16, 224, 1, 1, 0, 0),
     # 8 tiles: 7-chunk slabs, still the local scan; 9 tiles: self-summing
-    (512, 14336): (7, 1, 2, 16, 256, 1, 1, 0, 0),
-    (576, 14336): (7, 1, 2, 16, 288, 1, 0, 1, 0),
-    # around the self-summing limit (1024 blocks)
-    (2047, 14336): (7, 1, 2, 16, 1024, 1, 0, 1, 0),
-    (2049, 14336): (7, 1, 2, 16, 1056, 1, 0, 0, 0),
+    (512, 14336, 8): (7, 1, 2, 16, 256, 1, 1, 0, 0),
+    (576, 14336, 8): (7, 1, 2, 16, 288, 1, 0, 1, 0),
+    # around the self-summing limit of 7-chunk slabs (1024 blocks)
+    (2047, 14336, 8): (7, 1, 2, 16, 1024, 1, 0, 1, 0),
+    (2049, 14336, 8): (7, 1, 2, 16, 1056, 1, 0, 0, 0),
     # around the x-early limit (2560 blocks): 80 and 81 tiles
-    (5120, 14336): (7, 1, 2, 16, 2560, 1, 0, 0, 0),
-    (5121, 14336): (7, 1, 2, 16, 2592, 1, 0, 0, 1),
+    (5120, 14336, 8): (7, 1, 2, 16, 2560, 1, 0, 0, 0),
+    (5121, 14336, 8): (7, 1, 2, 16, 2592, 1, 0, 0, 1),
+    # slabs of at most 4 chunks sum in every block at any size while a block sums at most
+    # 8192 published words (tiles x worldSize rounded up to a power of two)
+    (16384, 3584, 8): (4, 1, 1, 16, 4096, 0, 0, 1, 2),
+    (65536, 2048, 8): (2, 1, 1, 16, 16384, 1, 0, 1, 2),
+    (8192, 4096, 64): (4, 1, 1, 16, 2048, 1, 0, 1, 2),
+    (8256, 4096, 64): (4, 1, 1, 16, 2064, 1, 0, 0, 0),
+    (12000, 4096, 40): (4, 1, 1, 16, 3008, 1, 0, 0, 1),
     # 528-byte rows: more than 16384 / 32768 one-token waves take 2 / 4 tokens per wave
-    (66000, 528): (1, 2, 1, 8, 8256, 0, 0, 0, 1),
-    (132000, 528): (1, 4, 1, 4, 8252, 0, 0, 0, 1),
+    (66000, 528, 8): (1, 2, 1, 8, 8256, 0, 0, 0, 1),
+    (132000, 528, 8): (1, 4, 1, 4, 8252, 0, 0, 0, 1),
     # 8-chunk slabs; rows past 8 chunks that are not whole: 8-chunk slabs with bound checks
-    (1000, 8192): (8, 1, 1, 16, 256, 1, 0, 1, 0),
-    (1000, 9728): (8, 1, 2, 16, 512, 0, 0, 1, 0),
+    (1000, 8192, 8): (8, 1, 1, 16, 256, 1, 0, 1, 0),
+    (1000, 9728, 8): (8, 1, 2, 16, 512, 0, 0, 1, 0),
     # no tokens: nothing but recvCount
-    (0, 14336): (0, 0, 0, 0, 0, 0, 0, 0, 0),
+    (0, 14336, 8): (0, 0, 0, 0, 0, 0, 0, 0, 0),
 }
 
 
@@ -72,14 +79,16 @@ PUSH = {
 
 
 def _run(exe, kind, table):
+    """Plans of the given shapes: (T, rowBytes, W) for the dispatch, (rows, rowBytes) else."""
     args = [str(v) for shape in table for v in shape]
     r = subprocess.run([exe, kind, *args], capture_output=True, text=True, timeout=60)
     assert r.returncode == 0, r.stderr
+    n = 3 if kind == "dispatch" else 2
     got = {}
     for line in r.stdout.split("\n"):
         if line.strip():
             v = [int(x) for x in line.split()]
-            got[(v[0], v[1])] = tuple(v[2:])
+            got[tuple(v[:n])] = tuple(v[n:])
     return got
 
 
@@ -100,7 +109,7 @@ def test_launch_plans(tmp_path):
 
 
 def _gpu_parity_shapes():
-    """(numTokens, dispatch row bytes) of the dispatches the GPU parity tests run."""
+    """(numTokens, dispatch row bytes, worldSize) of the dispatches the GPU parity tests run."""
     import workloads
     import test_gpu_parity as P
     import test_gpu_random_shapes as R
@@ -108,21 +117,21 @@ def _gpu_parity_shapes():
     shapes = set()
     for name, _ in P.CONFIG_SEEDS:
         w = workloads.CONFIGS[name]
-        shapes.add((w.numTokens, w.dispatchHidden * wb[w.wire]))
-    for _name, _W, _Epr, _M, T, _K, H, _routing, _useW in P.EDGE:
-        shapes.add((T, H * 2))
+        shapes.add((w.numTokens, w.dispatchHidden * wb[w.wire], w.worldSize))
+    for _name, W, _Epr, _M, T, _K, H, _routing, _useW in P.EDGE:
+        shapes.add((T, H * 2, W))
     for name, base, wire, comb in P.DTYPES:
         if base is None:
             w = workloads.Workload(name, 5, 3, 700, 650, 7, 1056, "uniform", 1, wire=wire, combineDtype=comb)
         else:
             w = workloads.CONFIGS[base].with_(wire=wire, combineDtype=comb)
         rb = w.dispatchHidden * wb[wire] + (56 * 4 if name == "fp8_rows_with_block_scales" else 0)
-        shapes.add((w.numTokens, rb))
+        shapes.add((w.numTokens, rb, w.worldSize))
     for _id, name, over in P.GRAPH_CASES:
         w = workloads.CONFIGS[name].with_(**(over or {}))
-        shapes.add((w.numTokens, w.dispatchHidden * wb[w.wire]))
-    for _i, _W, _Epr, _M, T, _K, H, dt, _useW, _routing in R.CASES:
-        shapes.add((T, H * wb[dt]))
+        shapes.add((w.numTokens, w.dispatchHidden * wb[w.wire], w.worldSize))
+    for _i, W, _Epr, _M, T, _K, H, dt, _useW, _routing in R.CASES:
+        shapes.add((T, H * wb[dt], W))
     return sorted(shapes)
 
 
@@ -172,8 +181,8 @@ def test_gpu_parity_reaches_every_dispatch_variant(tmp_path):
 
 
 def test_random_plans_only_ask_for_compiled_kernels(tmp_path):
-    """Over a sweep of token counts (1..300000) and row sizes (16 B..64 KiB),
-    every plan names a compiled kernel."""
+    """Over a sweep of token counts (1..300000), row sizes (16 B..64 KiB) and
+    world sizes (1..64), every plan names a compiled kernel."""
     import sys
     sys.path.insert(0, ROOT)
     from combine_count_amd import _build as B
@@ -183,10 +192,11 @@ def test_random_plans_only_ask_for_compiled_kernels(tmp_path):
     assert r.returncode == 0, r.stderr
     import numpy as np
     rng = np.random.Generator(np.random.PCG64(3))
-    shapes = {(int(t), 16 * int(c)) for t, c in zip(rng.integers(1, 300001, 3000), rng.integers(1, 4097, 3000))}
-    shapes |= {(t, rb) for t in (1, 64, 512, 513, 4096, 16384, 65536, 131072, 131073)
-               for rb in (16, 1024, 3584, 7168, 14336, 28672, 65536)}
+    shapes = {(int(t), 16 * int(c), int(w)) for t, c, w in zip(rng.integers(1, 300001, 3000),
+                                                              rng.integers(1, 4097, 3000), rng.integers(1, 65, 3000))}
+    shapes |= {(t, rb, w) for t in (1, 64, 512, 513, 4096, 16384, 65536, 131072, 131073)
+               for rb in (16, 1024, 3584, 7168, 14336, 28672, 65536) for w in (1, 8, 64)}
     got = _run(exe, "dispatch", sorted(shapes))
     compiled = _launchable_variants()
-    for (T, rb), (cpw, ntw, _s, _u, nB, full, local, _ss, xe) in got.items():
-        assert (cpw, ntw, full, local, xe) in compiled, (T, rb)
+    for (T, rb, W), (cpw, ntw, _s, _u, nB, full, local, _ss, xe) in got.items():
+        assert (cpw, ntw, full, local, xe) in compiled, (T, rb, W)
