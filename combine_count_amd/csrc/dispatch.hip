@@ -216,10 +216,11 @@ __device__ __forceinline__ void copy_scale_tail(const DispatchParams &P, int32_t
 //      trip off the path.
 //   3. Loads: the slab-0 waves' metadata rows (ids, weights and scales),
 //      then every wave's NTW x slabs, once the SCAN is done (XO late); or
-//      the x slabs before COUNT (XO early); or, once COUNT is done, the
-//      SCAN's reads first, then the metadata rows and the x slabs, and only
-//      then the wait for the SCAN's reads (XO mid).  See plan_dispatch in
-//      epdc_internal.h for which launch takes which order.
+//      the x slabs before COUNT (XO early); or, once every wave has waited
+//      for COUNT, the SCAN's first reads, then the metadata rows and the x
+//      slabs as soon as those reads are in, before the rest of the SCAN (XO
+//      mid).  See plan_dispatch in epdc_internal.h for which launch takes
+//      which order.
 //   4. FINALIZE: one wait for the wave's loads, then every store of its NTW
 //      tokens to every destination, with no further wait (vmcnt is one
 //      in-order counter for loads and stores on this ISA, so waiting on a
@@ -387,9 +388,14 @@ __global__ __launch_bounds__(256) void dispatch_kernel(DispatchParams P, int nSl
         int idx = tid;
         if constexpr (xMid) {
             // The first 1024 published words are requested, then the
-            // metadata rows and the x slabs; a word's use waits for it
-            // alone (loads complete in order).  A word not yet published is
-            // polled again behind the x loads.
+            // metadata rows and the x slabs.  As compiled, the x loads wait
+            // for those words to arrive: the wait analysis merges the paths
+            // on which the ids' loads were not consumed and waits for every
+            // earlier load.  (An explicit wait after COUNT lets the x loads
+            // overlap the words' round trip; measured even: 4096 tokens,
+            // fp4x2 rows 15.41 against 15.55 us, h1024 11.64 against 11.34,
+            // h2048 at 16384 tokens 47.88 against 47.45.)  A word not yet
+            // published is polled again behind the x loads.
             uint32_t v[4];
 #pragma unroll
             for (int i = 0; i < 4; ++i) v[i] = idx + i * 256 < n ? load_published(published + idx + i * 256) : 1u;
