@@ -235,10 +235,23 @@ def rotation(torch, w, push, requested):
     return max(1, min(n, 64, int((8 << 30) // b), int(free * 0.5 // b)))
 
 
+# Launches per loop of the per-kernel durations and graph replays (and the
+# warmup and steps of the other configurations): at least this many whatever
+# --steps says, so that a short timed region (--steps 20) does not leave
+# microsecond kernels measured over 20 launches, where the loop's start and
+# end dominate.
+MIN_AUX_STEPS = 200
+MIN_SWEEP_WARMUP = 50
+
+
 def measure(torch, w, inp, args, push, headline=False):
     """Every figure of one workload: the timed step loop, per-kernel
     back-to-back durations, the graph-replayed step and (headline) the
-    spread and a hot loop."""
+    spread and a hot loop.  The headline's timed loop (and its repeats and
+    hot loop) is exactly --steps steps after --warmup warmup steps; the
+    other loops, and every loop of the other configurations, take at least
+    MIN_AUX_STEPS launches (the other configurations warm up for at least
+    MIN_SWEEP_WARMUP steps)."""
     from gpu_harness import DeviceRun
     nsets = rotation(torch, w, push, args.rotate)
     sets = [DeviceRun(w, inp) for _ in range(nsets)]
@@ -265,44 +278,47 @@ def measure(torch, w, inp, args, push, headline=False):
             run(s)
 
     stream = torch.cuda.current_stream()
-    for i in range(args.warmup):
+    steps = args.steps if headline else max(args.steps, MIN_AUX_STEPS)
+    aux = max(args.steps, MIN_AUX_STEPS)
+    warmup = args.warmup if headline else max(args.warmup, MIN_SWEEP_WARMUP)
+    for i in range(warmup):
         step(sets[i % nsets])
     torch.cuda.synchronize()
 
-    def loop_ms(run, sel):
+    def loop_ms(run, sel, n):
         a = torch.cuda.Event(enable_timing=True)
         b = torch.cuda.Event(enable_timing=True)
         torch.cuda.synchronize()
         a.record(stream)
-        for i in range(args.steps):
+        for i in range(n):
             run(sel(i))
         b.record(stream)
         torch.cuda.synchronize()
-        return a.elapsed_time(b) / args.steps
+        return a.elapsed_time(b) / n
 
     # Timed region: exactly `steps` steps between two events, nothing else on
     # the stream (per-launch events cost about 10 us a step on this stack).
-    ms_step = loop_ms(step, lambda i: sets[i % nsets])
+    ms_step = loop_ms(step, lambda i: sets[i % nsets], steps)
     res = {"U": U, "stages": stages, "step_b": step_b, "ms_step": ms_step, "sets": nsets,
-           "rotated_bytes": nsets * step_b}
+           "rotated_bytes": nsets * step_b, "warmup": warmup, "steps": steps, "aux_launches": aux}
     if headline:
         # Spread and cache state, beside `value` (the loop above alone): the
         # same cold loop four more times, then `steps` steps on one set.
-        res["repeats"] = [ms_step] + [loop_ms(step, lambda i: sets[i % nsets]) for _ in range(4)]
-        res["hot_ms"] = loop_ms(step, lambda i: sets[0])
-    # Per-kernel durations: each kernel alone, `steps` launches back to back
+        res["repeats"] = [ms_step] + [loop_ms(step, lambda i: sets[i % nsets], steps) for _ in range(4)]
+        res["hot_ms"] = loop_ms(step, lambda i: sets[0], steps)
+    # Per-kernel durations: each kernel alone, `aux` launches back to back
     # over the same rotating sets, between two HIP events on the launch stream
     # (an event pair around every launch adds ~2 us to each reading).
-    res["kern_ms"] = {name: loop_ms(run, lambda i: sets[i % nsets]) for name, run, _ in stages}
-    # Launch latency: the same `steps` steps captured once into a HIP graph
-    # and replayed, which takes the per-launch host cost (Python, ctypes, the
-    # HIP launch call) out of the step; at a few tokens that cost is the step.
+    res["kern_ms"] = {name: loop_ms(run, lambda i: sets[i % nsets], aux) for name, run, _ in stages}
+    # Launch latency: `aux` steps captured once into a HIP graph and
+    # replayed, which takes the per-launch host cost (Python, ctypes, the HIP
+    # launch call) out of the step; at a few tokens that cost is the step.
     graph = torch.cuda.CUDAGraph()
     cap = torch.cuda.Stream()
     cap.wait_stream(stream)
     with torch.cuda.stream(cap):
         with torch.cuda.graph(graph, stream=cap):
-            for i in range(args.steps):
+            for i in range(aux):
                 step(sets[i % nsets])
     stream.wait_stream(cap)
     graph.replay()
@@ -312,7 +328,7 @@ def measure(torch, w, inp, args, push, headline=False):
     graph.replay()
     g1.record(stream)
     torch.cuda.synchronize()
-    res["graph_ms"] = g0.elapsed_time(g1) / args.steps
+    res["graph_ms"] = g0.elapsed_time(g1) / aux
     del graph
     res["scratch_ok"] = all(s.scratch_clean() for s in sets)
     del sets, g
@@ -331,7 +347,7 @@ def summary(w, r):
             "step_us": round(r["ms_step"] * 1e3, 2), "step_GB/s": round(r["step_b"] / r["ms_step"] / 1e6, 1),
             "graph_replay_step_us": round(r["graph_ms"] * 1e3, 2), "kernels": kern,
             "buffer_sets_rotated": r["sets"], "rotated_step_bytes": r["rotated_bytes"],
-            "scratch_clean": r["scratch_ok"]}
+            "warmup": r["warmup"], "steps": r["steps"], "scratch_clean": r["scratch_ok"]}
 
 
 def main():
@@ -439,6 +455,7 @@ def main():
                    "graph_replay_step_us": round(r["graph_ms"] * 1e3, 2),
                    "buffer_sets_rotated": r["sets"], "rotated_step_bytes": r["rotated_bytes"],
                    "scratch_clean": r["scratch_ok"],
+                   "per_kernel_and_graph_launches": r["aux_launches"],
                    "frac_of_hbm_peak": round(value / HBM_PEAK_GBPS, 4),
                    "stream_reference_GBps": dict(ref, what="torch copy_ (1 GiB read + 1 GiB written) and fill_ "
                                                            "(1 GiB written) on the same GPU, 20 launches each")
