@@ -51,8 +51,9 @@ constexpr bool kCombineNtLoad = true;       // returned rows: non-temporal loads
 constexpr bool kCombineNtStore = true;      // out rows: non-temporal stores
 constexpr bool kPushNtLoad = true;          // rows the push moves: non-temporal loads
 constexpr bool kPushNtStore = true;         // landing rows: non-temporal stores
-constexpr int kXEarlyBlocks = 2560;         // launches of more blocks request x before COUNT
+constexpr int kXEarlyBlocks = 2560;         // launches of more blocks (not self-summing) request x before COUNT
 constexpr int kSelfScanBlocks = 1024;       // launches of up to this many blocks sum the tile counts in every block
+                                            // (and, within kSelfScanWords, any launch of slabs of <= 4 chunks)
 constexpr int kXMidSelfCpw = 4;             // self-summing launches with slabs of at most this many chunks request
                                             // x between COUNT and the SCAN's wait
 constexpr int kSelfScanWords = 8192;        // ... and sum up to this many published words per block at any size

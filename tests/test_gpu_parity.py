@@ -241,8 +241,8 @@ SCALES = [
     # name, base workload (None: ragged rows, 5 PEs, 3 experts each, topk 7), wire, scaleDim.
     # The scale rows travel as the fourth metadata field of every received row (MORI JIT v2
     # §4/§5: the dispatch's scales and the out_scales region; mori PR #599's merge notes).
-    ("fp8_scales56_h7168", "gen_zipf_h7168", "fp8", 56),  # one scale per 128 values; self-summing scan
-    ("fp4x2_scales1_h7168", "gen_zipf_h7168", "fp4x2", 1),  # one per token; x before COUNT
+    ("fp8_scales56_h7168", "gen_zipf_h7168", "fp8", 56),  # one scale per 128 values; 4 + 3-chunk slabs, x mid
+    ("fp4x2_scales1_h7168", "gen_zipf_h7168", "fp4x2", 1),  # one per token; self-summing, x mid
     ("bf16_scales56_leader_scan", "gen_zipf_h7168", "bf16", 56),  # 2048 blocks: tile leaders publish
     ("fp32_scales8_x_early", "gen_zipf_h7168", "fp32", 8),  # 4096 blocks: x before COUNT
     ("bf16_scales64_defaults", "epcfg_defaults", "bf16", 64),  # local scan, exactly one wave of scales
@@ -406,7 +406,7 @@ GRAPH_CASES = [
     # id, workload, overrides
     ("epcfg_defaults", "epcfg_defaults", None),  # 2 tiles: 2-chunk slabs, local scan
     ("pr_scale", "pr_scale", None),  # 8 tiles: local scan, scratch untouched
-    # 16 tiles, 256 blocks: every block sums the published counts, x before COUNT (4-chunk slabs)
+    # 16 tiles, 256 blocks: every block sums the published counts, x mid (4-chunk slabs)
     ("h2048_t1024_self_scan", "gen_zipf_h2048", dict(numTokens=1024, maxTokPerRank=1024)),
     # 2048 blocks: the tile leaders publish base rows, x after the SCAN
     ("h7168_t4096_leader_scan", "gen_zipf_h7168", None),

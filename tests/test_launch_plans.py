@@ -176,7 +176,8 @@ def test_gpu_parity_reaches_every_dispatch_variant(tmp_path):
     assert variants <= compiled, sorted(variants - compiled)
     assert compiled == variants, sorted(compiled - variants)
     assert len(compiled) == 56
-    # a self-summing launch (<= 1024 blocks) never requests x before COUNT (> 2560 blocks)
+    # a self-summing launch requests x after the SCAN (7- and 8-chunk slabs) or between COUNT and
+    # the SCAN's wait (at most 4 chunks), never before COUNT
     assert modes == {(0, 0), (0, 1), (1, 0), (1, 2)}, sorted(modes)
 
 
