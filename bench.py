@@ -218,21 +218,34 @@ def host_cpu():
     return {"cpu_model": model, "nproc": os.cpu_count(), "usable_cores": usable}
 
 
+def cacheable_bytes(w):
+    """Bytes of one buffer set that the path reads or writes with plain
+    (cache-allocating) accesses and that the next use of the set would find
+    again: the token inputs (x, ids, weights, scales), sendMap and the
+    received rows' metadata (at most min(W, K) rows per token).  The row
+    copies themselves use non-temporal accesses, which do not keep a set's
+    data in the 256 MB memory-side cache; x did stay there between uses of a
+    set when only the whole step's bytes were counted (4096 tokens x h7168:
+    dispatch 40.1 us with 3 sets, 54.0 with 6, 55.6 with 10)."""
+    T, K, W, S = w.numTokens, w.numExpertPerToken, w.worldSize, w.scaleDim
+    xr, _, _ = row_bytes(w)
+    u_max = T * min(W, K)
+    return T * (xr + K * 8 + S * 4) + T * K * 4 + u_max * (4 + K * 8 + S * 4)
+
+
 def rotation(torch, w, push, requested):
-    """Buffer sets to cycle: the requested number, or at least 3 and as many
-    as make the bytes the rotated steps touch exceed COLD_BYTES (estimated
-    with every token reaching min(W, K) PEs), within 64 sets, 8 GB of
-    buffers and half the free device memory.  Configurations of a few
-    tokens touch too little to leave the cache that way (they are bound by
-    launch latency, not bytes)."""
+    """Buffer sets to cycle: the requested number, or as many as make the
+    cacheable bytes of the rotated sets exceed COLD_BYTES (at least 3, and at
+    least 2 where memory allows no more), within 1024 sets, 16 GB of buffers
+    and half the free device memory.  Configurations of a few tokens touch
+    too little to leave the cache that way (they are bound by launch
+    latency, not bytes)."""
     b = set_bytes(w, push)
     if requested > 0:
         return requested
-    u_max = w.numTokens * min(w.worldSize, w.numExpertPerToken)
-    touched = sum(push_bytes(w, u_max)) + algorithmic_bytes(w, u_max)[0] if push else sum(algorithmic_bytes(w, u_max))
     free, _ = torch.cuda.mem_get_info()
-    n = max(3, math.ceil(COLD_BYTES / max(touched, 1)))
-    return max(1, min(n, 64, int((8 << 30) // b), int(free * 0.5 // b)))
+    n = max(3, math.ceil(COLD_BYTES / max(cacheable_bytes(w), 1)))
+    return max(1, min(n, 1024, int((16 << 30) // b), int(free * 0.5 // b)))
 
 
 # Launches per loop of the per-kernel durations and graph replays (and the

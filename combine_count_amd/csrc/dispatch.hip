@@ -194,33 +194,31 @@ __device__ __forceinline__ void copy_scale_tail(const DispatchParams &P, int32_t
 // One kernel.  A block has 4 waves and copies the 4*NTW tokens
 // [sub*4*NTW, (sub+1)*4*NTW) of a 64-token tile -- NTW consecutive tokens per
 // wave -- over chunks [slab*CPW, (slab+1)*CPW).  Block b = blockIdx.x is
-// (tile * nSubs + sub) * nSlabs + slab, except in self-summing launches
-// (selfScan), where the tile leaders (sub 0, slab 0) come first: blocks
-// 0..nTiles-1, then every tile's other blocks in the same order.  The
+// (tile * nSubs + sub) * nSlabs + slab, except where every block sums the
+// SCAN (SCAN self), where the tile leaders (sub 0, slab 0) come first:
+// blocks 0..nTiles-1, then every tile's other blocks in the same order.  The
 // leaders' COUNT then starts in the first blocks of the grid, before the
 // rest of it floods the memory with row loads (4096 tokens: fp4x2 rows 16.1
 // -> 15.4 us, h2048 17.2 -> 16.6; larger launches, whose blocks wait on
 // their leader, lose 2-5% with it).
-//   0. Launches of at most kLocalScanTiles tiles request all
-//      their loads first and scan locally (step 2); the others:
+//   0. Loads.  A local scan (launches of at most kLocalScanTiles tiles)
+//      requests every load up front: the ids it counts, then the x slabs and
+//      the metadata rows.  The other forms request the wave's x slabs before
+//      COUNT (with x cold in HBM, the sooner they are in flight the better),
+//      with COUNT's ids ahead of them when every block sums the SCAN and
+//      behind them when the tile leaders publish (plan_dispatch in
+//      epdc_internal.h has the measurements).
 //   1. COUNT (wave 0): the tile's PE masks (each lane's ids requested
-//      together) and per-PE ballots; the tile's
-//      leader (its first block: sub 0, slab 0) publishes the per-PE counts
-//      as count+1.
+//      together) and per-PE ballots; the tile's leader (its first block:
+//      sub 0, slab 0) publishes the per-PE counts as count+1.
 //   2. SCAN: the leader sums the published counts of all earlier tiles into
 //      the tile's base row on each PE and publishes it as base+1; the
 //      tile's other blocks wait for that single line (so polling traffic
-//      does not grow with the number of blocks per tile).  In launches of
-//      at most kSelfScanBlocks blocks every block sums the
-//      counts itself (selfScan), which takes the publish-and-poll round
-//      trip off the path.
-//   3. Loads: the slab-0 waves' metadata rows (ids, weights and scales),
-//      then every wave's NTW x slabs, once the SCAN is done (XO late); or
-//      the x slabs before COUNT (XO early); or, once every wave has waited
-//      for COUNT, the SCAN's first reads, then the metadata rows and the x
-//      slabs as soon as those reads are in, before the rest of the SCAN (XO
-//      mid).  See plan_dispatch in epdc_internal.h for which launch takes
-//      which order.
+//      does not grow with the number of blocks per tile).  With SCAN self
+//      every block sums the counts itself, which takes the
+//      publish-and-poll round trip off the path.
+//   3. The slab-0 waves' metadata rows (ids, weights and scales) are
+//      requested once the SCAN is done.
 //   4. FINALIZE: one wait for the wave's loads, then every store of its NTW
 //      tokens to every destination, with no further wait (vmcnt is one
 //      in-order counter for loads and stores on this ISA, so waiting on a
@@ -230,15 +228,13 @@ __device__ __forceinline__ void copy_scale_tail(const DispatchParams &P, int32_t
 //   5. The last block to finish clears the published counts; the done
 //      counters wrap to zero by themselves, so the scratch is zero again for
 //      the next call (and for every replay of a captured graph).
-// XO (the x order) is a compile-time choice: with it a runtime flag, the
-// compiler's waits had to cover every load order at once (measured: the
-// 4096-token h7168 launch, which never takes the early order, 1.4% slower).
-template <int CPW, int NTW, bool FULL, bool LOCAL, int XO>
-__global__ __launch_bounds__(256) void dispatch_kernel(DispatchParams P, int nSlabs, int nSubs, int nBlocks,
-                                                            int selfScan) {
-    constexpr bool xEarly = XO == kXOrderEarly;
-    constexpr bool xMid = XO == kXOrderMid;
-    static_assert(!(LOCAL && XO != kXOrderLate), "a local scan requests every load up front");
+// The SCAN form (and with it the load order) is a compile-time choice: with
+// the order a runtime flag, the compiler's waits had to cover every order at
+// once (measured: the 4096-token h7168 launch 1.4% slower).
+template <int CPW, int NTW, bool FULL, int SCAN>
+__global__ __launch_bounds__(256) void dispatch_kernel(DispatchParams P, int nSlabs, int nSubs, int nBlocks) {
+    constexpr bool localScan = SCAN == kScanLocal;
+    constexpr bool selfScan = SCAN == kScanSelf;
     __shared__ uint64_t sMask[kTile];  // destination-PE set of each token of the tile
     __shared__ uint64_t sBal[64];      // per PE: which tokens of the tile go there
     __shared__ int32_t sPre[64];       // per PE: rows taken by earlier tiles
@@ -256,7 +252,7 @@ __global__ __launch_bounds__(256) void dispatch_kernel(DispatchParams P, int nSl
     __syncthreads();
     const int b = blockIdx.x;
     int slab, sub, tile;
-    if (selfScan) {  // leaders first
+    if constexpr (selfScan) {  // leaders first
         if (b < nTilesAll) {
             tile = b;
             sub = 0;
@@ -279,15 +275,14 @@ __global__ __launch_bounds__(256) void dispatch_kernel(DispatchParams P, int nSl
     const int nTok = min(kTile, P.T - tok0);
     const int iBeg = (sub * 4 + wave) * NTW;  // this wave's tokens: [iBeg, iBeg + NTW) of the tile
     const uint8_t *xTile = P.x + (int64_t)tok0 * P.rowBytes;
-    // LOCAL (launches of at most kLocalScanTiles tiles): every
-    // block counts the earlier tiles' tokens itself (their ids are a few KB,
-    // read from L2), so there is no publishing, no cross-block wait and no
+    // SCAN local (launches of at most kLocalScanTiles tiles): every block
+    // counts the earlier tiles' tokens itself (their ids are a few KB, read
+    // from L2), so there is no publishing, no cross-block wait and no
     // scratch, and every load can be issued up front -- small launches are
     // bound by round trips, not bytes.  (One tile: its base rows are 0.)  A
     // separate instantiation, so the scratch path compiles as if alone.  A
     // block whose token group lies past the last token only counts itself
     // done.
-    constexpr bool localScan = LOCAL;
     const bool active = sub * 4 * NTW < nTok;
     if (active) {
 
@@ -319,18 +314,19 @@ __global__ __launch_bounds__(256) void dispatch_kernel(DispatchParams P, int nSl
             if (slab == 0 && i < nTok && lane < P.S) msc[j] = P.scales[(int64_t)(tok0 + i) * P.S + lane];
         }
     };
-    // The ids COUNT reads (wave 0: a token of the tile per lane) and, for a
-    // local scan, those of the earlier tiles this wave counts (tiles wave,
-    // wave + 4, ...; all full) go out before the local scan's x slabs, so
-    // counting waits for them alone (one round trip where a scan is a chain
-    // of them).  With xEarly the x slabs go out first: there the blocks that
-    // count sooner only reach the SCAN's wait sooner and poll it longer
-    // (measured 1% slower at 16384 tokens).
+    // 0. Loads.  The ids COUNT reads (wave 0: a token of the tile per lane)
+    // and, for a local scan, those of the earlier tiles this wave counts
+    // (tiles wave, wave + 4, ...; all full) go out before the local scan's
+    // x slabs, so counting waits for them alone (one round trip where a scan
+    // is a chain of them); so do they when every block sums the SCAN.  When
+    // the tile leaders publish, the x slabs go out first: there the blocks
+    // that count sooner only reach the wait for the leader's line sooner.
     constexpr int kScanPerWave = (kLocalScanTiles + 2) / 4 > 0 ? (kLocalScanTiles + 2) / 4 : 1;
     int32_t idOwn[8];
     int32_t idScan[kScanPerWave][8];
-    if (!localScan && xEarly) load_x();
+    if constexpr (SCAN == kScanLeader) load_x();
     if (wave == 0) load_ids(P, tok0 + min(lane, nTok - 1), idOwn);
+    if constexpr (selfScan) load_x();
     if constexpr (localScan) {
 #pragma unroll
         for (int i = 0; i < kScanPerWave; ++i)
@@ -356,15 +352,12 @@ __global__ __launch_bounds__(256) void dispatch_kernel(DispatchParams P, int nSl
             __hip_atomic_store(published + (int64_t)tile * P.Wp + lane, (uint32_t)cnt + 1u, __ATOMIC_RELAXED,
                                __HIP_MEMORY_SCOPE_AGENT);
     }
-    // x mid: every wave waits for COUNT (its ids' round trip runs alone), so
-    // that the SCAN's reads go out before the x flood.
-    if constexpr (xMid) __syncthreads();
 
     // 3. SCAN: exclusive base of this tile on each PE.  The leader sums the
     // published counts of all earlier tiles (the row stride Wp is a power of
     // two dividing 256, so thread tid only ever sums PE tid % Wp) and
     // publishes the result; the tile's other blocks wait for that one line.
-    // With selfScan every block sums for itself and nothing is published:
+    // With SCAN self every block sums for itself and nothing is published:
     // a block still waits only for the counts of earlier tiles, whose
     // leaders were dispatched before it.
     // Tile 0's base rows are 0: nothing to sum, publish or wait for.  A
@@ -386,30 +379,6 @@ __global__ __launch_bounds__(256) void dispatch_kernel(DispatchParams P, int nSl
         const int n = tile * P.Wp;
         uint32_t acc = 0;
         int idx = tid;
-        if constexpr (xMid) {
-            // The first 1024 published words are requested, then the
-            // metadata rows and the x slabs.  As compiled, the x loads wait
-            // for those words to arrive: the wait analysis merges the paths
-            // on which the ids' loads were not consumed and waits for every
-            // earlier load.  (An explicit wait after COUNT lets the x loads
-            // overlap the words' round trip; measured even: 4096 tokens,
-            // fp4x2 rows 15.41 against 15.55 us, h1024 11.64 against 11.34,
-            // h2048 at 16384 tokens 47.88 against 47.45.)  A word not yet
-            // published is polled again behind the x loads.
-            uint32_t v[4];
-#pragma unroll
-            for (int i = 0; i < 4; ++i) v[i] = idx + i * 256 < n ? load_published(published + idx + i * 256) : 1u;
-            load_meta();
-            load_x();
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                if (idx + i * 256 < n) {
-                    if (v[i] == 0) v[i] = wait_published(published + idx + i * 256, hdr + kScratchError);
-                    acc += v[i] - 1u;
-                }
-            }
-            idx += 4 * 256;
-        }
         for (; idx + 3 * 256 < n; idx += 4 * 256) {
             uint32_t v0 = load_published(published + idx), v1 = load_published(published + idx + 256);
             uint32_t v2 = load_published(published + idx + 512), v3 = load_published(published + idx + 768);
@@ -425,37 +394,24 @@ __global__ __launch_bounds__(256) void dispatch_kernel(DispatchParams P, int nSl
             acc += v - 1u;
         }
         if (acc) atomicAdd(&sPre[tid & (P.Wp - 1)], (int32_t)acc);
-        if (!selfScan) {
+        if constexpr (!selfScan) {
             __syncthreads();
             if (tid < P.Wp)
                 __hip_atomic_store(prefixes + (int64_t)tile * P.Wp + tid, (uint32_t)sPre[tid] + 1u,
                                    __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }
-    } else if (tile > 0) {
-        uint32_t v = tid < P.Wp ? load_published(prefixes + (int64_t)tile * P.Wp + tid) : 1u;
-        if constexpr (xMid) {
-            load_meta();
-            load_x();
-        }
-        if (tid < P.Wp) {
-            if (v == 0) v = wait_published(prefixes + (int64_t)tile * P.Wp + tid, hdr + kScratchError);
-            sPre[tid] = (int32_t)(v - 1u);
-        }
-    } else if constexpr (xMid) {  // tile 0: no SCAN to wait for
-        load_meta();
-        load_x();
+    } else if (tile > 0 && tid < P.Wp) {
+        uint32_t v = load_published(prefixes + (int64_t)tile * P.Wp + tid);
+        if (v == 0) v = wait_published(prefixes + (int64_t)tile * P.Wp + tid, hdr + kScratchError);
+        sPre[tid] = (int32_t)(v - 1u);
     }
     __syncthreads();
 
-    // Scanning through the scratch with x late, the metadata rows and then
-    // the x slabs are requested only now: issued before the SCAN, the x flood
-    // would delay the SCAN's own small reads (with x early only the metadata
-    // rows are left).  In every order no wait below follows a store.
+    // 3. Scanning through the scratch, the metadata rows are requested only
+    // now (the slab-0 waves' ids, weights and scales).  No wait below
+    // follows a store.
     const int32_t E = P.W * P.Epr;
-    if constexpr (!localScan && !xMid) {
-        load_meta();
-        if (!xEarly) load_x();
-    }
+    if constexpr (!localScan) load_meta();
 
     // 4. FINALIZE payload: one wait for every load above, then only stores.
     wait_vmcnt<0>();
@@ -530,11 +486,17 @@ __global__ __launch_bounds__(256) void dispatch_kernel(DispatchParams P, int nSl
 }
 
 // Runs a plan (plan_dispatch in epdc_internal.h) with its compiled variant.
-template <int CPW, int NTW, bool FULL, bool LOCAL, int XO>
+template <int CPW, int NTW, bool FULL, int SCAN>
 hipError_t launch_variant(const DispatchParams &P, const DispatchPlan &pl, hipStream_t stream) {
-    hipLaunchKernelGGL((dispatch_kernel<CPW, NTW, FULL, LOCAL, XO>), dim3((uint32_t)pl.nBlocks), dim3(256), 0, stream,
-                       P, pl.nSlabs, pl.nSubs, (int)pl.nBlocks, pl.selfScan ? 1 : 0);
+    hipLaunchKernelGGL((dispatch_kernel<CPW, NTW, FULL, SCAN>), dim3((uint32_t)pl.nBlocks), dim3(256), 0, stream, P,
+                       pl.nSlabs, pl.nSubs, (int)pl.nBlocks);
     return hipGetLastError();
+}
+
+template <int CPW, int NTW, int SCAN>
+hipError_t launch_full(const DispatchParams &P, const DispatchPlan &pl, hipStream_t stream) {
+    return pl.full ? launch_variant<CPW, NTW, true, SCAN>(P, pl, stream)
+                   : launch_variant<CPW, NTW, false, SCAN>(P, pl, stream);
 }
 
 template <int CPW, int NTW>
@@ -542,25 +504,13 @@ hipError_t launch_fused(const DispatchParams &P, const DispatchPlan &pl, hipStre
     static_assert(kTile % (4 * NTW) == 0, "a block's tokens must tile the 64-token tile");
     if (pl.nBlocks > INT32_MAX) return hipErrorInvalidConfiguration;
     if constexpr (NTW == 1) {
-        if (pl.local)  // every load is requested up front: no other x order
-            return pl.full ? launch_variant<CPW, NTW, true, true, kXOrderLate>(P, pl, stream)
-                           : launch_variant<CPW, NTW, false, true, kXOrderLate>(P, pl, stream);
-        if (pl.xOrder == kXOrderLate)
-            return pl.full ? launch_variant<CPW, NTW, true, false, kXOrderLate>(P, pl, stream)
-                           : launch_variant<CPW, NTW, false, false, kXOrderLate>(P, pl, stream);
-        // x mid: only self-summing launches of slabs of at most kXMidSelfCpw
-        // chunks (plan_dispatch)
-        if constexpr (CPW <= kXMidSelfCpw) {
-            if (pl.xOrder == kXOrderMid)
-                return pl.full ? launch_variant<CPW, NTW, true, false, kXOrderMid>(P, pl, stream)
-                               : launch_variant<CPW, NTW, false, false, kXOrderMid>(P, pl, stream);
-        }
+        if (pl.scan == kScanLocal) return launch_full<CPW, NTW, kScanLocal>(P, pl, stream);
+        if (pl.scan == kScanSelf) return launch_full<CPW, NTW, kScanSelf>(P, pl, stream);
     }
     // Several tokens per wave only come with launches of over 8192 blocks,
-    // which always request x before COUNT (plan_dispatch).
-    if (pl.xOrder != kXOrderEarly) return hipErrorInvalidConfiguration;
-    return pl.full ? launch_variant<CPW, NTW, true, false, kXOrderEarly>(P, pl, stream)
-                   : launch_variant<CPW, NTW, false, false, kXOrderEarly>(P, pl, stream);
+    // whose tile leaders always publish (plan_dispatch).
+    if (pl.scan != kScanLeader) return hipErrorInvalidConfiguration;
+    return launch_full<CPW, NTW, kScanLeader>(P, pl, stream);
 }
 
 template <int CPW>

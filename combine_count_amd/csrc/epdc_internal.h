@@ -45,18 +45,15 @@ __device__ __forceinline__ void wait_vmcnt() {
 
 // Measured choices (each was timed against its alternatives; the reasons
 // are with the code that uses them).
-constexpr bool kDispatchNtLoad = false;     // x rows: plain loads
+constexpr bool kDispatchNtLoad = true;      // x rows: non-temporal loads
 constexpr bool kDispatchNtStore = true;     // recvX rows: non-temporal, device-scope stores (store16_nt_dev)
 constexpr bool kCombineNtLoad = true;       // returned rows: non-temporal loads
 constexpr bool kCombineNtStore = true;      // out rows: non-temporal stores
 constexpr bool kPushNtLoad = true;          // rows the push moves: non-temporal loads
 constexpr bool kPushNtStore = true;         // landing rows: non-temporal stores
-constexpr int kXEarlyBlocks = 2560;         // launches of more blocks (not self-summing) request x before COUNT
 constexpr int kSelfScanBlocks = 1024;       // launches of up to this many blocks sum the tile counts in every block
-                                            // (and, within kSelfScanWords, any launch of slabs of <= 4 chunks)
-constexpr int kXMidSelfCpw = 4;             // self-summing launches with slabs of at most this many chunks request
-                                            // x between COUNT and the SCAN's wait
-constexpr int kSelfScanWords = 8192;        // ... and sum up to this many published words per block at any size
+constexpr int kSelfScanAnyCpw = 4;          // ... and launches of slabs of at most this many chunks, at any size
+constexpr int kSelfScanWords = 8192;        //     while a block sums at most this many published words
 constexpr int kNarrowTiles = 4;             // launches of up to this many tiles use 1- or 2-chunk slabs
 constexpr int kLocalScanTiles = 8;          // launches of up to this many 64-token tiles scan in every block
 constexpr int kCombineGroup = 8;            // returned rows requested together per wave (gather combine)
@@ -195,15 +192,17 @@ inline DivMagic div_magic(uint32_t d) {
     return DivMagic{(uint32_t)m, l < 1 ? l : 1, l > 1 ? l - 1 : 0};
 }
 
-// Launch geometry of one dispatch, chosen from the token count and the row
-// size alone (host code; the launcher runs exactly this plan, and a host test
-// pins it for the documented shapes).
-// When a dispatch wave requests its x slabs (a compile-time choice of the
-// kernel): after the SCAN, before COUNT, or between COUNT and the SCAN's wait
-// (once the SCAN's own reads are out).
-constexpr int kXOrderLate = 0;
-constexpr int kXOrderEarly = 1;
-constexpr int kXOrderMid = 2;
+// Launch geometry of one dispatch, chosen from the token count, the row size
+// and the world size (host code; the launcher runs exactly this plan, and a
+// host test pins it for the documented shapes).
+// The SCAN's form, a compile-time choice of the kernel (dispatch.hip, step
+// 3): every block counts the earlier tiles' ids itself (local); every block
+// sums the counts the tile leaders publish (self); or the tile leader sums
+// them and publishes the tile's base rows, which its other blocks read
+// (leader).
+constexpr int kScanLocal = 0;
+constexpr int kScanSelf = 1;
+constexpr int kScanLeader = 2;
 
 struct DispatchPlan {
     int32_t cpw;      // 1 KiB chunks per slab: 1, 2, 4, 7 or 8
@@ -212,9 +211,7 @@ struct DispatchPlan {
     int32_t nSubs;    // blocks per tile and slab (64 / (4 * ntw))
     int64_t nBlocks;  // grid size (0: no tokens, only recvCount is written)
     bool full;        // every slab lies inside the row: no per-lane bound checks
-    bool local;       // local scan: every block counts the earlier tiles' ids
-    bool selfScan;    // every block sums the published tile counts
-    int32_t xOrder;   // when the x slabs are requested: kXOrderLate / kXOrderEarly / kXOrderMid
+    int32_t scan;     // kScanLocal / kScanSelf / kScanLeader
 };
 
 inline DispatchPlan plan_dispatch(int32_t T, int32_t rowBytes, int32_t W) {
@@ -231,13 +228,14 @@ inline DispatchPlan plan_dispatch(int32_t T, int32_t rowBytes, int32_t W) {
     // checks); other rows (not a whole number of 1 KiB chunks, e.g. 3.5 KiB
     // fp4x2 rows at hidden 7168) take the narrowest of 1/2/4/7/8 chunks that
     // covers the row (8 beyond that) with bound checks on the tail.  Rows of
-    // exactly 7 chunks (fp8 rows at h7168, bf16 at h3584) take two
-    // bound-checked 4-chunk slabs (4 + 3), which puts them under the
-    // self-summing SCAN with x mid below (4096 tokens: fp8 rows 24.33 ->
-    // 23.97 us, h3584 24.24 -> 23.91; 8192 fp8 tokens 44.2 -> 41.7).
+    // exactly 7 chunks (fp8 rows at h7168, bf16 at h3584) in launches whose
+    // 7-chunk slabs would pass kSelfScanBlocks take two bound-checked 4-chunk
+    // slabs (4 + 3) instead, which keeps them under the self-summing SCAN
+    // below (8192 fp8 tokens 52.1 -> 49.8 us; at 4096 tokens one 7-chunk
+    // slab, already self-summing, is faster: 25.6 against 30.2).
     if (nTiles <= kNarrowTiles)
         pl.cpw = nChunks <= 1 ? 1 : (!whole || nChunks % 2 == 0) ? 2 : 1;
-    else if (whole && nChunks == 7)
+    else if (whole && nChunks == 7 && (int64_t)nTiles * (kTile / 4) > kSelfScanBlocks)
         pl.cpw = 4;
     else if (whole)
         pl.cpw = nChunks % 8 == 0 ? 8 : nChunks % 7 == 0 ? 7 : nChunks % 4 == 0 ? 4 : nChunks % 2 == 0 ? 2 : 1;
@@ -255,48 +253,38 @@ inline DispatchPlan plan_dispatch(int32_t T, int32_t rowBytes, int32_t W) {
     // wave within 8 tiles takes over 128 slabs per row (rows of 128 KiB and
     // up), and its id registers would then cost occupancy; such launches scan
     // through the scratch.
-    pl.local = pl.ntw == 1 && nTiles <= kLocalScanTiles;
     // Every block sums the earlier tiles' counts itself in launches of up to
     // 4 blocks per CU, where it saves a round trip (measured at 4096 tokens:
     // fp4x2 rows 2.6%, h2048 2.3%; 640 / 1024 tokens at h7168 5.3% / 3.6%).
     // In larger launches of 7- and 8-chunk slabs the tile leader's one
     // published line is faster (1.5% at 2048 blocks, 1.6% for fp8 rows at
-    // 1536; every block summing with x mid: 16384 tokens 5% slower).  One-
-    // token-per-wave launches of slabs of at most 4 chunks sum in every
-    // block at any size, with x mid, while a block's sum stays within
-    // kSelfScanWords published words (one library per process, 3 rounds,
-    // against the leader's line with x before COUNT: fp4x2 rows at 8192 /
-    // 16384 / 65536 tokens 28.6 -> 24.3, 49.4 -> 43.0, 236.4 -> 188.0 us;
-    // h2048 at 16384 tokens 53.3 -> 48.0; h1024 at 16384 / 65536 tokens
-    // 37.6 -> 29.5, 173.3 -> 131.8).
+    // 1536; every block summing at 16384 tokens: 7.5% slower).  One-token-
+    // per-wave launches of slabs of at most 4 chunks sum in every block at
+    // any size, while a block sums at most kSelfScanWords published words
+    // (cold x, one library per process, 3 rounds, against the leader's line:
+    // fp4x2 rows at 16384 tokens 57.4 -> 50.1 us, h2048 at 16384 tokens 63.2
+    // -> 56.3, fp8 rows at 8192 tokens 60.3 -> 50.1).
     int32_t wp = 1;
     while (wp < W) wp <<= 1;
-    pl.selfScan = !pl.local && (pl.nBlocks <= kSelfScanBlocks ||
-                                (pl.cpw <= kXMidSelfCpw && pl.ntw == 1 && (int64_t)nTiles * wp <= kSelfScanWords));
-    // x before COUNT in launches of well over one round of resident blocks
-    // (about 7 per CU, 1792 on the chip): blocks that start once HBM is
-    // saturated would otherwise idle through the SCAN's round trips, each
-    // queued behind streaming traffic.  In smaller launches the early x flood
-    // delays the SCAN instead.  Measured crossover: between 2048 blocks (after
-    // the SCAN 1-3% faster) and 3072 (before COUNT 4% faster; 8-10% at 4096).
-    // Self-summing launches whose slabs are at most 4 chunks request x once
-    // COUNT is done and the SCAN's reads are out, before waiting for them:
-    // the ids' round trip then runs without the x flood and the x loads
-    // overlap the SCAN's (4096 tokens, one library per process, 3 rounds,
-    // against x before COUNT: fp4x2 rows 16.06 -> 15.62 us, h2048 17.27 ->
-    // 16.67, h1024 12.04 -> 11.59, fp8 rows at h4096 17.25 -> 16.62; x after
-    // the SCAN was slower than both).  With 7- or 8-chunk slabs the order
-    // between COUNT and the SCAN's wait was mixed (fp8 rows at h7168 1.7%
-    // slower, 2000 tokens at h7168 1.5% faster), so they keep x after the
-    // SCAN.  (A local scan requests every load up front anyway.)
-    if (pl.local)
-        pl.xOrder = kXOrderLate;
-    else if (pl.selfScan && pl.cpw <= kXMidSelfCpw)
-        pl.xOrder = kXOrderMid;
-    else if (pl.nBlocks > kXEarlyBlocks)
-        pl.xOrder = kXOrderEarly;
+    if (pl.ntw == 1 && nTiles <= kLocalScanTiles)
+        pl.scan = kScanLocal;
+    else if (pl.nBlocks <= kSelfScanBlocks ||
+             (pl.cpw <= kSelfScanAnyCpw && pl.ntw == 1 && (int64_t)nTiles * wp <= kSelfScanWords))
+        pl.scan = kScanSelf;
     else
-        pl.xOrder = kXOrderLate;
+        pl.scan = kScanLeader;
+    // The x order goes with the SCAN form (dispatch.hip): a local scan
+    // requests every load up front, the ids first; the other forms request
+    // the x slabs before COUNT, with the ids ahead of them when every block
+    // sums (a block counts sooner and its first poll finds the leaders'
+    // counts; 4096 tokens, cold x: fp4x2 rows 16.16 -> 15.70 us, h2048
+    // 17.55 -> 17.16) and behind them when the leaders publish (there
+    // counting sooner only lengthens the wait for the leader's line: 4096
+    // tokens x h7168 50.84 against 51.63).  With x cold in HBM every launch
+    // gains from requesting x before COUNT (4096 tokens x h7168 55.4 -> 50.8
+    // us; x after the SCAN, and x between COUNT and the SCAN's wait, were
+    // tuned with x left in the memory-side cache by the previous call, where
+    // they won).
     return pl;
 }
 

@@ -1,7 +1,7 @@
 // Prints the launch plans of csrc/epdc_internal.h (host code the launchers
 // run) for shapes given on the command line:
-//   dispatch T rowBytes W ...  -> T rowBytes W cpw ntw nSlabs nSubs nBlocks full local selfScan xOrder
-//                                 (xOrder: 0 after the SCAN, 1 before COUNT, 2 between COUNT and the SCAN's wait)
+//   dispatch T rowBytes W ...  -> T rowBytes W cpw ntw nSlabs nSubs nBlocks full scan
+//                                 (scan: 0 local, 1 every block sums, 2 the tile leaders publish)
 //   combine  T rowBytes ...    -> T rowBytes cpw nSlabs waves nBlocks full
 //   push     L rowBytes ...    -> L rowBytes cpw nSlabs waves nBlocks full   (L = landing rows)
 #include <cstdio>
@@ -20,8 +20,8 @@ int main(int argc, char **argv) {
         if (dispatch) {
             const int W = std::atoi(argv[i + 2]);
             const epdc::DispatchPlan p = epdc::plan_dispatch(n, rowBytes, W);
-            std::printf("%d %d %d %d %d %d %d %lld %d %d %d %d\n", n, rowBytes, W, p.cpw, p.ntw, p.nSlabs, p.nSubs,
-                        (long long)p.nBlocks, (int)p.full, (int)p.local, (int)p.selfScan, (int)p.xOrder);
+            std::printf("%d %d %d %d %d %d %d %lld %d %d\n", n, rowBytes, W, p.cpw, p.ntw, p.nSlabs, p.nSubs,
+                        (long long)p.nBlocks, (int)p.full, (int)p.scan);
         } else {
             const epdc::RowPlan p =
                 !std::strcmp(kind, "combine") ? epdc::plan_combine(n, rowBytes) : epdc::plan_push(n, rowBytes);

@@ -56,17 +56,17 @@ def test_no_scratch_and_no_spills(compiled):
 def test_default_variants_keep_their_occupancy(compiled):
     d, c, p = compiled["dispatch.hip"][0], compiled["combine.hip"][0], compiled["combine_push.hip"][0]
     # 4096 tokens x h7168 bf16: dispatch 7-chunk slabs, 1 token per wave, no bound checks,
-    # scan through the scratch, x after the SCAN (last argument 0); its x-early twin (1:
-    # fp32 rows, 16384 tokens); and the same slabs for launches of at most 8 tiles (local scan)
-    assert _kernel(d, r"dispatch_kernelILi7ELi1ELb1ELb0ELi0EE")["Occupancy"] >= 7
-    assert _kernel(d, r"dispatch_kernelILi7ELi1ELb1ELb0ELi1EE")["Occupancy"] >= 7
-    assert _kernel(d, r"dispatch_kernelILi7ELi1ELb1ELb1ELi0EE")["Occupancy"] >= 7
-    # 4-chunk slabs with x between COUNT and the SCAN's wait (h2048; fp4x2 rows bound-checked)
-    assert _kernel(d, r"dispatch_kernelILi4ELi1ELb1ELb0ELi2EE")["Occupancy"] >= 7
-    assert _kernel(d, r"dispatch_kernelILi4ELi1ELb0ELb0ELi2EE")["Occupancy"] >= 7
+    # tile leaders publishing (last argument 2); the same slabs where every block sums (1: fp8
+    # rows at 4096 tokens) and for launches of at most 8 tiles (0: local scan)
+    assert _kernel(d, r"dispatch_kernelILi7ELi1ELb1ELi2EE")["Occupancy"] >= 7
+    assert _kernel(d, r"dispatch_kernelILi7ELi1ELb1ELi1EE")["Occupancy"] >= 7
+    assert _kernel(d, r"dispatch_kernelILi7ELi1ELb1ELi0EE")["Occupancy"] >= 7
+    # 4-chunk slabs where every block sums (h2048; fp4x2 rows bound-checked)
+    assert _kernel(d, r"dispatch_kernelILi4ELi1ELb1ELi1EE")["Occupancy"] >= 7
+    assert _kernel(d, r"dispatch_kernelILi4ELi1ELb0ELi1EE")["Occupancy"] >= 7
     # launches of at most 4 tiles: 2- (or 1-) chunk slabs under the local scan
-    assert _kernel(d, r"dispatch_kernelILi2ELi1ELb1ELb1ELi0EE")["Occupancy"] == 8
-    assert _kernel(d, r"dispatch_kernelILi1ELi1ELb1ELb1ELi0EE")["Occupancy"] == 8
+    assert _kernel(d, r"dispatch_kernelILi2ELi1ELb1ELi0EE")["Occupancy"] == 8
+    assert _kernel(d, r"dispatch_kernelILi1ELi1ELb1ELi0EE")["Occupancy"] == 8
     # gather combine, 2-chunk slabs, bf16 rows and output (up to 8 rows in flight), its
     # landing-row twin, and bf16 rows into an fp32 output
     assert _kernel(c, r"combine_kernelILi2ELb1ELb0ELb0ELb0EE")["Occupancy"] >= 4

@@ -8,52 +8,53 @@ import subprocess
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
-FIELDS = ("cpw", "ntw", "nSlabs", "nSubs", "nBlocks", "full", "local", "selfScan", "xOrder")
+FIELDS = ("cpw", "ntw", "nSlabs", "nSubs", "nBlocks", "full", "scan")
 ROW_FIELDS = ("cpw", "nSlabs", "waves", "nBlocks", "full")
 EXPECT = {
-    # (numTokens, rowBytes, worldSize): (cpw, ntw, nSlabs, nSubs, nBlocks, full, local, selfScan, xOrder)
-    # xOrder: 0 x after the SCAN, 1 x before COUNT, 2 x between COUNT and the SCAN's wait
-    # 4096 tokens x h7168 bf16: two 7-chunk slabs, 2048 blocks, tile leaders publish, x after the SCAN
-    (4096, 14336, 8): (7, 1, 2, 16, 2048, 1, 0, 0, 0),
-    # fp8 rows (7 chunks): two bound-checked 4-chunk slabs, every block sums the counts, x mid
-    (4096, 7168, 8): (4, 1, 2, 16, 2048, 0, 0, 1, 2),
-    # fp4x2 rows (3.5 KiB): one bound-checked 4-chunk slab, self-summing, x mid
-    (4096, 3584, 8): (4, 1, 1, 16, 1024, 0, 0, 1, 2),
-    # h2048 bf16: one 4-chunk slab, self-summing, x mid
-    (4096, 4096, 8): (4, 1, 1, 16, 1024, 1, 0, 1, 2),
-    # fp32 rows: four 7-chunk slabs, 4096 blocks: x before COUNT
-    (4096, 28672, 8): (7, 1, 4, 16, 4096, 1, 0, 0, 1),
-    # 16384 tokens: 8192 blocks, x before COUNT
-    (16384, 14336, 8): (7, 1, 2, 16, 8192, 1, 0, 0, 1),
+    # (numTokens, rowBytes, worldSize): (cpw, ntw, nSlabs, nSubs, nBlocks, full, scan)
+    # scan: 0 local (every block counts the earlier tiles' ids), 1 every block sums the leaders'
+    # published counts, 2 the tile leader publishes the tile's base rows
+    # 4096 tokens x h7168 bf16: two 7-chunk slabs, 2048 blocks, tile leaders publish
+    (4096, 14336, 8): (7, 1, 2, 16, 2048, 1, 2),
+    # fp8 rows (7 chunks): one 7-chunk slab, 1024 blocks, every block sums
+    (4096, 7168, 8): (7, 1, 1, 16, 1024, 1, 1),
+    # ... at 8192 tokens 7-chunk slabs would pass 1024 blocks: two 4-chunk slabs (4 + 3), every block sums
+    (8192, 7168, 8): (4, 1, 2, 16, 4096, 0, 1),
+    # fp4x2 rows (3.5 KiB): one bound-checked 4-chunk slab, every block sums
+    (4096, 3584, 8): (4, 1, 1, 16, 1024, 0, 1),
+    # h2048 bf16: one 4-chunk slab, every block sums
+    (4096, 4096, 8): (4, 1, 1, 16, 1024, 1, 1),
+    # fp32 rows: four 7-chunk slabs, 4096 blocks, leaders publish
+    (4096, 28672, 8): (7, 1, 4, 16, 4096, 1, 2),
+    # 16384 tokens: 8192 blocks, leaders publish
+    (16384, 14336, 8): (7, 1, 2, 16, 8192, 1, 2),
     # one tile: 2-chunk slabs (at most 4 tiles), local scan
-    (1, 14336, 8): (2, 1, 7, 16, 112, 1, 1, 0, 0),
-    (8, 14336, 8): (2, 1, 7, 16, 112, 1, 1, 0, 0),
+    (1, 14336, 8): (2, 1, 7, 16, 112, 1, 0),
+    (8, 14336, 8): (2, 1, 7, 16, 112, 1, 0),
     # two tiles of odd-chunk fp8 rows: 1-chunk slabs, local scan
-    (128, 7168, 8): (1, 1, 7, 16, 224, 1, 1, 0, 0),
-    # 8 tiles: 7-chunk slabs, still the local scan; 9 tiles: self-summing
-    (512, 14336, 8): (7, 1, 2, 16, 256, 1, 1, 0, 0),
-    (576, 14336, 8): (7, 1, 2, 16, 288, 1, 0, 1, 0),
-    # around the self-summing limit of 7-chunk slabs (1024 blocks)
-    (2047, 14336, 8): (7, 1, 2, 16, 1024, 1, 0, 1, 0),
-    (2049, 14336, 8): (7, 1, 2, 16, 1056, 1, 0, 0, 0),
-    # around the x-early limit (2560 blocks): 80 and 81 tiles
-    (5120, 14336, 8): (7, 1, 2, 16, 2560, 1, 0, 0, 0),
-    (5121, 14336, 8): (7, 1, 2, 16, 2592, 1, 0, 0, 1),
+    (128, 7168, 8): (1, 1, 7, 16, 224, 1, 0),
+    # 8 tiles: 7-chunk slabs, still the local scan; 9 tiles: every block sums
+    (512, 14336, 8): (7, 1, 2, 16, 256, 1, 0),
+    (576, 14336, 8): (7, 1, 2, 16, 288, 1, 1),
+    # around the every-block limit of 7-chunk slabs (1024 blocks)
+    (2047, 14336, 8): (7, 1, 2, 16, 1024, 1, 1),
+    (2049, 14336, 8): (7, 1, 2, 16, 1056, 1, 2),
+    (5121, 14336, 8): (7, 1, 2, 16, 2592, 1, 2),
     # slabs of at most 4 chunks sum in every block at any size while a block sums at most
     # 8192 published words (tiles x worldSize rounded up to a power of two)
-    (16384, 3584, 8): (4, 1, 1, 16, 4096, 0, 0, 1, 2),
-    (65536, 2048, 8): (2, 1, 1, 16, 16384, 1, 0, 1, 2),
-    (8192, 4096, 64): (4, 1, 1, 16, 2048, 1, 0, 1, 2),
-    (8256, 4096, 64): (4, 1, 1, 16, 2064, 1, 0, 0, 0),
-    (12000, 4096, 40): (4, 1, 1, 16, 3008, 1, 0, 0, 1),
+    (16384, 3584, 8): (4, 1, 1, 16, 4096, 0, 1),
+    (65536, 2048, 8): (2, 1, 1, 16, 16384, 1, 1),
+    (8192, 4096, 64): (4, 1, 1, 16, 2048, 1, 1),
+    (8256, 4096, 64): (4, 1, 1, 16, 2064, 1, 2),
+    (12000, 4096, 40): (4, 1, 1, 16, 3008, 1, 2),
     # 528-byte rows: more than 16384 / 32768 one-token waves take 2 / 4 tokens per wave
-    (66000, 528, 8): (1, 2, 1, 8, 8256, 0, 0, 0, 1),
-    (132000, 528, 8): (1, 4, 1, 4, 8252, 0, 0, 0, 1),
+    (66000, 528, 8): (1, 2, 1, 8, 8256, 0, 2),
+    (132000, 528, 8): (1, 4, 1, 4, 8252, 0, 2),
     # 8-chunk slabs; rows past 8 chunks that are not whole: 8-chunk slabs with bound checks
-    (1000, 8192, 8): (8, 1, 1, 16, 256, 1, 0, 1, 0),
-    (1000, 9728, 8): (8, 1, 2, 16, 512, 0, 0, 1, 0),
+    (1000, 8192, 8): (8, 1, 1, 16, 256, 1, 1),
+    (1000, 9728, 8): (8, 1, 2, 16, 512, 0, 1),
     # no tokens: nothing but recvCount
-    (0, 14336, 8): (0, 0, 0, 0, 0, 0, 0, 0, 0),
+    (0, 14336, 8): (0, 0, 0, 0, 0, 0, 0),
 }
 
 
@@ -136,27 +137,22 @@ def _gpu_parity_shapes():
 
 
 def _launchable_variants():
-    """(cpw, ntw, full, local, xOrder) of every dispatch kernel the launcher
-    can run (dispatch.hip, launch_fused): one token per wave with the local
-    scan, or scanning through the scratch with x after the SCAN or before
-    COUNT, or (slabs of at most 4 chunks) between COUNT and the SCAN's wait;
-    two or four tokens per wave only with x before COUNT (plan_dispatch
-    gives them only to launches of over 8192 blocks, which always take that
-    order)."""
+    """(cpw, ntw, full, scan) of every dispatch kernel the launcher can run
+    (dispatch.hip, launch_fused): one token per wave with any SCAN form; two
+    or four tokens per wave only with the tile leaders publishing
+    (plan_dispatch gives them only to launches of over 8192 blocks, which
+    never scan locally or in every block)."""
     out = set()
     for c in (1, 2, 4, 7, 8):
         for f in (0, 1):
-            out |= {(c, 1, f, 1, 0), (c, 1, f, 0, 0), (c, 1, f, 0, 1), (c, 2, f, 0, 1), (c, 4, f, 0, 1)}
-            if c <= 4:
-                out.add((c, 1, f, 0, 2))
+            out |= {(c, 1, f, 0), (c, 1, f, 1), (c, 1, f, 2), (c, 2, f, 2), (c, 4, f, 2)}
     return out
 
 
 def test_gpu_parity_reaches_every_dispatch_variant(tmp_path):
-    """The GPU parity cases reach all 56 compiled dispatch kernels (slab width x
-    tokens per wave x bound checks x SCAN form x x order), and every
-    combination of SCAN form (tile leader / every block) and x order that a
-    plan can give; no plan asks for a kernel that is not compiled."""
+    """The GPU parity cases reach all 50 compiled dispatch kernels (slab width x
+    tokens per wave x bound checks x SCAN form); no plan asks for a kernel
+    that is not compiled."""
     import sys
     sys.path.insert(0, ROOT)
     sys.path.insert(0, os.path.join(ROOT, "tests"))
@@ -167,18 +163,11 @@ def test_gpu_parity_reaches_every_dispatch_variant(tmp_path):
     assert r.returncode == 0, r.stderr
     shapes = [s for s in _gpu_parity_shapes() if s[0] > 0]
     got = _run(exe, "dispatch", shapes)
-    variants, modes = set(), set()
-    for cpw, ntw, _nSlabs, _nSubs, _nBlocks, full, local, self_scan, x_early in got.values():
-        variants.add((cpw, ntw, full, local, x_early))
-        if not local:
-            modes.add((self_scan, x_early))
+    variants = {(cpw, ntw, full, scan) for cpw, ntw, _nSlabs, _nSubs, _nBlocks, full, scan in got.values()}
     compiled = _launchable_variants()
+    assert len(compiled) == 50
     assert variants <= compiled, sorted(variants - compiled)
     assert compiled == variants, sorted(compiled - variants)
-    assert len(compiled) == 56
-    # a self-summing launch requests x after the SCAN (7- and 8-chunk slabs) or between COUNT and
-    # the SCAN's wait (at most 4 chunks), never before COUNT
-    assert modes == {(0, 0), (0, 1), (1, 0), (1, 2)}, sorted(modes)
 
 
 def test_random_plans_only_ask_for_compiled_kernels(tmp_path):
@@ -199,5 +188,5 @@ def test_random_plans_only_ask_for_compiled_kernels(tmp_path):
                for rb in (16, 1024, 3584, 7168, 14336, 28672, 65536) for w in (1, 8, 64)}
     got = _run(exe, "dispatch", sorted(shapes))
     compiled = _launchable_variants()
-    for (T, rb, W), (cpw, ntw, _s, _u, nB, full, local, _ss, xe) in got.items():
-        assert (cpw, ntw, full, local, xe) in compiled, (T, rb, W)
+    for (T, rb, W), (cpw, ntw, _s, _u, nB, full, scan) in got.items():
+        assert (cpw, ntw, full, scan) in compiled, (T, rb, W)
