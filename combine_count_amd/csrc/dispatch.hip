@@ -335,7 +335,7 @@ __global__ __launch_bounds__(256) void dispatch_kernel(DispatchParams P, int nSl
         load_meta();
     }
 
-    // 2. COUNT for this tile (wave 0); the tile's leader block (sub 0,
+    // 1. COUNT for this tile (wave 0); the tile's leader block (sub 0,
     // slab 0: the first block of the tile) publishes the per-PE counts.
     const bool leader = (sub == 0 && slab == 0);
     if (wave == 0) {
@@ -353,7 +353,7 @@ __global__ __launch_bounds__(256) void dispatch_kernel(DispatchParams P, int nSl
                                __HIP_MEMORY_SCOPE_AGENT);
     }
 
-    // 3. SCAN: exclusive base of this tile on each PE.  The leader sums the
+    // 2. SCAN: exclusive base of this tile on each PE.  The leader sums the
     // published counts of all earlier tiles (the row stride Wp is a power of
     // two dividing 256, so thread tid only ever sums PE tid % Wp) and
     // publishes the result; the tile's other blocks wait for that one line.
