@@ -236,7 +236,7 @@ def cacheable_bytes(w):
 def rotation(torch, w, push, requested):
     """Buffer sets to cycle: the requested number, or as many as make the
     cacheable bytes of the rotated sets exceed COLD_BYTES (at least 3, and at
-    least 2 where memory allows no more), within 1024 sets, 16 GB of buffers
+    least 2 where memory allows no more), within 1024 sets, 24 GB of buffers
     and half the free device memory.  Configurations of a few tokens touch
     too little to leave the cache that way (they are bound by launch
     latency, not bytes)."""
@@ -245,7 +245,7 @@ def rotation(torch, w, push, requested):
         return requested
     free, _ = torch.cuda.mem_get_info()
     n = max(3, math.ceil(COLD_BYTES / max(cacheable_bytes(w), 1)))
-    return max(1, min(n, 1024, int((16 << 30) // b), int(free * 0.5 // b)))
+    return max(1, min(n, 1024, int((24 << 30) // b), int(free * 0.5 // b)))
 
 
 # Launches per loop of the per-kernel durations and graph replays (and the

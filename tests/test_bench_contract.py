@@ -65,3 +65,36 @@ def test_timed_path_does_not_import_the_oracle():
             "print('ok')\n").format(root=ROOT, tests=os.path.join(ROOT, "tests"))
     r = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, timeout=300)
     assert r.returncode == 0 and r.stdout.strip() == "ok", r.stderr[-2000:]
+
+
+def test_rotation_leaves_no_set_in_the_cache():
+    """Every configuration whose inputs are not a few KB rotates enough
+    buffer sets that the bytes read or written with cache-allocating
+    accesses exceed twice the 256 MB memory-side cache, within the 24 GB
+    buffer cap; the 4096-token h7168 workload takes 9 sets."""
+    sys.path.insert(0, ROOT)
+    sys.path.insert(0, os.path.join(ROOT, "tests"))
+    import bench
+    import workloads
+
+    class _Cuda:
+        @staticmethod
+        def mem_get_info():
+            return 250 << 30, 288 << 30
+
+    class _Torch:
+        cuda = _Cuda()
+
+    assert bench.rotation(_Torch, workloads.CONFIGS["gen_zipf_h7168"], False, 0) == 9
+    assert bench.rotation(_Torch, workloads.CONFIGS["gen_zipf_h7168"], False, 2) == 2
+    for name in ("gen_zipf_h7168", "gen_zipf_h2048", "pr_scale", "epcfg_defaults", "large_weighted",
+                 "large_unweighted"):
+        w = workloads.CONFIGS[name]
+        for push in (False, True):
+            n = bench.rotation(_Torch, w, push, 0)
+            assert n * bench.cacheable_bytes(w) > bench.COLD_BYTES, (name, push, n)
+            assert n * bench.set_bytes(w, push) <= 24 << 30, (name, push, n)
+    # x, ids, weights, sendMap and the metadata of at most min(W, K) rows per token
+    w = workloads.CONFIGS["gen_zipf_h7168"]
+    T, K, row = 4096, 8, 7168 * 2
+    assert bench.cacheable_bytes(w) == T * (row + K * 8) + T * K * 4 + T * 8 * (4 + K * 8)
