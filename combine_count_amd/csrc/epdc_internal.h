@@ -54,6 +54,8 @@ constexpr bool kPushNtStore = true;         // landing rows: non-temporal stores
 constexpr int kSelfScanBlocks = 1024;       // launches of up to this many blocks sum the tile counts in every block
 constexpr int kSelfScanAnyCpw = 4;          // ... and launches of slabs of at most this many chunks, at any size
 constexpr int kSelfScanWords = 8192;        //     while a block sums at most this many published words
+constexpr int kWideFillBlocks = 7 * 256;   // wide-slab grids of this many blocks fill the GPU: 2-chunk slabs instead
+constexpr int kOneTokenWaveBlocks = 16384; // launches of up to this many blocks move one token per wave
 constexpr int kNarrowTiles = 4;             // launches of up to this many tiles use 1- or 2-chunk slabs
 constexpr int kLocalScanTiles = 8;          // launches of up to this many 64-token tiles scan in every block
 constexpr int kCombineGroup = 8;            // returned rows requested together per wave (gather combine)
@@ -233,18 +235,42 @@ inline DispatchPlan plan_dispatch(int32_t T, int32_t rowBytes, int32_t W) {
     // slabs (4 + 3) instead, which keeps them under the self-summing SCAN
     // below (8192 fp8 tokens 52.1 -> 49.8 us; at 4096 tokens one 7-chunk
     // slab, already self-summing, is faster: 25.6 against 30.2).
-    if (nTiles <= kNarrowTiles)
+    // Wide slabs (7 or 8 chunks) of a whole row of at least 8 chunks, an even
+    // number, become 2-chunk slabs where the wide grid would fill every
+    // block slot of the GPU at once (kWideFillBlocks: 256 CUs x 7 blocks, the
+    // wide kernels' occupancy) and the 2-chunk grid still moves one token per
+    // wave; such launches then sum the SCAN in every block (below) instead of
+    // waiting on the tile leaders' line, and the later blocks of the longer
+    // grid find the counts published when they start.  Cold x, one library
+    // per process, 2 rounds, dispatch us: h7168 at 3584 / 4096 / 6144 / 8192
+    // tokens 44.8 -> 41.1, 50.7 -> 45.8, 73.6 -> 66.7, 98.6 -> 87.0; fp32
+    // rows (28 chunks) at 2048 / 4096 tokens 48.3 -> 44.7, 94.1 -> 85.0; h4096
+    // at 8192 tokens 58.3 -> 53.0.  Below the fill point they lose (h7168 at
+    // 2560 / 3072 tokens, 1280 / 1536 wide blocks: 29.2 -> 30.8, 34.8 -> 36.0;
+    // fp32 rows at 1536 tokens 33.8 -> 34.9), and so do 1-chunk slabs (63.3
+    // at 4096 tokens) and 2-chunk slabs with the leaders' line (63.3); at
+    // 16384 tokens (28,672 2-chunk blocks) they were even (276.8 against
+    // 276.1).
+    int32_t wp = 1;
+    while (wp < W) wp <<= 1;
+    if (nTiles <= kNarrowTiles) {
         pl.cpw = nChunks <= 1 ? 1 : (!whole || nChunks % 2 == 0) ? 2 : 1;
-    else if (whole && nChunks == 7 && (int64_t)nTiles * (kTile / 4) > kSelfScanBlocks)
+    } else if (whole && nChunks == 7 && (int64_t)nTiles * (kTile / 4) > kSelfScanBlocks) {
         pl.cpw = 4;
-    else if (whole)
+    } else if (whole) {
         pl.cpw = nChunks % 8 == 0 ? 8 : nChunks % 7 == 0 ? 7 : nChunks % 4 == 0 ? 4 : nChunks % 2 == 0 ? 2 : 1;
-    else
+        const int64_t perTile = kTile / 4;  // one-token-per-wave blocks per tile and slab
+        if (pl.cpw > kSelfScanAnyCpw && nChunks >= 8 && nChunks % 2 == 0 &&
+            (int64_t)nTiles * perTile * (nChunks / pl.cpw) >= kWideFillBlocks &&
+            (int64_t)nTiles * perTile * (nChunks / 2) <= kOneTokenWaveBlocks && (int64_t)nTiles * wp <= kSelfScanWords)
+            pl.cpw = 2;
+    } else {
         pl.cpw = nChunks <= 1 ? 1 : nChunks <= 2 ? 2 : nChunks <= 4 ? 4 : nChunks <= 7 ? 7 : 8;
+    }
     // Tokens per wave: one (most blocks, measured fastest at 4096 and 16384
-    // tokens) unless that would exceed 16384 blocks.
+    // tokens) unless that would exceed kOneTokenWaveBlocks blocks.
     const int64_t perTokenWave = (int64_t)nTiles * (kTile / 4) * ceil_div(nChunks, pl.cpw);
-    pl.ntw = perTokenWave <= 16384 ? 1 : perTokenWave <= 2 * 16384 ? 2 : 4;
+    pl.ntw = perTokenWave <= kOneTokenWaveBlocks ? 1 : perTokenWave <= 2 * kOneTokenWaveBlocks ? 2 : 4;
     pl.nSubs = kTile / (4 * pl.ntw);
     pl.nSlabs = ceil_div(nChunks, pl.cpw);
     pl.nBlocks = (int64_t)nTiles * pl.nSubs * pl.nSlabs;
@@ -264,8 +290,6 @@ inline DispatchPlan plan_dispatch(int32_t T, int32_t rowBytes, int32_t W) {
     // (cold x, one library per process, 3 rounds, against the leader's line:
     // fp4x2 rows at 16384 tokens 57.4 -> 50.1 us, h2048 at 16384 tokens 63.2
     // -> 56.3, fp8 rows at 8192 tokens 60.3 -> 50.1).
-    int32_t wp = 1;
-    while (wp < W) wp <<= 1;
     if (pl.ntw == 1 && nTiles <= kLocalScanTiles)
         pl.scan = kScanLocal;
     else if (pl.nBlocks <= kSelfScanBlocks ||

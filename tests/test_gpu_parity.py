@@ -97,13 +97,16 @@ EDGE = [
     ("self_scan_1024_blocks_t2047", 8, 32, 2048, 2047, 8, 7168, "zipf", 1),
     ("leader_scan_1056_blocks_t2049", 8, 32, 2049, 2049, 8, 7168, "zipf", 1),
     ("self_scan_63_tiles_h128", 4, 8, 4100, 4000, 4, 128, "uniform", 1),
-    # around the x-early switch at 2560 blocks: 80 tiles (x after the SCAN), 81 tiles (x
-    # before COUNT, a last tile of one token)
-    ("x_late_2560_blocks_t5120", 8, 32, 5120, 5120, 8, 7168, "zipf", 1),
-    ("x_early_2592_blocks_t5121", 8, 32, 5121, 5121, 8, 7168, "zipf", 1),
+    # around the point where wide slabs fill the GPU (1792 blocks of 7 or 8 chunks): 48 tiles
+    # of h7168 keep two 7-chunk slabs (1536 blocks, the tile leaders publish); 57 tiles (a
+    # last tile of one token) take seven 2-chunk slabs (6384 blocks, every block sums); 94
+    # tiles of h4096 keep one 8-chunk slab (1504 blocks, leaders publish)
+    ("wide7_leader_1536_blocks_t3072", 8, 32, 3072, 3072, 8, 7168, "zipf", 1),
+    ("slab2_self_6384_blocks_t3585", 8, 32, 3585, 3585, 8, 7168, "zipf", 1),
+    ("wide8_leader_1504_blocks_t6000_h4096", 2, 4, 6000, 6000, 3, 4096, "uniform", 1),
     # self-summing with x requested between COUNT and the SCAN's wait (slabs of at most 4
     # chunks), ragged 3.5 KiB rows
-    ("self_scan_x_mid_ragged_h1792", 4, 8, 1000, 1000, 5, 1792, "uniform", 1),
+    ("self_scan_ragged_h1792", 4, 8, 1000, 1000, 5, 1792, "uniform", 1),
     # the token-count x topk grid of mori PR #599's checks, at 8 PEs / 256 experts / h7168
     # (uniform routing; the Zipf workloads cover the skewed case)
     ("pr_grid_ct512_topk6", 8, 32, 512, 512, 6, 7168, "uniform", 1),
@@ -121,8 +124,8 @@ EDGE = [
     ("ragged_rows_5p5k", 8, 16, 300, 300, 8, 2816, "zipf", 1),
     ("ragged_rows_9p5k", 8, 16, 200, 130, 8, 4864, "uniform", 0),
     ("ragged_rows_9p5k_5_tiles", 8, 16, 320, 300, 8, 4864, "uniform", 1),  # 8-chunk slabs, local scan
-    # ragged rows in a launch of more than 2560 blocks (x requested before COUNT)
-    ("ragged_rows_x_early_t13000", 8, 16, 13000, 13000, 8, 2816, "uniform", 1),
+    # ragged rows (5.5 KiB, 7-chunk slabs) in a launch of 3264 blocks, tile leaders publish
+    ("ragged_rows_leader_t13000", 8, 16, 13000, 13000, 8, 2816, "uniform", 1),
     # further compiled dispatch variants (slab chunks, tokens per wave, bound checks, scan):
     ("ragged_ntw2_t66000_h264", 2, 4, 66000, 66000, 2, 264, "uniform", 1),       # 1, 2, checked
     ("ragged_ntw4_t132000_h264", 2, 4, 132000, 132000, 2, 264, "zipf", 0),       # 1, 4, checked
@@ -139,41 +142,40 @@ EDGE = [
     ("ragged_ntw2_cpw7_t66000_h2816", 2, 4, 66000, 66000, 2, 2816, "zipf", 1),   # 7, 2, checked
     ("ragged_ntw2_cpw8_t33000_h4864", 2, 4, 33000, 33000, 2, 4864, "uniform", 1),  # 8, 2, checked
     ("ntw4_cpw2_t26300_h5120", 2, 4, 26300, 26300, 2, 5120, "uniform", 1),       # 2, 4
-    # one token per wave with x before COUNT (over 2560 blocks) and slabs of at most 4 chunks
-    ("x_early_cpw4_t10300_h2048", 2, 4, 10300, 10300, 3, 2048, "uniform", 1),        # 4, full
-    ("x_early_cpw4_ragged_t10300_h1792", 2, 4, 10300, 10300, 3, 1792, "zipf", 1),    # 4, checked
-    ("x_early_cpw2_t3400_h3072", 2, 4, 3400, 3400, 3, 3072, "uniform", 1),           # 2, full, 3 slabs
-    ("x_early_cpw2_ragged_t10300_h768", 2, 4, 10300, 10300, 3, 768, "uniform", 0),   # 2, checked
-    ("x_early_cpw1_ragged_t10300_h264", 2, 4, 10300, 10300, 2, 264, "uniform", 1),   # 1, checked
+    # one token per wave, slabs of at most 4 chunks, over 2560 blocks: every block sums
+    ("self_cpw4_t10300_h2048", 2, 4, 10300, 10300, 3, 2048, "uniform", 1),        # 4, full
+    ("self_cpw4_ragged_t10300_h1792", 2, 4, 10300, 10300, 3, 1792, "zipf", 1),    # 4, checked
+    ("self_cpw2_t3400_h3072", 2, 4, 3400, 3400, 3, 3072, "uniform", 1),           # 2, full, 3 slabs
+    ("self_cpw2_ragged_t10300_h768", 2, 4, 10300, 10300, 3, 768, "uniform", 0),   # 2, checked
+    ("self_cpw1_ragged_t10300_h264", 2, 4, 10300, 10300, 2, 264, "uniform", 1),   # 1, checked
     # x between COUNT and the SCAN's wait with 1-chunk slabs (3 KiB rows: three slabs per row)
-    ("x_mid_cpw1_t1000_h1536", 4, 8, 1000, 1000, 5, 1536, "zipf", 1),
+    ("self_cpw1_t1000_h1536", 4, 8, 1000, 1000, 5, 1536, "zipf", 1),
     # slabs of at most 4 chunks where a block would sum over 8192 published words (64 PEs,
-    # over 128 tiles): the tile leaders publish, x after the SCAN (<= 2560 blocks) or before
-    # COUNT (over 2560)
-    ("w64_x_late_cpw1_ragged_t8256_h264", 64, 2, 8256, 8256, 2, 264, "uniform", 1),
-    ("w64_x_late_cpw1_t8256_h512", 64, 2, 8256, 8256, 2, 512, "uniform", 0),
-    ("w64_x_late_cpw2_ragged_t8256_h768", 64, 2, 8256, 8256, 2, 768, "uniform", 1),
-    ("w64_x_late_cpw2_t8256_h1024", 64, 2, 8256, 8256, 2, 1024, "zipf", 1),
-    ("w64_x_late_cpw4_ragged_t8256_h1792", 64, 2, 8256, 8256, 2, 1792, "uniform", 0),
-    ("w64_x_late_cpw4_t8256_h2048", 64, 2, 8256, 8256, 2, 2048, "uniform", 1),
-    ("w64_x_early_cpw1_ragged_t10300_h264", 64, 2, 10300, 10300, 2, 264, "zipf", 1),
-    ("w64_x_early_cpw1_t10300_h512", 64, 2, 10300, 10300, 2, 512, "uniform", 1),
-    ("w64_x_early_cpw2_ragged_t10300_h768", 64, 2, 10300, 10300, 2, 768, "uniform", 0),
-    ("w64_x_early_cpw2_t10300_h1024", 64, 2, 10300, 10300, 2, 1024, "uniform", 1),
-    ("w64_x_early_cpw4_ragged_t10300_h1792", 64, 2, 10300, 10300, 2, 1792, "zipf", 1),
-    ("w64_x_early_cpw4_t10300_h2048", 64, 2, 10300, 10300, 2, 2048, "uniform", 1),
+    # over 128 tiles): the tile leaders publish (2064 and 2576 blocks)
+    ("w64_leader_cpw1_ragged_t8256_h264", 64, 2, 8256, 8256, 2, 264, "uniform", 1),
+    ("w64_leader_cpw1_t8256_h512", 64, 2, 8256, 8256, 2, 512, "uniform", 0),
+    ("w64_leader_cpw2_ragged_t8256_h768", 64, 2, 8256, 8256, 2, 768, "uniform", 1),
+    ("w64_leader_cpw2_t8256_h1024", 64, 2, 8256, 8256, 2, 1024, "zipf", 1),
+    ("w64_leader_cpw4_ragged_t8256_h1792", 64, 2, 8256, 8256, 2, 1792, "uniform", 0),
+    ("w64_leader_cpw4_t8256_h2048", 64, 2, 8256, 8256, 2, 2048, "uniform", 1),
+    ("w64_leader_cpw1_ragged_t10300_h264", 64, 2, 10300, 10300, 2, 264, "zipf", 1),
+    ("w64_leader_cpw1_t10300_h512", 64, 2, 10300, 10300, 2, 512, "uniform", 1),
+    ("w64_leader_cpw2_ragged_t10300_h768", 64, 2, 10300, 10300, 2, 768, "uniform", 0),
+    ("w64_leader_cpw2_t10300_h1024", 64, 2, 10300, 10300, 2, 1024, "uniform", 1),
+    ("w64_leader_cpw4_ragged_t10300_h1792", 64, 2, 10300, 10300, 2, 1792, "zipf", 1),
+    ("w64_leader_cpw4_t10300_h2048", 64, 2, 10300, 10300, 2, 2048, "uniform", 1),
     ("ntw4_cpw4_t43700_h6144", 2, 4, 43700, 43700, 2, 6144, "uniform", 1),       # 4, 4
-    # one token per wave, scanned by tile leaders with x after the SCAN (1024 < blocks <= 2560),
-    # for the slab widths the wider rows above never reach there: 1, 2, 4 chunks
-    ("x_late_cpw1_t6000_h512", 2, 4, 6000, 6000, 3, 512, "uniform", 1),          # 1, 1
-    ("x_late_cpw1_ragged_t6000_h264", 2, 4, 6000, 6000, 3, 264, "zipf", 1),      # 1, 1, checked
-    ("x_late_cpw2_t6000_h1024", 2, 4, 6000, 6000, 3, 1024, "uniform", 0),        # 2, 1
-    ("x_late_cpw2_ragged_t6000_h768", 2, 4, 6000, 6000, 3, 768, "uniform", 1),   # 2, 1, checked
-    ("x_late_cpw4_t6000_h2048", 2, 4, 6000, 6000, 3, 2048, "zipf", 1),           # 4, 1
-    ("x_late_cpw4_ragged_t6000_h1792", 2, 4, 6000, 6000, 3, 1792, "uniform", 1),  # 4, 1, checked
-    # 8-chunk slabs with x before COUNT (over 2560 blocks)
-    ("x_early_cpw8_t12000_h4096", 2, 4, 12000, 12000, 3, 4096, "uniform", 1),    # 8, 1
-    ("x_early_cpw8_ragged_t6000_h4864", 2, 4, 6000, 6000, 3, 4864, "zipf", 1),   # 8, 1, checked
+    # one token per wave, 1504 blocks of slabs of 1, 2 and 4 chunks (every block sums)
+    ("self_1504_blocks_cpw1_t6000_h512", 2, 4, 6000, 6000, 3, 512, "uniform", 1),          # 1, 1
+    ("self_1504_blocks_cpw1_ragged_t6000_h264", 2, 4, 6000, 6000, 3, 264, "zipf", 1),      # 1, 1, checked
+    ("self_1504_blocks_cpw2_t6000_h1024", 2, 4, 6000, 6000, 3, 1024, "uniform", 0),        # 2, 1
+    ("self_1504_blocks_cpw2_ragged_t6000_h768", 2, 4, 6000, 6000, 3, 768, "uniform", 1),   # 2, 1, checked
+    ("self_1504_blocks_cpw4_t6000_h2048", 2, 4, 6000, 6000, 3, 2048, "zipf", 1),           # 4, 1
+    ("self_1504_blocks_cpw4_ragged_t6000_h1792", 2, 4, 6000, 6000, 3, 1792, "uniform", 1),  # 4, 1, checked
+    # rows of 8 chunks at 12000 tokens (3008 8-chunk blocks would fill the GPU: 2-chunk slabs,
+    # every block sums), and 8-chunk bound-checked slabs with the tile leaders publishing
+    ("slab2_self_t12000_h4096", 2, 4, 12000, 12000, 3, 4096, "uniform", 1),    # 8, 1
+    ("leader_cpw8_ragged_t6000_h4864", 2, 4, 6000, 6000, 3, 4864, "zipf", 1),   # 8, 1, checked
     # four tokens per wave with 7- and 8-chunk slabs (over 32768 one-token waves)
     ("ntw4_4plus3_t132000_h3584", 2, 4, 132000, 132000, 2, 3584, "uniform", 1),  # 4, 4, checked (7 = 4 + 3)
     ("ntw4_cpw7_w1_t65601_h7168", 1, 4, 65601, 65601, 2, 7168, "uniform", 1),    # 7, 4
@@ -195,7 +197,7 @@ DTYPES = [
     ("fp8_wire_bf16_combine_h7168", "gen_zipf_h7168", "fp8", "bf16"),
     ("fp4x2_wire_bf16_combine_h7168", "gen_zipf_h7168", "fp4x2", "bf16"),
     ("fp32_both_pr_scale", "pr_scale", "fp32", "fp32"),
-    ("fp32_both_h7168", "gen_zipf_h7168", "fp32", "fp32"),  # 4096 dispatch blocks: x before COUNT
+    ("fp32_both_h7168", "gen_zipf_h7168", "fp32", "fp32"),  # 14336 2-chunk dispatch blocks, every block sums
     ("bf16_wire_fp32_combine_defaults", "epcfg_defaults", "bf16", "fp32"),
     ("fp8_wire_fp32_combine_tiny", "tiny", "fp8", "fp32"),
     ("fp4x2_wire_ragged", None, "fp4x2", "bf16"),
@@ -243,8 +245,8 @@ SCALES = [
     # §4/§5: the dispatch's scales and the out_scales region; mori PR #599's merge notes).
     ("fp8_scales56_h7168", "gen_zipf_h7168", "fp8", 56),  # one scale per 128 values; 4 + 3-chunk slabs, x mid
     ("fp4x2_scales1_h7168", "gen_zipf_h7168", "fp4x2", 1),  # one per token; self-summing, x mid
-    ("bf16_scales56_leader_scan", "gen_zipf_h7168", "bf16", 56),  # 2048 blocks: tile leaders publish
-    ("fp32_scales8_x_early", "gen_zipf_h7168", "fp32", 8),  # 4096 blocks: x before COUNT
+    ("bf16_scales56_leader_scan", "wide7_leader_1536_blocks_t3072", "bf16", 56),  # tile leaders publish
+    ("fp32_scales8_slab2_self", "gen_zipf_h7168", "fp32", 8),  # 14336 2-chunk blocks, every block sums
     ("bf16_scales64_defaults", "epcfg_defaults", "bf16", 64),  # local scan, exactly one wave of scales
     ("fp8_scales65_pr_scale", "pr_scale", "fp8", 65),  # one past a wave: the scale-tail loop
     ("fp8_scales1024_tiny", "tiny", "fp8", 1024),  # the maximum scaleDim
@@ -267,7 +269,7 @@ def _edge_workload(name):
 def test_scale_forwarding(case):
     """Per-token scales are copied bitwise beside every row of their token:
     recvScales whole-buffer equal to the oracle's (sentinels past the counts
-    untouched), through every SCAN form and x order."""
+    untouched), through every SCAN form."""
     name, base, wire, S = case
     if base is None:
         w = workloads.Workload(name, 5, 3, 700, 650, 7, 1056, "uniform", 1)
@@ -408,9 +410,11 @@ GRAPH_CASES = [
     ("pr_scale", "pr_scale", None),  # 8 tiles: local scan, scratch untouched
     # 16 tiles, 256 blocks: every block sums the published counts, x mid (4-chunk slabs)
     ("h2048_t1024_self_scan", "gen_zipf_h2048", dict(numTokens=1024, maxTokPerRank=1024)),
-    # 2048 blocks: the tile leaders publish base rows, x after the SCAN
-    ("h7168_t4096_leader_scan", "gen_zipf_h7168", None),
-    ("h7168_fp32_x_early", "gen_zipf_h7168", dict(wire="fp32", combineDtype="fp32")),  # 4096 blocks
+    # 1536 blocks of 7-chunk slabs: the tile leaders publish base rows
+    ("h7168_t3072_leader_scan", "gen_zipf_h7168", dict(numTokens=3072)),
+    # 7168 and 14336 blocks of 2-chunk slabs (bf16 and fp32 rows): every block sums
+    ("h7168_t4096_slab2_self", "gen_zipf_h7168", None),
+    ("h7168_fp32_slab2_self", "gen_zipf_h7168", dict(wire="fp32", combineDtype="fp32")),
 ]
 
 

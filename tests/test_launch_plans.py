@@ -14,8 +14,20 @@ EXPECT = {
     # (numTokens, rowBytes, worldSize): (cpw, ntw, nSlabs, nSubs, nBlocks, full, scan)
     # scan: 0 local (every block counts the earlier tiles' ids), 1 every block sums the leaders'
     # published counts, 2 the tile leader publishes the tile's base rows
-    # 4096 tokens x h7168 bf16: two 7-chunk slabs, 2048 blocks, tile leaders publish
-    (4096, 14336, 8): (7, 1, 2, 16, 2048, 1, 2),
+    # 4096 tokens x h7168 bf16: two 7-chunk slabs would fill the GPU (2048 blocks): seven
+    # 2-chunk slabs, 7168 blocks, every block sums
+    (4096, 14336, 8): (2, 1, 7, 16, 7168, 1, 1),
+    # the fill point of 7-chunk slabs (1792 blocks, 7 per CU): 3072 tokens keep them (1536 blocks,
+    # leaders publish), 3584 take 2-chunk slabs
+    (3072, 14336, 8): (7, 1, 2, 16, 1536, 1, 2),
+    (3584, 14336, 8): (2, 1, 7, 16, 6272, 1, 1),
+    # ... up to 16384 one-token 2-chunk blocks (146 tiles x 112); 147 tiles keep 7-chunk slabs
+    (9344, 14336, 8): (2, 1, 7, 16, 16352, 1, 1),
+    (9408, 14336, 8): (7, 1, 2, 16, 4704, 1, 2),
+    # h4096 (8 chunks) at 8192 tokens: 2048 8-chunk blocks fill the GPU: 2-chunk slabs
+    (8192, 8192, 8): (2, 1, 4, 16, 8192, 1, 1),
+    # ... while a block would sum at most 8192 published words (tiles x worldSize rounded up)
+    (8192, 8192, 128): (8, 1, 1, 16, 2048, 1, 2),
     # fp8 rows (7 chunks): one 7-chunk slab, 1024 blocks, every block sums
     (4096, 7168, 8): (7, 1, 1, 16, 1024, 1, 1),
     # ... at 8192 tokens 7-chunk slabs would pass 1024 blocks: two 4-chunk slabs (4 + 3), every block sums
@@ -24,8 +36,10 @@ EXPECT = {
     (4096, 3584, 8): (4, 1, 1, 16, 1024, 0, 1),
     # h2048 bf16: one 4-chunk slab, every block sums
     (4096, 4096, 8): (4, 1, 1, 16, 1024, 1, 1),
-    # fp32 rows: four 7-chunk slabs, 4096 blocks, leaders publish
-    (4096, 28672, 8): (7, 1, 4, 16, 4096, 1, 2),
+    # fp32 rows (28 chunks): fourteen 2-chunk slabs, 14336 blocks, every block sums; at 1536
+    # tokens 7-chunk slabs (1536 blocks) stay
+    (4096, 28672, 8): (2, 1, 14, 16, 14336, 1, 1),
+    (1536, 28672, 8): (7, 1, 4, 16, 1536, 1, 2),
     # 16384 tokens: 8192 blocks, leaders publish
     (16384, 14336, 8): (7, 1, 2, 16, 8192, 1, 2),
     # one tile: 2-chunk slabs (at most 4 tiles), local scan
@@ -39,7 +53,7 @@ EXPECT = {
     # around the every-block limit of 7-chunk slabs (1024 blocks)
     (2047, 14336, 8): (7, 1, 2, 16, 1024, 1, 1),
     (2049, 14336, 8): (7, 1, 2, 16, 1056, 1, 2),
-    (5121, 14336, 8): (7, 1, 2, 16, 2592, 1, 2),
+    (5121, 14336, 8): (2, 1, 7, 16, 9072, 1, 1),
     # slabs of at most 4 chunks sum in every block at any size while a block sums at most
     # 8192 published words (tiles x worldSize rounded up to a power of two)
     (16384, 3584, 8): (4, 1, 1, 16, 4096, 0, 1),

@@ -56,10 +56,10 @@ def _assert_same(a, b, tag):
 
 SEQUENCES = [
     # (first workload, second with fewer tokens): the SCAN forms of the first call
-    ("leader_scan_then_self_scan", workloads.CONFIGS["gen_zipf_h7168"], dict(numTokens=777)),
+    ("leader_scan_then_self_scan", workloads.CONFIGS["gen_zipf_h7168"].with_(numTokens=3072), dict(numTokens=777)),
     ("self_scan_then_local", workloads.CONFIGS["gen_zipf_h7168"].with_(wire="fp8", scaleDim=56),
      dict(numTokens=300)),
-    ("x_early_then_leader_scan", workloads.CONFIGS["large_unweighted"], dict(numTokens=3000)),
+    ("large_leader_then_leader_scan", workloads.CONFIGS["large_unweighted"], dict(numTokens=3000)),
     ("local_then_one_token", workloads.CONFIGS["pr_scale"], dict(numTokens=1)),
 ]
 
