@@ -304,9 +304,9 @@ inline DispatchPlan plan_dispatch(int32_t T, int32_t rowBytes, int32_t W) {
     // counts; 4096 tokens, cold x: fp4x2 rows 16.16 -> 15.70 us, h2048
     // 17.55 -> 17.16) and behind them when the leaders publish (there
     // counting sooner only lengthens the wait for the leader's line: 4096
-    // tokens x h7168 50.84 against 51.63).  With x cold in HBM every launch
-    // gains from requesting x before COUNT (4096 tokens x h7168 55.4 -> 50.8
-    // us; x after the SCAN, and x between COUNT and the SCAN's wait, were
+    // tokens x h7168 in 7-chunk slabs 50.84 against 51.63).  With x cold in
+    // HBM every launch gains from requesting x before COUNT (the same launch
+    // 55.4 -> 50.8 us; x after the SCAN, and x between COUNT and the SCAN's wait, were
     // tuned with x left in the memory-side cache by the previous call, where
     // they won).
     return pl;
