@@ -15,8 +15,11 @@
 //   * lane k0 of a kept slot sums, in slot order from +0, the weights of the
 //     slots on its PE (read from the other lanes by shuffles) -- once the
 //     first group's rows are requested, so that the wait for the ids and
-//     weights and this sum overlap those rows in flight (4096 tokens x h7168:
-//     41.6 -> 40.0 us; h2048 15.0 -> 14.0; EpCfg defaults 5.7 -> 5.1);
+//     weights and this sum overlap those rows in flight (cold, against a
+//     form whose ids and weights were waited for before the ballot: 4096
+//     tokens x h7168 41.3 -> 40.2 us, h2048 14.93 -> 14.34; 16384 tokens
+//     with uniform routing, ~5.3 rows a token, 237.9 -> 245.2, where fewer
+//     rows in flight per CU are faster);
 //   * the PE loop walks the kept slots in ascending order, a group of up to
 //     kCombineGroup rows at a time: all of a group's row loads are issued
 //     before its first FMA; every lane owns 16 contiguous bytes per chunk
@@ -141,7 +144,7 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineParams P, int nSlab
     int32_t flat = -1;
     uint64_t kept;
     float s = 1.0f;
-    int32_t epe = -1;
+    int32_t eid = -1;  // the slot's expert id (its PE is derived once the rows are requested)
     float ew = 0.0f;
     bool scalesDue = !LAND && P.useWeights;
     if constexpr (LAND) {
@@ -165,27 +168,27 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineParams P, int nSlab
         flat = L;
         if (P.useWeights && ok) s = P.landScale[L];
     } else {
-        const int32_t E = P.W * P.Epr;
-        int32_t pe = -1;
-        float w = 0.0f;
+        // The three loads go out back to back, unconditionally (an
+        // unweighted call, whose ids and weights may be NULL, re-reads its
+        // sendMap entry in their place), so that the ballot waits for
+        // sendMap alone; the expert id stays raw until the scale step, which
+        // runs once the first rows are requested.  (Deriving the PE here made
+        // the compiled code wait for the ids and only then request the
+        // weights: two round trips before the first row load.)
         if (lane < P.K) {
             const int64_t o = (int64_t)t * P.K + lane;
+            const int32_t *ids = P.useWeights ? P.expertIds : P.sendMap;
+            const float *wts = P.useWeights ? P.weights : reinterpret_cast<const float *>(P.sendMap);
             flat = P.sendMap[o];
-            if (P.useWeights) {
-                const int32_t e = P.expertIds[o];
-                if (e >= 0 && e < E) pe = P.eprShift >= 0 ? (e >> P.eprShift) : (e / P.Epr);
-                w = P.weights[o];
-            }
+            eid = ids[o];
+            ew = wts[o];
         }
         // Kept slots; an entry outside [0, W*M) (not written by a dispatch
         // of this cfg) counts as dropped rather than being read out of bounds.
         kept = __ballot(lane < P.K && flat >= 0 && flat < P.W * P.M);
-
         // Scale of each kept slot's PE: sum of the token's weights on that
         // PE, in slot order starting from +0 (computed once the first
         // group's rows are requested).
-        epe = pe;
-        ew = w;
     }
 
     constexpr bool kSplit = OUT32 && !FP32;
@@ -220,6 +223,12 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineParams P, int nSlab
         }
         auto mid = [&](float (&scl)[8]) {
             if (scalesDue) {
+                const int32_t E = P.W * P.Epr;
+                int32_t epe = -1;
+                // Keeps the id's first use (and so the wait for it) here,
+                // behind the row loads, rather than hoisted above them.
+                asm volatile("" : "+v"(eid));
+                if (eid >= 0 && eid < E) epe = P.eprShift >= 0 ? (eid >> P.eprShift) : (eid / P.Epr);
                 s = 0.0f;
                 for (int k = 0; k < P.K; ++k) {
                     const int32_t pk = __shfl(epe, k);
