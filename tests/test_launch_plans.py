@@ -26,8 +26,9 @@ EXPECT = {
     (9408, 14336, 8): (7, 1, 2, 16, 4704, 1, 2),
     # h4096 (8 chunks) at 8192 tokens: 2048 8-chunk blocks fill the GPU: 2-chunk slabs
     (8192, 8192, 8): (2, 1, 4, 16, 8192, 1, 1),
-    # ... while a block would sum at most 8192 published words (tiles x worldSize rounded up)
-    (8192, 8192, 128): (8, 1, 1, 16, 2048, 1, 2),
+    # ... while a block would sum at most 8192 published words (tiles x worldSize rounded up):
+    # 129 tiles at 64 PEs keep one 8-chunk slab, tile leaders publish
+    (8256, 8192, 64): (8, 1, 1, 16, 2064, 1, 2),
     # fp8 rows (7 chunks): one 7-chunk slab, 1024 blocks, every block sums
     (4096, 7168, 8): (7, 1, 1, 16, 1024, 1, 1),
     # ... at 8192 tokens 7-chunk slabs would pass 1024 blocks: two 4-chunk slabs (4 + 3), every block sums
